@@ -1,0 +1,219 @@
+/*
+ * pagedkv.h -- C ABI of the MI355X (gfx950) paged KV cache library.
+ *
+ * Three operations make up the hot path of a paged KV cache in a dense GQA
+ * decoder such as Qwen3-0.6B:
+ *   pa_reshape_and_cache      token-major K/V -> paged cache, through a slot
+ *                             mapping (optional SWA remap, optional fp8 scale)
+ *   pa_concat_and_cast_mla_k  per-head k_nope ++ shared k_rope -> K, with a cast
+ *   pa_decode_attention       one query token per sequence against its paged
+ *                             K/V, read back through a block table (GQA)
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller. The library
+ *     never allocates, frees or retains device memory and holds no state
+ *     between calls except the thread-local error text.
+ *   - Strides and sizes are in ELEMENTS of the tensor they describe.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream). Every call
+ *     only enqueues work: it returns after the launch, never synchronises,
+ *     never reads device memory on the host, and its launch shapes depend on
+ *     host arguments only, so a call can be captured into a HIP graph.
+ *   - Return value: PA_OK, or an error code with pa_last_error() describing
+ *     it. On an error nothing was enqueued. Host-visible arguments are fully
+ *     validated; device-resident metadata (slots, tables, lengths) cannot be
+ *     checked on the host, so the kernels treat out-of-range values as
+ *     documented below instead of faulting.
+ *   - Calls that write overlapping memory from different streams race; calls
+ *     on one stream are ordered.
+ */
+#ifndef PAGEDKV_H_
+#define PAGEDKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_ABI_VERSION 1
+
+typedef int32_t pa_status;
+enum {
+  PA_OK = 0,
+  PA_EINVAL = 1,       /* bad size, stride, pointer or shape relation */
+  PA_EDTYPE = 2,       /* unsupported dtype or dtype combination */
+  PA_EUNSUPPORTED = 3, /* valid but not implemented (e.g. head_size) */
+  PA_EHIP = 4,         /* the HIP runtime reported an error at launch */
+  PA_EWORKSPACE = 5    /* workspace missing, too small or misaligned */
+};
+
+/* Element types. bf16 and fp32 are IEEE-style; fp8 is OCP e4m3fn (bias 7,
+ * max 448, no infinities, NaN = S.1111.111), the native fp8 of gfx950. */
+typedef int32_t pa_dtype;
+enum { PA_BF16 = 0, PA_F32 = 2, PA_FP8_E4M3FN = 3 };
+
+/* Text describing the last non-OK status returned on the calling thread. */
+const char* pa_last_error(void);
+
+/* PA_ABI_VERSION of the built library. */
+int32_t pa_abi_version(void);
+
+/*
+ * pa_reshape_and_cache -- write token-major K (and V) into paged caches.
+ *
+ * Defined by: the store_kvcache Triton kernel in section 2.6 "Attention" of the
+ * Qwen3-0.6B engine walkthrough page (cache layout, slot -> block/offset, the
+ * skip of slot -1, source offset t*H*D + h*D + d) and reshape_and_cache_flash /
+ * launch_reshape_and_cache_flash of SGLang's cache_ops.py (token strides,
+ * optional second-stage SWA slot table, optional division by k/v scale before
+ * the store, block stride of the cache).
+ *
+ * For every token t in [0, num_tokens):
+ *   s = slot_mapping[t];              s < 0           -> token skipped
+ *   if swa_slot_mapping:              s >= swa_len    -> skipped
+ *       s = swa_slot_mapping[s];      s < 0           -> skipped
+ *   s >= num_blocks*block_size                        -> skipped
+ *   blk = s / block_size, off = s % block_size
+ *   key_cache[blk*block_stride + (off*num_heads + h)*head_size + d]
+ *       = enc(key[t*key_token_stride + h*head_size + d], k_scale)   (all h, d)
+ *   and the same for value/value_cache/v_scale when value != NULL.
+ * enc(x, scale):
+ *   src_dtype == cache_dtype and no scale: bit copy (keeps -0 and NaN bits);
+ *   otherwise y = fp32(x) / *scale (IEEE fp32 division; no division when the
+ *   scale is NULL), then one round-to-nearest-even to cache_dtype:
+ *     bf16: overflow -> inf; NaN -> sign | top payload bits | quiet bit;
+ *     e4m3fn: |y| > 464 (rounds past 448), +-inf and NaN -> 0x7F | sign.
+ *
+ * Arguments
+ *   key, value      [num_tokens, num_heads, head_size] with token stride
+ *                   key_token_stride / value_token_stride (>= num_heads*head_size),
+ *                   head stride head_size, dim stride 1. value == NULL (with
+ *                   value_cache == NULL) writes K only.
+ *   src_dtype       PA_BF16 or PA_F32.
+ *   key_cache,      [num_blocks, block_size, num_heads, head_size], block stride
+ *   value_cache     block_stride (>= block_size*num_heads*head_size), inner
+ *                   [block_size, num_heads, head_size] contiguous.
+ *   cache_dtype     PA_BF16, PA_F32 or PA_FP8_E4M3FN.
+ *   slot_mapping    int64 [num_tokens].
+ *   swa_slot_mapping  int64 [swa_len] or NULL (no remap).
+ *   k_scale,v_scale device fp32 scalars; both or neither (NULL = no division).
+ * Preconditions (not checkable on the host): final slots of written tokens are
+ *   distinct (duplicates race: one of the writers wins per element).
+ * Errors: PA_EINVAL (null pointer, negative or inconsistent sizes/strides,
+ *   only one scale, value without value_cache), PA_EDTYPE, PA_EHIP.
+ * num_tokens == 0 is a valid no-op.
+ */
+pa_status pa_reshape_and_cache(const void* key, const void* value, pa_dtype src_dtype,
+                               int64_t num_tokens, int32_t num_heads, int32_t head_size,
+                               int64_t key_token_stride, int64_t value_token_stride,
+                               void* key_cache, void* value_cache, pa_dtype cache_dtype,
+                               int64_t num_blocks, int32_t block_size, int64_t block_stride,
+                               const int64_t* slot_mapping, const int64_t* swa_slot_mapping,
+                               int64_t swa_len, const float* k_scale, const float* v_scale,
+                               void* stream);
+
+/*
+ * pa_concat_and_cast_mla_k -- assemble MLA-style K from per-head k_nope and a
+ * k_rope row shared by all heads.
+ *
+ * Defined by: concat_and_cast_mha_k_kernel / concat_and_cast_mha_k_triton of
+ * SGLang's cache_ops.py (grid over tokens; the shape checks of the wrapper;
+ * the source dtype is converted to k's dtype at the store).
+ *
+ *   k[t, h, d]            = cast(k_nope[t, h, d])               d < nope_dim
+ *   k[t, h, nope_dim + d] = cast(k_rope[t, 0, d])               d < rope_dim
+ * cast: bit copy for equal dtypes, exact widening bf16 -> fp32, and the
+ * round-to-nearest-even narrowing of pa_reshape_and_cache otherwise.
+ *
+ * Arguments
+ *   k        [num_tokens, num_heads, nope_dim + rope_dim], strides
+ *            (k_stride0, k_stride1, 1); k_dtype PA_F32, PA_BF16 or PA_FP8_E4M3FN.
+ *   k_nope   [num_tokens, num_heads, nope_dim], strides (nope_stride0,
+ *            nope_stride1, 1); nope_dtype PA_BF16 or PA_F32.
+ *   k_rope   [num_tokens, 1, rope_dim], token stride rope_stride0, dim stride 1;
+ *            rope_dtype == nope_dtype.
+ * Errors: PA_EINVAL (null pointers, negative sizes, strides too small for the
+ *   row, overlapping rows of k), PA_EDTYPE, PA_EHIP. num_tokens == 0 is a no-op.
+ */
+pa_status pa_concat_and_cast_mla_k(void* k, pa_dtype k_dtype, int64_t k_stride0,
+                                   int64_t k_stride1, const void* k_nope, pa_dtype nope_dtype,
+                                   int64_t nope_stride0, int64_t nope_stride1,
+                                   const void* k_rope, pa_dtype rope_dtype, int64_t rope_stride0,
+                                   int64_t num_tokens, int32_t num_heads, int32_t nope_dim,
+                                   int32_t rope_dim, void* stream);
+
+/*
+ * pa_decode_attention_workspace_size -- bytes of device workspace that
+ * pa_decode_attention needs for these sizes (a pure function of its
+ * arguments; 0 is never returned for valid sizes). Returns 0 and sets
+ * pa_last_error() for invalid sizes.
+ */
+size_t pa_decode_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                          int32_t num_kv_heads, int32_t head_size,
+                                          int32_t max_blocks_per_seq, int32_t block_size);
+
+/*
+ * pa_decode_attention -- single-token paged decode attention with GQA.
+ *
+ * Defined by: section 2.6 "Attention" of the Qwen3-0.6B engine walkthrough
+ * page (the decode attention kernel reads K/V back along physical blocks
+ * through block_tables) and the PagedAttention principle page (GQA: H_Q is an
+ * integer multiple of H_KV; decode writes the new token's K/V before
+ * attention; a block is [block_size, H_KV, d_h]; blocks are physically
+ * scattered and ordered only by a table). Attention itself is the standard
+ * scaled-dot-product softmax; groups are contiguous (q head h reads kv head
+ * h / (num_q_heads / num_kv_heads)).
+ *
+ * For sequence b with n = clamp(context_lens[b], 0, max_blocks_per_seq*block_size)
+ * and q head h (g = h / G):
+ *   row(p)   = block_tables[b*max_blocks_per_seq + p/block_size], offset p%block_size
+ *   s_p      = softmax_scale * sum_d q[b,h,d] * (K[row(p), p%bs, g, d] * k_scale)
+ *   out[b,h] = sum_p softmax(s)_p * (V[row(p), p%bs, g, :] * v_scale)    (p < n)
+ * n == 0 writes zeros. A table entry outside [0, num_blocks) removes its
+ * positions from the softmax instead of being dereferenced.
+ *
+ * Arguments
+ *   out      [num_seqs, num_q_heads, head_size], sequence stride out_seq_stride;
+ *            out_dtype PA_BF16 or PA_F32 (round to nearest even from fp32).
+ *   q        [num_seqs, num_q_heads, head_size], sequence stride q_seq_stride;
+ *            q_dtype PA_BF16.
+ *   key_cache, value_cache  [num_blocks, block_size, num_kv_heads, head_size],
+ *            block stride block_stride, inner part contiguous; cache_dtype
+ *            PA_BF16 or PA_FP8_E4M3FN.
+ *   block_tables  int32 [num_seqs, max_blocks_per_seq], row-major, device.
+ *   context_lens  int32 [num_seqs], device.
+ *   k_scale, v_scale  device fp32 scalars or NULL (= 1.0).
+ *   workspace, workspace_bytes  device scratch of at least
+ *            pa_decode_attention_workspace_size(...) bytes, 256-byte aligned;
+ *            its contents on entry do not matter.
+ * Supported: head_size in {64, 128, 256}; num_q_heads % num_kv_heads == 0;
+ *   num_q_heads / num_kv_heads <= 16.
+ * Errors: PA_EINVAL, PA_EDTYPE, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_EHIP.
+ * num_seqs == 0 is a valid no-op.
+ */
+pa_status pa_decode_attention(void* out, pa_dtype out_dtype, int64_t out_seq_stride,
+                              const void* q, pa_dtype q_dtype, int64_t q_seq_stride,
+                              const void* key_cache, const void* value_cache,
+                              pa_dtype cache_dtype, int64_t num_blocks, int32_t block_size,
+                              int64_t block_stride, const int32_t* block_tables,
+                              int32_t max_blocks_per_seq, const int32_t* context_lens,
+                              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_size, float softmax_scale, const float* k_scale,
+                              const float* v_scale, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
+ * pa_hbm_copy -- streaming device-to-device copy of `bytes` bytes
+ * (measurement utility, not part of the cache path): the reference kernel
+ * against which achieved HBM bandwidth and profiler byte counters are
+ * calibrated. dst and src must be 16-byte aligned and must not overlap.
+ * Errors: PA_EINVAL, PA_EHIP.
+ */
+pa_status pa_hbm_copy(void* dst, const void* src, size_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H_ */

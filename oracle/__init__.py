@@ -1,0 +1,203 @@
+"""CPU oracle for the paged KV cache hot path (test infrastructure).
+
+Only the tests, ``__graft_entry__.smoke()`` and the benchmark's ``cpu_baseline``
+leg may import this package. The product library neither imports nor links it,
+and the two share no code: the arithmetic lives in ``pagedkv_oracle.c`` (plain
+C, fp64 for attention, exact bit arithmetic for the encodes), and this module
+only marshals numpy arrays into it.
+
+Every function states the passage it follows; the readings R1..R7 are listed in
+the header of ``pagedkv_oracle.c``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "pagedkv_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+# dtype codes of the C oracle (its own numbering)
+BF16, F32, FP8_E4M3FN = 0, 2, 3
+_NP_STORAGE = {BF16: np.uint16, F32: np.float32, FP8_E4M3FN: np.uint8}
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (IEEE arithmetic, no contraction, OpenMP)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+               "-fPIC", "-shared", "-Wall", "-Wextra", "-Werror", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I64, I32, F64 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double
+    lib.orc_e4m3fn_to_f64.argtypes = [ctypes.c_uint8]
+    lib.orc_e4m3fn_to_f64.restype = F64
+    lib.orc_f32_to_bf16.argtypes = [ctypes.c_float]
+    lib.orc_f32_to_bf16.restype = ctypes.c_uint16
+    lib.orc_f32_to_e4m3fn.argtypes = [ctypes.c_float]
+    lib.orc_f32_to_e4m3fn.restype = ctypes.c_uint8
+    lib.orc_encode_bf16_to_fp8_scaled.argtypes = [ctypes.c_uint16, ctypes.c_float]
+    lib.orc_encode_bf16_to_fp8_scaled.restype = ctypes.c_uint8
+    lib.orc_resolve_slot.argtypes = [P, I64, P, I64, I64]
+    lib.orc_resolve_slot.restype = I64
+    lib.orc_reshape_and_cache.argtypes = [P, P, I32, I64, I32, I32, I64, I64, P, P, I32, I64, I32,
+                                          I64, P, P, I64, P, P]
+    lib.orc_reshape_and_cache.restype = I64
+    lib.orc_concat_and_cast.argtypes = [P, I32, I64, I64, P, I32, I64, I64, P, I32, I64, I64, I32,
+                                        I32, I32]
+    lib.orc_concat_and_cast.restype = None
+    lib.orc_decode_attention.argtypes = [P, P, I32, I64, P, P, I32, I64, I32, I64, P, I32, P, I32,
+                                         I32, I32, I32, F64, P, P]
+    lib.orc_decode_attention.restype = None
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _scalar_f32(x):
+    return None if x is None else np.array([x], dtype=np.float32)
+
+
+# ------------------------------------------------------------------ encodes
+
+def e4m3fn_to_f64(codes) -> np.ndarray:
+    """Value of each OCP e4m3fn code (R4), exactly, as float64."""
+    lib = _load()
+    codes = np.asarray(codes, dtype=np.uint8).ravel()
+    return np.array([lib.orc_e4m3fn_to_f64(int(c)) for c in codes], dtype=np.float64)
+
+
+def f32_to_bf16(x) -> np.ndarray:
+    """fp32 -> bf16 bits, round to nearest even (R5)."""
+    lib = _load()
+    x = np.asarray(x, dtype=np.float32).ravel()
+    return np.array([lib.orc_f32_to_bf16(float(v)) for v in x], dtype=np.uint16)
+
+
+def f32_to_e4m3fn(x) -> np.ndarray:
+    """fp32 -> e4m3fn code, round to nearest even, overflow/inf/NaN -> signed NaN (R4)."""
+    lib = _load()
+    x = np.asarray(x, dtype=np.float32).ravel()
+    return np.array([lib.orc_f32_to_e4m3fn(float(v)) for v in x], dtype=np.uint8)
+
+
+def encode_bf16_to_fp8_scaled(bits, scale: float) -> np.ndarray:
+    """bf16 bits -> fp32 -> IEEE fp32 division by ``scale`` -> e4m3fn (R3, R4)."""
+    lib = _load()
+    bits = np.asarray(bits, dtype=np.uint16).ravel()
+    s = float(np.float32(scale))
+    return np.array([lib.orc_encode_bf16_to_fp8_scaled(int(b), s) for b in bits], dtype=np.uint8)
+
+
+# ------------------------------------------------------------ slot resolution
+
+def resolve_slots(slot_mapping, num_blocks: int, block_size: int, swa=None) -> np.ndarray:
+    """Final slot of every token, -1 for a skipped token (a1; R1, R2)."""
+    lib = _load()
+    sm = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+    sw = None if swa is None else np.ascontiguousarray(swa, dtype=np.int64)
+    swa_len = 0 if sw is None else sw.shape[0]
+    pool = int(num_blocks) * int(block_size)
+    return np.array([lib.orc_resolve_slot(_ptr(sm), t, _ptr(sw), swa_len, pool)
+                     for t in range(sm.shape[0])], dtype=np.int64)
+
+
+# --------------------------------------------------------- reshape_and_cache
+
+def reshape_and_cache(key, value, src_dtype: int, key_cache, value_cache, cache_dtype: int,
+                      slot_mapping, swa_slot_mapping=None, k_scale=None, v_scale=None,
+                      key_token_stride=None, value_token_stride=None) -> int:
+    """In-place write of token-major K (and V) into the paged caches (a1, a2).
+
+    ``key``/``value`` are storage arrays (uint16 for bf16, float32, uint8 for
+    fp8) viewed as ``[T, ...]`` with the row of token t starting at element
+    ``t * token_stride``; the caches are ``[NB, BS, H, D]`` storage arrays
+    (contiguous inner ``[BS, H, D]``; the block stride is taken from the array).
+    Returns the number of tokens written.
+    """
+    lib = _load()
+    T = int(slot_mapping.shape[0])
+    NB, BS, H, D = key_cache.shape
+    assert key_cache.dtype == _NP_STORAGE[cache_dtype]
+    assert key.dtype == _NP_STORAGE[src_dtype]
+    kstride = key_token_stride if key_token_stride is not None else key.strides[0] // key.itemsize
+    vstride = 0
+    if value is not None:
+        vstride = (value_token_stride if value_token_stride is not None
+                   else value.strides[0] // value.itemsize)
+    block_stride = key_cache.strides[0] // key_cache.itemsize
+    assert key_cache.strides[1] // key_cache.itemsize == H * D
+    sm = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+    sw = None if swa_slot_mapping is None else np.ascontiguousarray(swa_slot_mapping,
+                                                                     dtype=np.int64)
+    ks, vs = _scalar_f32(k_scale), _scalar_f32(v_scale)
+    return int(lib.orc_reshape_and_cache(
+        _ptr(key), _ptr(value), src_dtype, T, H, D, kstride, vstride,
+        _ptr(key_cache), _ptr(value_cache), cache_dtype, NB, BS, block_stride,
+        _ptr(sm), _ptr(sw), 0 if sw is None else sw.shape[0], _ptr(ks), _ptr(vs)))
+
+
+# ------------------------------------------------------------ concat_and_cast
+
+def concat_and_cast(k, k_dtype: int, k_nope, nope_dtype: int, k_rope, rope_dtype: int) -> None:
+    """In-place ``k[t,h,:] = cast(cat(k_nope[t,h,:], k_rope[t,0,:]))`` (a3)."""
+    lib = _load()
+    T, H, KD = k.shape
+    nope = k_nope.shape[2]
+    rope = k_rope.shape[2]
+    assert KD == nope + rope and k_rope.shape[1] == 1 and k_nope.shape[:2] == (T, H)
+    for a in (k, k_nope, k_rope):
+        assert a.strides[2] == a.itemsize
+    es = lambda a, i: a.strides[i] // a.itemsize  # noqa: E731
+    lib.orc_concat_and_cast(_ptr(k), k_dtype, es(k, 0), es(k, 1), _ptr(k_nope), nope_dtype,
+                            es(k_nope, 0), es(k_nope, 1), _ptr(k_rope), rope_dtype, es(k_rope, 0),
+                            T, H, nope, rope)
+
+
+# ---------------------------------------------------------- decode attention
+
+def decode_attention(q, q_dtype: int, key_cache, value_cache, cache_dtype: int, block_tables,
+                     context_lens, softmax_scale: float, k_scale=None, v_scale=None,
+                     num_kv_heads=None) -> np.ndarray:
+    """fp64 single-token paged decode attention, unrounded (a4..a7; R6, R7).
+
+    ``q`` is a ``[B, H_Q, D]`` storage array; caches are ``[NB, BS, H_KV, D]``;
+    ``block_tables`` int32 ``[B, W]``; ``context_lens`` int32 ``[B]``.
+    """
+    lib = _load()
+    B, HQ, D = q.shape
+    NB, BS, HKV, D2 = key_cache.shape
+    assert D == D2 and HQ % HKV == 0
+    assert q.strides[1] // q.itemsize == D and q.strides[2] == q.itemsize
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+    assert bt.shape[0] == B and cl.shape[0] == B
+    block_stride = key_cache.strides[0] // key_cache.itemsize
+    assert value_cache.strides == key_cache.strides
+    out = np.zeros((B, HQ, D), dtype=np.float64)
+    ks, vs = _scalar_f32(k_scale), _scalar_f32(v_scale)
+    lib.orc_decode_attention(out.ctypes.data, _ptr(q), q_dtype, q.strides[0] // q.itemsize,
+                             _ptr(key_cache), _ptr(value_cache), cache_dtype, NB, BS,
+                             block_stride, _ptr(bt), bt.shape[1], _ptr(cl), B, HQ, HKV, D,
+                             float(softmax_scale), _ptr(ks), _ptr(vs))
+    return out
