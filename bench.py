@@ -1,0 +1,394 @@
+"""Benchmark of the paged KV cache hot path on one MI355X.
+
+A step is one decode step of a single Qwen3-0.6B-shaped layer: the cache write
+of the 64 new tokens (pa_reshape_and_cache, bf16) followed by paged decode
+attention over the whole batch (pa_decode_attention), inputs resident in HBM.
+Default workload: batch 64, H_Q=16, H_KV=8, d_h=128, block_size 16, context
+lengths uniform in [512, 4096], 32,768-block bf16 pool.
+
+Prints ONE JSON line. ``value`` is the step's KV-read throughput: the K/V bytes
+attention must read (2 * sum(ctx) * H_KV * d_h * 2 B) divided by the measured
+time per step (write + attention). ``roofline`` is for the dominant kernel
+(decode attention) against MI355X's 8 TB/s; ``cpu_baseline`` is the CPU oracle
+timed on this host on the same step.
+
+Other workloads (parity-test configurations, for measurement only):
+``--workload prefill_fp8 | decode_fp8_b256 | mla_concat_swa``.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+MALL_FLUSH_BYTES = 1 << 30   # > 256 MB Infinity Cache
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="decode_b64",
+                   choices=["decode_b64", "prefill_fp8", "decode_fp8_b256", "mla_concat_swa"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--profile-steps", type=int, default=0,
+                   help="only run this many untimed steps (for rocprofv3 runs)")
+    return p.parse_args()
+
+
+class Timer:
+    """Event pairs on one stream; mean duration in ms."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream, self.pairs = torch, stream, []
+
+    def start(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record(self.stream)
+        self.pairs.append([e, None])
+
+    def stop(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record(self.stream)
+        self.pairs[-1][1] = e
+
+    def mean_ms(self):
+        return float(np.mean([a.elapsed_time(b) for a, b in self.pairs]))
+
+
+def cpu_cores():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+# --------------------------------------------------------------------------- #
+# decode step (default)
+# --------------------------------------------------------------------------- #
+
+def setup_decode(torch, pkv, workloads, w):
+    B, HQ, HKV, D, BS, NB = (w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_size,
+                             w.block_size, w.num_blocks)
+    dev = "cuda"
+    if w.cache_dtype == "fp8":
+        kc = workloads.device_normal((NB, BS, HKV, D), torch.float8_e4m3fn, dev, w.seed,
+                                     std=1.0 / w.k_scale)
+        vc = workloads.device_normal((NB, BS, HKV, D), torch.float8_e4m3fn, dev, w.seed + 1,
+                                     std=1.0 / w.v_scale)
+    else:
+        kc = workloads.device_normal((NB, BS, HKV, D), torch.bfloat16, dev, w.seed)
+        vc = workloads.device_normal((NB, BS, HKV, D), torch.bfloat16, dev, w.seed + 1)
+    t = dict(kc=kc, vc=vc)
+    t["q"] = workloads.device_normal((B, HQ, D), torch.bfloat16, dev, w.seed + 2)
+    t["new_k"] = workloads.device_normal((B, HKV, D), torch.bfloat16, dev, w.seed + 3)
+    t["new_v"] = workloads.device_normal((B, HKV, D), torch.bfloat16, dev, w.seed + 4)
+    t["slots"] = torch.from_numpy(w.new_token_slots).to(dev)
+    t["bt"] = torch.from_numpy(w.block_tables).to(dev)
+    t["cl"] = torch.from_numpy(w.context_lens).to(dev)
+    t["out"] = torch.empty((B, HQ, D), dtype=torch.bfloat16, device=dev)
+    t["ks"] = None if w.k_scale is None else torch.tensor([w.k_scale], device=dev)
+    t["vs"] = None if w.v_scale is None else torch.tensor([w.v_scale], device=dev)
+    need = pkv.decode_attention_workspace_size(B, HQ, HKV, D, w.width, BS)
+    t["ws"] = torch.empty(need, dtype=torch.uint8, device=dev)
+    return t
+
+
+def decode_write(pkv, t, w):
+    if w.cache_dtype == "fp8":
+        pkv.reshape_and_cache(t["new_k"], t["new_v"], t["kc"], t["vc"], t["slots"],
+                              k_scale=t["ks"], v_scale=t["vs"])
+    else:
+        pkv.reshape_and_cache(t["new_k"], t["new_v"], t["kc"], t["vc"], t["slots"])
+
+
+def decode_attn(pkv, t, w):
+    pkv.decode_attention(t["out"], t["q"], t["kc"], t["vc"], t["bt"], t["cl"], w.softmax_scale,
+                         t["ks"], t["vs"], workspace=t["ws"])
+
+
+def decode_bytes(w):
+    """Algorithmic HBM bytes of one attention call and of the new-token write."""
+    ctx = w.context_lens.astype(np.int64)
+    e_kv = 1 if w.cache_dtype == "fp8" else 2
+    kv = int(2 * ctx.sum() * w.num_kv_heads * w.head_size * e_kv)
+    qo = int(w.num_seqs * w.num_q_heads * w.head_size * (2 + 2))
+    meta = int(np.sum(-(-ctx // w.block_size)) * 4 + 4 * w.num_seqs)
+    scales = 8 if w.k_scale is not None else 0
+    write = int(w.num_seqs * (8 + 2 * w.num_kv_heads * w.head_size * (2 + e_kv)))
+    return kv, kv + qo + meta + scales, write
+
+
+def cpu_baseline_decode(torch, t, w, oracle):
+    """The oracle (all host threads) on the same step: new-token write + attention."""
+    cdt = oracle.FP8_E4M3FN if w.cache_dtype == "fp8" else oracle.BF16
+    raw = torch.uint8 if w.cache_dtype == "fp8" else torch.int16
+    npv = np.uint8 if w.cache_dtype == "fp8" else np.uint16
+    kc = t["kc"].view(raw).cpu().numpy().view(npv)
+    vc = t["vc"].view(raw).cpu().numpy().view(npv)
+    q = t["q"].view(torch.int16).cpu().numpy().view(np.uint16)
+    nk = t["new_k"].view(torch.int16).cpu().numpy().view(np.uint16)
+    nv = t["new_v"].view(torch.int16).cpu().numpy().view(np.uint16)
+    kv_bytes, _, _ = decode_bytes(w)
+    t0 = time.perf_counter()
+    oracle.reshape_and_cache(nk, nv, oracle.BF16, kc, vc, cdt, w.new_token_slots,
+                             k_scale=w.k_scale, v_scale=w.v_scale)
+    oracle.decode_attention(q, oracle.BF16, kc, vc, cdt, w.block_tables, w.context_lens,
+                            w.softmax_scale, w.k_scale, w.v_scale)
+    dt = time.perf_counter() - t0
+    return {"value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": cpu_cores(),
+            "kind": "oracle",
+            "sample": f"the whole step ({w.num_seqs} sequences, {int(w.context_lens.sum())} cached "
+                      f"tokens): oracle write of the new tokens + fp64 attention, {dt:.2f} s, "
+                      f"KV-read bytes / time"}
+
+
+def run_decode(args, torch, pkv, workloads, w, metric_name):
+    t = setup_decode(torch, pkv, workloads, w)
+    stream = torch.cuda.current_stream()
+    if args.profile_steps:
+        for _ in range(args.profile_steps):
+            decode_write(pkv, t, w)
+            decode_attn(pkv, t, w)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_steps": args.profile_steps, "workload": w.name}))
+        return
+    for _ in range(args.warmup):
+        decode_write(pkv, t, w)
+        decode_attn(pkv, t, w)
+    torch.cuda.synchronize()
+    # (1) the contract: K back-to-back steps between two synchronisations
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        decode_write(pkv, t, w)
+        decode_attn(pkv, t, w)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    # (2) per-call durations on the launch stream (attention = split pass + merge pass)
+    ta, tw = Timer(torch, stream), Timer(torch, stream)
+    for _ in range(args.steps):
+        tw.start()
+        decode_write(pkv, t, w)
+        tw.stop()
+        ta.start()
+        decode_attn(pkv, t, w)
+        ta.stop()
+    torch.cuda.synchronize()
+    # (3) cold: the 256 MB Infinity Cache flushed before every attention call
+    flush_src = torch.empty(MALL_FLUSH_BYTES // 2, dtype=torch.uint8, device="cuda")
+    flush_dst = torch.empty_like(flush_src)
+    tc = Timer(torch, stream)
+    for _ in range(max(3, args.steps // 5)):
+        pkv.hbm_copy(flush_dst, flush_src)
+        tc.start()
+        decode_attn(pkv, t, w)
+        tc.stop()
+    torch.cuda.synchronize()
+    # (4) the streaming-copy reference on the same device (read + write bytes)
+    tcopy = Timer(torch, stream)
+    for _ in range(5):
+        tcopy.start()
+        pkv.hbm_copy(flush_dst, flush_src)
+        tcopy.stop()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * flush_src.numel() / (tcopy.mean_ms() * 1e-3) / 1e9
+    del flush_src, flush_dst
+
+    kv, attn_bytes, write_bytes = decode_bytes(w)
+    attn_ms, write_ms, cold_ms = ta.mean_ms(), tw.mean_ms(), tc.mean_ms()
+    achieved = attn_bytes / (attn_ms * 1e-3) / 1e9
+    value = kv / (ms_per_step * 1e-3) / 1e9
+    res = {
+        "metric": metric_name,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.cache_dtype == "bf16" else "fp8_e4m3fn",
+        "data": "synthetic (seeded N(0,1) K/V/q of Qwen3-0.6B shapes)",
+        "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_size": w.head_size,
+                   "block_size": w.block_size, "num_blocks": w.num_blocks,
+                   "context_lens": f"{int(w.context_lens.min())}..{int(w.context_lens.max())} "
+                                   f"(sum {int(w.context_lens.sum())})",
+                   "kv_read_bytes_per_step": kv},
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
+        "tokens_per_s": round(w.num_seqs / (ms_per_step * 1e-3), 1),
+        "attention": {"ms": round(attn_ms, 5), "bytes": attn_bytes,
+                      "GBps": round(achieved, 2), "cold_ms": round(cold_ms, 5),
+                      "cold_GBps": round(attn_bytes / (cold_ms * 1e-3) / 1e9, 2)},
+        "cache_write": {"ms": round(write_ms, 5), "bytes": write_bytes,
+                        "GBps": round(write_bytes / (write_ms * 1e-3) / 1e9, 2),
+                        "tokens": w.num_seqs},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic_from_profiles("decode_attention", w.name)},
+        "hbm_copy_GBps": round(copy_gbps, 1),
+        "frac_of_copy": round(achieved / copy_gbps, 4),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        res["cpu_baseline"] = cpu_baseline_decode(torch, t, w, oracle)
+    print(json.dumps(res))
+
+
+def traffic_from_profiles(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken on
+    the current kernel source; otherwise None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.md")
+    src = os.path.join(ROOT, "paged_kv_cache_304_amd", "csrc", f"{kernel}.hip")
+    if not os.path.exists(path) or not os.path.exists(src):
+        return None
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.startswith("- "):
+            k, v = line[2:].split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("source_sha256_16") != sha:
+        return None
+    try:
+        return int(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# --------------------------------------------------------------------------- #
+# other workloads (measurement of the parity-test configurations)
+# --------------------------------------------------------------------------- #
+
+def run_prefill_fp8(args, torch, pkv, workloads):
+    w = workloads.prefill_write_fp8()
+    T, H, D, BS, NB = w["num_tokens"], w["num_heads"], w["head_size"], w["block_size"], w["num_blocks"]
+    key = workloads.device_normal((T, H, D), torch.bfloat16, "cuda", w["seed"], std=w["std"])
+    val = workloads.device_normal((T, H, D), torch.bfloat16, "cuda", w["seed"] + 1, std=w["std"])
+    kc = torch.empty((NB, BS, H, D), dtype=torch.float8_e4m3fn, device="cuda")
+    vc = torch.empty_like(kc)
+    slots = torch.from_numpy(w["slot_mapping"]).cuda()
+    ks = torch.tensor([w["k_scale"]], device="cuda")
+    vs = torch.tensor([w["v_scale"]], device="cuda")
+
+    def step():
+        pkv.reshape_and_cache(key, val, kc, vc, slots, k_scale=ks, v_scale=vs)
+
+    kept = int((w["slot_mapping"] >= 0).sum())
+    nbytes = 8 * T + kept * 2 * H * D * (2 + 1)
+    return generic(args, torch, pkv, step, nbytes, "reshape_and_cache",
+                   "bulk_prefill_write_32768_bf16_to_fp8", "fp8_e4m3fn", T, "tokens_per_s")
+
+
+def run_mla(args, torch, pkv, workloads):
+    w = workloads.mla_concat_swa()
+    T, H, nope, rope, BS, NB = (w["num_tokens"], w["num_heads"], w["nope_dim"], w["rope_dim"],
+                                w["block_size"], w["num_blocks"])
+    kn = workloads.device_normal((T, H, nope), torch.bfloat16, "cuda", w["seed"])
+    kr = workloads.device_normal((T, 1, rope), torch.bfloat16, "cuda", w["seed"] + 1)
+    k = torch.empty((T, H, nope + rope), dtype=torch.float32, device="cuda")
+    cache = torch.empty((NB, BS, H, nope + rope), dtype=torch.bfloat16, device="cuda")
+    slots = torch.from_numpy(w["slot_mapping"]).cuda()
+    swa = torch.from_numpy(w["swa_slot_mapping"]).cuda()
+
+    def step():
+        pkv.concat_and_cast_mla_k(k, kn, kr)
+        pkv.reshape_and_cache(k, None, cache, None, slots, swa)
+
+    kept = int((oracle_free_resolve(w) >= 0).sum())
+    cat_bytes = T * H * nope * 2 + T * rope * 2 + T * H * (nope + rope) * 4
+    write_bytes = 8 * T + 8 * T + kept * H * (nope + rope) * (4 + 2)
+    return generic(args, torch, pkv, step, cat_bytes + write_bytes, "concat_and_cast",
+                   "mla_concat_16384x128_then_swa_write", "bf16", T, "tokens_per_s")
+
+
+def oracle_free_resolve(w):
+    """Final slot per token for the MLA workload's two-stage table (host bookkeeping)."""
+    s = w["slot_mapping"]
+    fin = np.where(s >= 0, w["swa_slot_mapping"][np.maximum(s, 0)], -1)
+    return fin
+
+
+def run_decode_fp8(args, torch, pkv, workloads):
+    w = workloads.mixed_decode_fp8()
+    return run_decode(args, torch, pkv, workloads, w,
+                      "paged decode attn KV-read GB/s & % HBM peak; cache-write GB/s (1 MI355X)")
+
+
+def generic(args, torch, pkv, step, nbytes, kernel, name, dtype, units, unit_name):
+    stream = torch.cuda.current_stream()
+    if args.profile_steps:
+        for _ in range(args.profile_steps):
+            step()
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_steps": args.profile_steps, "workload": name}))
+        return
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "paged decode attn KV-read GB/s & % HBM peak; cache-write GB/s (1 MI355X)",
+        "value": round(gbps, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
+        "config": {"workload": name, "bytes_per_step": nbytes},
+        "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+        unit_name: round(units / (ms * 1e-3), 1),
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic_from_profiles(kernel, name)},
+    }))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the paged "
+              "KV cache kernels shard by sequence or KV head with no exchange; see the design "
+              "notes)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import paged_kv_cache_304_amd as pkv
+    import workloads
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    metric = "paged decode attn KV-read GB/s & % HBM peak; cache-write GB/s (1 MI355X)"
+    if args.workload == "decode_b64":
+        run_decode(args, torch, pkv, workloads, workloads.qwen3_decode_b64(), metric)
+    elif args.workload == "decode_fp8_b256":
+        run_decode_fp8(args, torch, pkv, workloads)
+    elif args.workload == "prefill_fp8":
+        run_prefill_fp8(args, torch, pkv, workloads)
+    else:
+        run_mla(args, torch, pkv, workloads)
+
+
+if __name__ == "__main__":
+    main()

@@ -167,7 +167,7 @@ def concat_and_cast(k, k_dtype: int, k_nope, nope_dtype: int, k_rope, rope_dtype
     rope = k_rope.shape[2]
     assert KD == nope + rope and k_rope.shape[1] == 1 and k_nope.shape[:2] == (T, H)
     for a in (k, k_nope, k_rope):
-        assert a.strides[2] == a.itemsize
+        assert a.size == 0 or a.strides[2] == a.itemsize
     es = lambda a, i: a.strides[i] // a.itemsize  # noqa: E731
     lib.orc_concat_and_cast(_ptr(k), k_dtype, es(k, 0), es(k, 1), _ptr(k_nope), nope_dtype,
                             es(k_nope, 0), es(k_nope, 1), _ptr(k_rope), rope_dtype, es(k_rope, 0),

@@ -1,0 +1,176 @@
+// Device-side helpers shared by the gfx950 kernels of the paged KV cache
+// library: element conversions, 8-element vector loads/stores and wave-level
+// reductions. Everything here is CDNA4-specific (wave64, DPP row operations).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+enum class Ty : int { BF16 = 0, F32 = 2, FP8 = 3 };
+
+template <Ty T> struct TyInfo;
+template <> struct TyInfo<Ty::BF16> { using Storage = uint16_t; static constexpr int kBytes = 2; };
+template <> struct TyInfo<Ty::F32> { using Storage = float; static constexpr int kBytes = 4; };
+template <> struct TyInfo<Ty::FP8> { using Storage = uint8_t; static constexpr int kBytes = 1; };
+
+// ------------------------------------------------------------------ decoding
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Two OCP e4m3fn codes (bytes 0,1 or 2,3 of w) -> two fp32 values. gfx950's
+// conversion instruction decodes the OCP format exactly (every code is a
+// float32 value).
+__device__ __forceinline__ f32x2 fp8x2_lo(uint32_t w) { return __builtin_amdgcn_cvt_pk_f32_fp8(w, false); }
+__device__ __forceinline__ f32x2 fp8x2_hi(uint32_t w) { return __builtin_amdgcn_cvt_pk_f32_fp8(w, true); }
+
+// ------------------------------------------------------------------ encoding
+
+// fp32 -> bf16, round to nearest even on the 16 dropped bits; overflow
+// carries into the exponent and gives inf; NaN keeps sign and top payload and
+// gets the quiet bit.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  uint32_t rne = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  uint32_t nan = (u >> 16) | 0x40u;
+  return ((u & 0x7FFFFFFFu) > 0x7F800000u) ? nan : rne;
+}
+
+// fp32 -> OCP e4m3fn, round to nearest even. |y| > 464 (past the midpoint
+// above 448), infinities and NaN give 0x7F with the sign of y.
+__device__ __forceinline__ uint32_t f32_to_fp8(float y) {
+  uint32_t u = __float_as_uint(y);
+  uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7FFFFFFFu;
+  // normal range [2^-6, 464]: keep 3 mantissa bits, RNE on the 20 dropped bits,
+  // rebias the exponent from 127 to 7
+  uint32_t normal = ((a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
+  // below 2^-6 the grid step is 2^-9: the code is |y| * 2^9 rounded to even
+  uint32_t sub = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  uint32_t code = (a < 0x3C800000u) ? sub : normal;
+  code = (a > 0x43E80000u) ? 0x7Fu : code;
+  return sign | code;
+}
+
+// 8 source elements widened to fp32.
+template <Ty S> struct Load8;
+template <> struct Load8<Ty::BF16> {
+  using Raw = u32x4;
+  __device__ __forceinline__ static Raw load(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  }
+  __device__ __forceinline__ static void widen(const Raw& r, float (&f)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = bf16_lo(r[i]);
+      f[2 * i + 1] = bf16_hi(r[i]);
+    }
+  }
+};
+struct F32x8 { u32x4 a, b; };
+template <> struct Load8<Ty::F32> {
+  using Raw = F32x8;
+  __device__ __forceinline__ static Raw load(const void* p) {
+    const u32x4* q = reinterpret_cast<const u32x4*>(p);
+    return Raw{__builtin_nontemporal_load(q), __builtin_nontemporal_load(q + 1)};
+  }
+  __device__ __forceinline__ static void widen(const Raw& r, float (&f)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[i] = __uint_as_float(r.a[i]);
+      f[4 + i] = __uint_as_float(r.b[i]);
+    }
+  }
+};
+
+// 8 fp32 values rounded to the destination type and stored.
+template <Ty D> struct Store8;
+template <> struct Store8<Ty::BF16> {
+  __device__ __forceinline__ static void store(void* p, const float (&f)[8]) {
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = f32_to_bf16(f[2 * i]) | (f32_to_bf16(f[2 * i + 1]) << 16);
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+  }
+};
+template <> struct Store8<Ty::F32> {
+  __device__ __forceinline__ static void store(void* p, const float (&f)[8]) {
+    u32x4 a, b;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] = __float_as_uint(f[i]);
+      b[i] = __float_as_uint(f[4 + i]);
+    }
+    u32x4* q = reinterpret_cast<u32x4*>(p);
+    __builtin_nontemporal_store(a, q);
+    __builtin_nontemporal_store(b, q + 1);
+  }
+};
+template <> struct Store8<Ty::FP8> {
+  __device__ __forceinline__ static void store(void* p, const float (&f)[8]) {
+    u32x2 v;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      v[i] = f32_to_fp8(f[4 * i]) | (f32_to_fp8(f[4 * i + 1]) << 8) |
+             (f32_to_fp8(f[4 * i + 2]) << 16) | (f32_to_fp8(f[4 * i + 3]) << 24);
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p));
+  }
+};
+
+// Single elements (unaligned fallback paths).
+template <Ty S> __device__ __forceinline__ float load1(const void* p, int64_t i);
+template <> __device__ __forceinline__ float load1<Ty::BF16>(const void* p, int64_t i) {
+  return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(p)[i] << 16);
+}
+template <> __device__ __forceinline__ float load1<Ty::F32>(const void* p, int64_t i) {
+  return reinterpret_cast<const float*>(p)[i];
+}
+template <Ty D> __device__ __forceinline__ void store1(void* p, int64_t i, float f);
+template <> __device__ __forceinline__ void store1<Ty::BF16>(void* p, int64_t i, float f) {
+  reinterpret_cast<uint16_t*>(p)[i] = (uint16_t)f32_to_bf16(f);
+}
+template <> __device__ __forceinline__ void store1<Ty::F32>(void* p, int64_t i, float f) {
+  reinterpret_cast<float*>(p)[i] = f;
+}
+template <> __device__ __forceinline__ void store1<Ty::FP8>(void* p, int64_t i, float f) {
+  reinterpret_cast<uint8_t*>(p)[i] = (uint8_t)f32_to_fp8(f);
+}
+
+// ------------------------------------------------------- wave-level shuffles
+
+// DPP row operations act inside rows of 16 lanes.
+enum : int {
+  kDppQuadXor1 = 0xB1,       // quad_perm [1,0,3,2]
+  kDppQuadXor2 = 0x4E,       // quad_perm [2,3,0,1]
+  kDppRowHalfMirror = 0x141, // lane i <-> 7-i within each half row
+  kDppRowMirror = 0x140,     // lane i <-> 15-i within each row
+};
+
+template <int Ctrl>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), Ctrl, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of N lanes (N = 2, 4, 8, 16, 32 or 64); every lane of
+// a group receives the group's sum.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16 || N == 32 || N == 64, "group");
+  if constexpr (N >= 2) x += dpp<kDppQuadXor1>(x);
+  if constexpr (N >= 4) x += dpp<kDppQuadXor2>(x);
+  if constexpr (N >= 8) x += dpp<kDppRowHalfMirror>(x);
+  if constexpr (N >= 16) x += dpp<kDppRowMirror>(x);
+  if constexpr (N >= 32) x += __shfl_xor(x, 16, 64);
+  if constexpr (N >= 64) x += __shfl_xor(x, 32, 64);
+  return x;
+}
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+}  // namespace pa

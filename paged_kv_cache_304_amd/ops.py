@@ -1,0 +1,158 @@
+"""torch-tensor front ends of the C entry points (argument marshalling only).
+
+Each function checks what a tensor can tell (device, dtype, rank, strides),
+passes raw device pointers, element strides and the current HIP stream to the
+library, and raises ``PagedKVError`` on a non-OK status. All arithmetic happens
+in the HIP kernels.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import PA_BF16, PA_F32, PA_FP8_E4M3FN, check, lib
+
+_DTYPES = {torch.bfloat16: PA_BF16, torch.float32: PA_F32, torch.float8_e4m3fn: PA_FP8_E4M3FN}
+
+
+def _code(t: torch.Tensor, what: str) -> int:
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise _lib.PagedKVError(_lib.PA_EDTYPE, f"{what}: unsupported dtype {t.dtype}") from None
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _on_gpu(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("pagedkv: every tensor must live on the GPU")
+
+
+def _stream(stream=None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def reshape_and_cache(key: torch.Tensor, value: Optional[torch.Tensor], key_cache: torch.Tensor,
+                      value_cache: Optional[torch.Tensor], slot_mapping: torch.Tensor,
+                      swa_slot_mapping: Optional[torch.Tensor] = None,
+                      k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
+                      stream=None) -> None:
+    """Write ``key``/``value`` [T, H, D] into ``key_cache``/``value_cache`` [NB, BS, H, D]."""
+    _on_gpu(key, value, key_cache, value_cache, slot_mapping, swa_slot_mapping, k_scale, v_scale)
+    if key.dim() != 3 or key_cache.dim() != 4:
+        raise ValueError("key must be [T, H, D] and key_cache [NB, BS, H, D]")
+    T, H, D = key.shape
+    NB, BS, H2, D2 = key_cache.shape
+    if (H2, D2) != (H, D):
+        raise ValueError(f"cache heads/dims {(H2, D2)} differ from source {(H, D)}")
+    if key.stride(2) != 1 or key.stride(1) != D:
+        raise ValueError("key must have head stride D and unit dim stride")
+    if key_cache.stride(3) != 1 or key_cache.stride(2) != D or key_cache.stride(1) != H * D:
+        raise ValueError("key_cache inner [BS, H, D] must be contiguous")
+    if value is not None:
+        if value.shape != key.shape or value.stride(2) != 1 or value.stride(1) != D:
+            raise ValueError("value must match key")
+        if value_cache is None or value_cache.shape != key_cache.shape or \
+                value_cache.stride() != key_cache.stride() or value_cache.dtype != key_cache.dtype:
+            raise ValueError("value_cache must match key_cache")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != T:
+        raise ValueError("slot_mapping must be int64 [T]")
+    if swa_slot_mapping is not None and (swa_slot_mapping.dtype != torch.int64
+                                         or not swa_slot_mapping.is_contiguous()):
+        raise ValueError("swa_slot_mapping must be contiguous int64")
+    for s in (k_scale, v_scale):
+        if s is not None and (s.dtype != torch.float32 or s.numel() != 1):
+            raise ValueError("scales must be single fp32 device scalars")
+    check(lib.pa_reshape_and_cache(
+        key.data_ptr(), _ptr(value), _code(key, "key"), T, H, D, key.stride(0),
+        value.stride(0) if value is not None else 0, key_cache.data_ptr(), _ptr(value_cache),
+        _code(key_cache, "key_cache"), NB, BS, key_cache.stride(0),
+        slot_mapping.contiguous().data_ptr(), _ptr(swa_slot_mapping),
+        swa_slot_mapping.numel() if swa_slot_mapping is not None else 0,
+        _ptr(k_scale), _ptr(v_scale), _stream(stream)))
+
+
+def concat_and_cast_mla_k(k: torch.Tensor, k_nope: torch.Tensor, k_rope: torch.Tensor,
+                          stream=None) -> None:
+    """``k[t, h, :] = cast(k_nope[t, h, :] ++ k_rope[t, 0, :])`` in place."""
+    _on_gpu(k, k_nope, k_rope)
+    if k.dim() != 3 or k_nope.dim() != 3 or k_rope.dim() != 3:
+        raise ValueError("k, k_nope and k_rope must be 3-D")
+    T, H, KD = k.shape
+    if k_nope.shape[0] != T or k_rope.shape[0] != T:
+        raise ValueError("token counts differ")
+    if k_nope.shape[1] != H or k_rope.shape[1] != 1:
+        raise ValueError("k_nope must have k's heads and k_rope a single head")
+    nope, rope = k_nope.shape[2], k_rope.shape[2]
+    if KD != nope + rope:
+        raise ValueError("k's last dim must equal nope_dim + rope_dim")
+    for t in (k, k_nope, k_rope):
+        if t.numel() > 0 and t.stride(2) != 1:
+            raise ValueError("innermost strides must be 1")
+    check(lib.pa_concat_and_cast_mla_k(
+        k.data_ptr(), _code(k, "k"), k.stride(0), k.stride(1), k_nope.data_ptr(),
+        _code(k_nope, "k_nope"), k_nope.stride(0), k_nope.stride(1), k_rope.data_ptr(),
+        _code(k_rope, "k_rope"), k_rope.stride(0), T, H, nope, rope, _stream(stream)))
+
+
+def decode_attention_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int,
+                                    head_size: int, max_blocks_per_seq: int,
+                                    block_size: int) -> int:
+    n = int(lib.pa_decode_attention_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_size,
+                                                   max_blocks_per_seq, block_size))
+    if n == 0:
+        raise _lib.PagedKVError(_lib.PA_EINVAL, _lib.last_error())
+    return n
+
+
+def decode_attention(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tensor,
+                     value_cache: torch.Tensor, block_tables: torch.Tensor,
+                     context_lens: torch.Tensor, softmax_scale: float,
+                     k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Single-token paged decode attention; writes and returns ``out`` [B, H_Q, D]."""
+    _on_gpu(out, q, key_cache, value_cache, block_tables, context_lens, k_scale, v_scale, workspace)
+    B, HQ, D = q.shape
+    NB, BS, HKV, D2 = key_cache.shape
+    if D2 != D or out.shape != q.shape:
+        raise ValueError("q, out and cache head sizes differ")
+    if q.stride(2) != 1 or q.stride(1) != D or out.stride(2) != 1 or out.stride(1) != D:
+        raise ValueError("q and out must be [B, H_Q, D] with contiguous [H_Q, D]")
+    if key_cache.stride(3) != 1 or key_cache.stride(2) != D or key_cache.stride(1) != HKV * D:
+        raise ValueError("cache inner [BS, H_KV, D] must be contiguous")
+    if value_cache.shape != key_cache.shape or value_cache.stride() != key_cache.stride() or \
+            value_cache.dtype != key_cache.dtype:
+        raise ValueError("value_cache must match key_cache")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or \
+            block_tables.shape[0] != B or not block_tables.is_contiguous():
+        raise ValueError("block_tables must be contiguous int32 [B, W]")
+    if context_lens.dtype != torch.int32 or context_lens.numel() != B or \
+            not context_lens.is_contiguous():
+        raise ValueError("context_lens must be contiguous int32 [B]")
+    W = block_tables.shape[1]
+    need = decode_attention_workspace_size(max(B, 1), HQ, HKV, D, W, BS)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    check(lib.pa_decode_attention(
+        out.data_ptr(), _code(out, "out"), out.stride(0), q.data_ptr(), _code(q, "q"), q.stride(0),
+        key_cache.data_ptr(), value_cache.data_ptr(), _code(key_cache, "key_cache"), NB, BS,
+        key_cache.stride(0), block_tables.data_ptr(), W, context_lens.data_ptr(), B, HQ, HKV, D,
+        float(softmax_scale), _ptr(k_scale), _ptr(v_scale), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def hbm_copy(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:
+    """Streaming copy of ``src``'s bytes into ``dst`` (bandwidth reference kernel)."""
+    _on_gpu(dst, src)
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < n or not (src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("dst must be contiguous and at least as large as src")
+    check(lib.pa_hbm_copy(dst.data_ptr(), src.data_ptr(), n, _stream(stream)))

@@ -1,0 +1,167 @@
+"""The C-ABI library loads, exports every symbol the header declares, and rejects
+invalid host arguments with an error code before touching the GPU. CPU only:
+every call here fails validation, so nothing is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedkv.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from paged_kv_cache_304_amd import _lib
+    return _lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    decl = declared_functions()
+    assert set(decl) == set(L.EXPORTS)
+    for name in decl:
+        assert hasattr(L.lib, name), name
+        assert ctypes.cast(getattr(L.lib, name), ctypes.c_void_p).value
+
+
+def test_abi_version_matches_header(L):
+    m = re.search(r"#define PA_ABI_VERSION (\d+)", open(HEADER).read())
+    assert L.abi_version() == int(m.group(1))
+
+
+def test_status_and_dtype_codes_match_header(L):
+    text = open(HEADER).read()
+    for name in ("PA_OK", "PA_EINVAL", "PA_EDTYPE", "PA_EUNSUPPORTED", "PA_EHIP", "PA_EWORKSPACE",
+                 "PA_BF16", "PA_F32", "PA_FP8_E4M3FN"):
+        m = re.search(rf"\b{name}\s*=\s*(\d+)", text)
+        assert m and int(m.group(1)) == getattr(L, name), name
+
+
+def rac(L, **over):
+    args = dict(key=1 << 20, value=1 << 21, src=L.PA_BF16, T=4, H=8, D=128, ks=1024, vs=1024,
+                kc=1 << 22, vc=1 << 23, cache=L.PA_BF16, NB=4, BS=16, bstride=16 * 1024,
+                slots=1 << 24, swa=None, swa_len=0, k_scale=None, v_scale=None)
+    args.update(over)
+    a = args
+    return L.lib.pa_reshape_and_cache(a["key"], a["value"], a["src"], a["T"], a["H"], a["D"],
+                                      a["ks"], a["vs"], a["kc"], a["vc"], a["cache"], a["NB"],
+                                      a["BS"], a["bstride"], a["slots"], a["swa"], a["swa_len"],
+                                      a["k_scale"], a["v_scale"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(T=-1), "PA_EINVAL"),
+    (dict(H=0), "PA_EINVAL"),
+    (dict(BS=0), "PA_EINVAL"),
+    (dict(bstride=100), "PA_EINVAL"),
+    (dict(key=None), "PA_EINVAL"),
+    (dict(slots=None), "PA_EINVAL"),
+    (dict(value=None), "PA_EINVAL"),          # value_cache without value
+    (dict(ks=1000), "PA_EINVAL"),             # token stride < H*D
+    (dict(k_scale=1 << 25), "PA_EINVAL"),     # k_scale without v_scale while V is written
+    (dict(v_scale=1 << 25), "PA_EINVAL"),     # v_scale without k_scale
+    (dict(src=3), "PA_EDTYPE"),               # fp8 source
+    (dict(cache=1), "PA_EDTYPE"),
+    (dict(swa=1 << 26, swa_len=-1), "PA_EINVAL"),
+])
+def test_reshape_and_cache_rejects(L, over, code):
+    assert rac(L, **over) == getattr(L, code)
+    assert L.last_error().startswith("pa_reshape_and_cache")
+
+
+def test_reshape_and_cache_zero_tokens_is_noop(L):
+    assert rac(L, T=0, key=None, slots=None) == L.PA_OK
+
+
+def cat(L, **over):
+    a = dict(k=1 << 20, kdt=L.PA_F32, k0=128 * 192, k1=192, nope=1 << 21, ndt=L.PA_BF16, n0=128 * 128,
+             n1=128, rope=1 << 22, rdt=L.PA_BF16, r0=64, T=4, H=128, nd=128, rd=64)
+    a.update(over)
+    return L.lib.pa_concat_and_cast_mla_k(a["k"], a["kdt"], a["k0"], a["k1"], a["nope"], a["ndt"],
+                                          a["n0"], a["n1"], a["rope"], a["rdt"], a["r0"], a["T"],
+                                          a["H"], a["nd"], a["rd"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(T=-2), "PA_EINVAL"),
+    (dict(H=0), "PA_EINVAL"),
+    (dict(k1=100), "PA_EINVAL"),          # k rows overlap
+    (dict(k0=100), "PA_EINVAL"),
+    (dict(n1=10), "PA_EINVAL"),
+    (dict(rdt=2), "PA_EDTYPE"),           # rope dtype differs from nope dtype
+    (dict(ndt=3, rdt=3), "PA_EDTYPE"),    # fp8 source
+    (dict(k=None), "PA_EINVAL"),
+])
+def test_concat_rejects(L, over, code):
+    assert cat(L, **over) == getattr(L, code)
+
+
+def attn(L, **over):
+    a = dict(out=1 << 20, odt=L.PA_BF16, os=2048, q=1 << 21, qdt=L.PA_BF16, qs=2048, kc=1 << 22,
+             vc=1 << 23, cdt=L.PA_BF16, NB=16, BS=16, bstride=16 * 8 * 128, bt=1 << 24, W=4,
+             cl=1 << 25, B=2, HQ=16, HKV=8, D=128, scale=0.088, ks=None, vs=None, ws=1 << 26,
+             wsb=1 << 30)
+    a.update(over)
+    return L.lib.pa_decode_attention(a["out"], a["odt"], a["os"], a["q"], a["qdt"], a["qs"],
+                                     a["kc"], a["vc"], a["cdt"], a["NB"], a["BS"], a["bstride"],
+                                     a["bt"], a["W"], a["cl"], a["B"], a["HQ"], a["HKV"], a["D"],
+                                     a["scale"], a["ks"], a["vs"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(HQ=12), "PA_EINVAL"),              # 12 % 8
+    (dict(HQ=24, HKV=8), "PA_EUNSUPPORTED"),  # G = 3
+    (dict(D=96), "PA_EUNSUPPORTED"),
+    (dict(BS=2), "PA_EUNSUPPORTED"),          # not a multiple of 4 rows at D=128
+    (dict(B=-1), "PA_EINVAL"),
+    (dict(W=0), "PA_EINVAL"),
+    (dict(odt=3), "PA_EDTYPE"),
+    (dict(qdt=2), "PA_EDTYPE"),
+    (dict(cdt=2), "PA_EDTYPE"),
+    (dict(scale=float("nan")), "PA_EINVAL"),
+    (dict(os=100), "PA_EINVAL"),
+    (dict(bstride=10), "PA_EINVAL"),
+    (dict(q=None), "PA_EINVAL"),
+    (dict(bt=None), "PA_EINVAL"),
+    (dict(wsb=16), "PA_EWORKSPACE"),
+    (dict(ws=(1 << 26) + 4), "PA_EWORKSPACE"),
+    (dict(q=(1 << 21) + 2), "PA_EINVAL"),     # misaligned q
+])
+def test_decode_attention_rejects(L, over, code):
+    assert attn(L, **over) == getattr(L, code)
+    assert L.last_error()
+
+
+def test_decode_attention_zero_seqs_is_noop(L):
+    assert attn(L, B=0, q=None, out=None) == L.PA_OK
+
+
+def test_workspace_size_is_pure_and_validates(L):
+    f = L.lib.pa_decode_attention_workspace_size
+    n = f(64, 16, 8, 128, 256, 16)
+    assert n > 0 and n == f(64, 16, 8, 128, 256, 16) and n % 256 == 0
+    assert f(64, 16, 8, 96, 256, 16) == 0 and "head_size" in L.last_error()
+    assert f(64, 12, 8, 128, 256, 16) == 0
+
+
+def test_hbm_copy_rejects(L):
+    assert L.lib.pa_hbm_copy(None, 1 << 20, 64, None) == L.PA_EINVAL
+    assert L.lib.pa_hbm_copy(1 << 20, (1 << 20) + 16, 64, None) == L.PA_EINVAL  # overlap
+    assert L.lib.pa_hbm_copy(1 << 20, 1 << 22, 0, None) == L.PA_OK
+
+
+def test_product_package_does_not_reach_the_oracle():
+    pkg = os.path.join(ROOT, "paged_kv_cache_304_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "liboracle" not in text and "orc_" not in text, f

@@ -1,0 +1,266 @@
+"""GPU parity of the cache write and the MLA K concat against the CPU oracle:
+bit-exact over whole sentinel-filled caches (untouched bytes must keep the
+sentinel), on small ragged cases, on every bf16 input pattern, and at the full
+bulk-prefill and MLA sizes."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity_util import sentinel, say, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+BF16, F32, FP8 = oracle.BF16, oracle.F32, oracle.FP8_E4M3FN
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def pkv():
+    import paged_kv_cache_304_amd as m
+    return m
+
+
+def run_write(key, value, src_dt, kc, vc, cache_dt, slots, swa=None, k_scale=None, v_scale=None,
+              key_token_stride=None, pad=0):
+    """Same inputs through the oracle and the GPU; returns (oracle caches, GPU caches)."""
+    ok, ov = kc.copy(), (None if vc is None else vc.copy())
+    oracle.reshape_and_cache(key, value, src_dt, ok, ov, cache_dt, slots, swa, k_scale, v_scale,
+                             key_token_stride=key_token_stride,
+                             value_token_stride=key_token_stride)
+    T = slots.shape[0]
+    H, D = kc.shape[2], kc.shape[3]
+    dk = to_dev(key, src_dt)
+    if pad:
+        dk = dk.view(T, H * D + pad)[:, :H * D].view(T, H, D) if dk.dim() == 2 else dk
+    dv = None if value is None else to_dev(value, src_dt)
+    if pad and dv is not None:
+        dv = dv.view(T, H * D + pad)[:, :H * D].view(T, H, D)
+    gk = to_dev(kc, cache_dt)
+    gv = None if vc is None else to_dev(vc, cache_dt)
+    dsl = torch.from_numpy(slots).cuda()
+    dswa = None if swa is None else torch.from_numpy(swa).cuda()
+    ks = None if k_scale is None else torch.tensor([k_scale], dtype=torch.float32, device="cuda")
+    vs = None if v_scale is None else torch.tensor([v_scale], dtype=torch.float32, device="cuda")
+    pkv().reshape_and_cache(dk, dv, gk, gv, dsl, dswa, ks, vs if dv is not None else None)
+    torch.cuda.synchronize()
+    return (ok, ov), (to_host(gk, cache_dt), None if gv is None else to_host(gv, cache_dt))
+
+
+def draw_src(rng, shape, dt, std=1.0):
+    if dt == BF16:
+        return workloads.normal_bf16_bits(rng, shape, std)
+    return (rng.standard_normal(shape) * std).astype(np.float32)
+
+
+def test_tiny_two_sequence_write():
+    say("reshape_and_cache tiny two-sequence workload bf16->bf16")
+    w = workloads.tiny_paged()
+    shape = (w["num_blocks"], w["block_size"], w["num_kv_heads"], w["head_size"])
+    kc, vc = sentinel(shape, BF16, 0xA5), sentinel(shape, BF16, 0xA5)
+    (ok, ov), (gk, gv) = run_write(w["key"], w["value"], BF16, kc, vc, BF16, w["slot_mapping"])
+    assert np.array_equal(gk, ok) and np.array_equal(gv, ov)
+
+
+CASES = [
+    # name, src, cache, scale, swa, T, H, D, NB, BS, pad, kv
+    ("bf16->bf16", BF16, BF16, False, False, 1001, 8, 128, 80, 16, 0, True),
+    ("bf16->fp8 /scale", BF16, FP8, True, False, 1001, 8, 128, 80, 16, 0, True),
+    ("f32->bf16", F32, BF16, False, False, 777, 4, 64, 64, 16, 0, True),
+    ("bf16->f32", BF16, F32, False, False, 513, 2, 64, 40, 16, 0, True),
+    ("f32->f32", F32, F32, False, False, 130, 2, 32, 20, 8, 0, True),
+    ("bf16->bf16 /scale", BF16, BF16, True, False, 300, 8, 128, 20, 16, 0, True),
+    ("f32->fp8 /scale swa", F32, FP8, True, True, 600, 8, 128, 50, 16, 0, True),
+    ("bf16->bf16 swa K-only", BF16, BF16, False, True, 999, 8, 128, 70, 16, 0, False),
+    ("bf16->bf16 padded source rows", BF16, BF16, False, False, 257, 8, 128, 20, 16, 24, True),
+    ("scalar path H*D%8!=0 bf16->fp8", BF16, FP8, True, False, 203, 3, 5, 20, 16, 0, True),
+    ("scalar path f32->bf16 odd block", F32, BF16, False, True, 150, 3, 6, 30, 7, 0, True),
+    ("long rows (row split over gridDim.y)", BF16, BF16, False, False, 37, 64, 256, 3, 16, 0, True),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_write_matches_oracle_bit_exact(case):
+    name, src, cache, scale, use_swa, T, H, D, NB, BS, pad, kv = case
+    say(f"reshape_and_cache {name} T={T} H={H} D={D} NB={NB} BS={BS}")
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    pool = NB * BS
+    if pad:
+        key = draw_src(rng, (T, H * D + pad), src, 2.0)
+        value = draw_src(rng, (T, H * D + pad), src, 2.0)
+    else:
+        key = draw_src(rng, (T, H, D), src, 2.0)
+        value = draw_src(rng, (T, H, D), src, 2.0)
+    if use_swa:
+        slots = rng.permutation(T + 40)[:T].astype(np.int64)          # first stage
+        swa = rng.permutation(pool)[:T + 40].astype(np.int64)         # second stage
+        swa[rng.choice(T + 40, size=(T + 40) // 10, replace=False)] = -1
+        swa[3] = pool + 5                                             # outside the pool
+        slots[rng.choice(T, size=T // 20, replace=False)] = -1
+        slots[7] = T + 1000                                           # beyond the table
+    else:
+        swa = None
+        slots = rng.permutation(pool)[:T].astype(np.int64)
+        slots[rng.choice(T, size=T // 20, replace=False)] = -1
+        slots[5] = pool + 3                                           # outside the pool
+        slots[6] = -12345
+    byte = 0x7F if cache == FP8 else 0xA5
+    kc = sentinel((NB, BS, H, D), cache, byte)
+    vc = sentinel((NB, BS, H, D), cache, byte) if kv else None
+    ks, vs = (0.05, 0.04) if scale else (None, None)
+    stride = H * D + pad if pad else None
+    (ok, ov), (gk, gv) = run_write(key, value if kv else None, src, kc, vc, cache, slots, swa,
+                                   ks, vs if kv else None, key_token_stride=stride, pad=pad)
+    assert np.array_equal(gk.view(np.uint8), ok.view(np.uint8))
+    if kv:
+        assert np.array_equal(gv.view(np.uint8), ov.view(np.uint8))
+
+
+@pytest.mark.parametrize("scale", [0.05, 0.04, 1.0, 3.0e-3])
+def test_every_bf16_pattern_through_the_fp8_write(scale):
+    """All 65,536 bf16 inputs (NaN, inf, subnormals, -0 included) through the scaled
+    fp8 write, as 64 tokens of [8, 128]."""
+    say(f"reshape_and_cache exhaustive bf16->fp8 scale={scale}")
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16).reshape(64, 8, 128)
+    slots = np.arange(64, dtype=np.int64)[::-1].copy()
+    kc = sentinel((4, 16, 8, 128), FP8, 0x00)
+    vc = sentinel((4, 16, 8, 128), FP8, 0x00)
+    (ok, ov), (gk, gv) = run_write(bits, bits, BF16, kc, vc, FP8, slots, None, scale, scale)
+    assert np.array_equal(gk, ok) and np.array_equal(gv, ov)
+    ref = oracle.encode_bf16_to_fp8_scaled(bits.ravel(), scale)
+    assert np.array_equal(gk.reshape(64, -1)[::-1].ravel(), ref)
+
+
+def test_fp32_specials_through_bf16_and_fp8_writes():
+    say("reshape_and_cache fp32 specials -> bf16 and fp8")
+    rng = np.random.default_rng(77)
+    raw = rng.integers(0, 2**32, size=64 * 1024, dtype=np.uint64).astype(np.uint32)
+    special = np.array([0x7F800000, 0xFF800000, 0x7FC00000, 0xFFC00001, 0x7F800001, 0x00000001,
+                        0x80000001, 0x007FFFFF, 0x7F7FFFFF, 0xFF7FFFFF, 0x43E80000, 0x43E80001,
+                        0x43E7FFFF, 0x3C800000, 0x3C7FFFFF, 0x3A800000, 0x3A800001, 0x80000000,
+                        0x3F808000, 0x3F818000, 0x3F80FFFF, 0x3F817FFF], dtype=np.uint32)
+    raw[:special.size] = special
+    x = raw.view(np.float32).reshape(64, 8, 128)
+    slots = np.arange(64, dtype=np.int64)
+    for cache in (BF16, FP8):
+        kc = sentinel((4, 16, 8, 128), cache, 0x11)
+        (ok, _), (gk, _) = run_write(x, None, F32, kc, None, cache, slots)
+        assert np.array_equal(gk.view(np.uint8), ok.view(np.uint8)), cache
+
+
+def test_empty_and_all_skipped():
+    say("reshape_and_cache empty input and all-negative slots")
+    m = pkv()
+    kc = torch.full((4, 16, 8, 128), 7, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    key = torch.zeros((0, 8, 128), dtype=torch.bfloat16, device="cuda")
+    m.reshape_and_cache(key, None, kc, None, torch.zeros(0, dtype=torch.int64, device="cuda"))
+    key = torch.ones((33, 8, 128), dtype=torch.bfloat16, device="cuda")
+    m.reshape_and_cache(key, key, kc, kc.clone(), torch.full((33,), -1, dtype=torch.int64,
+                                                              device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.all(kc.view(torch.int16) == 7)
+
+
+def test_bulk_prefill_fp8_write_full_size():
+    """32,768 tokens, 5% skipped, 2*N(0,1) bf16 -> fp8 with k/v scales 0.05/0.04:
+    whole caches compared with the oracle."""
+    w = workloads.prefill_write_fp8()
+    T, H, D, BS, NB = w["num_tokens"], w["num_heads"], w["head_size"], w["block_size"], w["num_blocks"]
+    say(f"reshape_and_cache bulk prefill fp8 T={T}")
+    rng = workloads.rng_for(3, 1)
+    key = workloads.normal_bf16_bits(rng, (T, H, D), w["std"])
+    value = workloads.normal_bf16_bits(rng, (T, H, D), w["std"])
+    kc = sentinel((NB, BS, H, D), FP8, 0x7F)
+    vc = sentinel((NB, BS, H, D), FP8, 0x7F)
+    (ok, ov), (gk, gv) = run_write(key, value, BF16, kc, vc, FP8, w["slot_mapping"], None,
+                                   w["k_scale"], w["v_scale"])
+    assert np.array_equal(gk, ok) and np.array_equal(gv, ov)
+
+
+CAT_CASES = [
+    # name, src, dst, T, H, nope, rope, k padding
+    ("bf16->f32", BF16, F32, 37, 5, 16, 8, 0),
+    ("bf16->bf16 strided k", BF16, BF16, 50, 6, 32, 16, 24),
+    ("f32->bf16", F32, BF16, 33, 4, 64, 32, 0),
+    ("bf16->fp8", BF16, FP8, 20, 3, 16, 16, 8),
+    ("f32->f32", F32, F32, 10, 2, 8, 8, 0),
+    ("scalar path nope=12 rope=4", BF16, F32, 21, 3, 12, 4, 0),
+    ("MLA shape 128 heads", BF16, F32, 9, 128, 128, 64, 0),
+    ("no rope part", BF16, F32, 9, 4, 32, 0, 0),
+]
+
+
+@pytest.mark.parametrize("case", CAT_CASES, ids=[c[0] for c in CAT_CASES])
+def test_concat_matches_oracle_bit_exact(case):
+    name, src, dst, T, H, nope, rope, padk = case
+    say(f"concat_and_cast {name} T={T} H={H} nope={nope} rope={rope}")
+    rng = np.random.default_rng(len(name) * 7 + T)
+    kn = draw_src(rng, (T, H, nope), src)
+    kr = draw_src(rng, (T, 1, rope), src) if rope else np.zeros((T, 1, 0),
+                                                                 dtype=kn.dtype)
+    kd = nope + rope
+    k_full = sentinel((T, H, kd + padk), dst, 0x3C)
+    ok = k_full.copy()
+    oracle.concat_and_cast(ok[:, :, :kd], dst, kn, src, kr, src)
+    gk_full = to_dev(k_full, dst)
+    gk = gk_full[:, :, :kd]
+    pkv().concat_and_cast_mla_k(gk, to_dev(kn, src), to_dev(kr, src))
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(gk_full, dst).view(np.uint8), ok.view(np.uint8))
+
+
+def test_mla_concat_then_swa_write_full_size():
+    """16,384 tokens x 128 heads: concat to fp32, then the bf16 K-only write through the
+    SWA table. Sampled tokens are compared with the oracle element by element; the
+    closed form of the widening and the set of written slots are checked whole."""
+    w = workloads.mla_concat_swa()
+    T, H, nope, rope, BS, NB = (w["num_tokens"], w["num_heads"], w["nope_dim"], w["rope_dim"],
+                                w["block_size"], w["num_blocks"])
+    say(f"concat_and_cast + SWA write full size T={T} H={H}")
+    m = pkv()
+    kn = workloads.device_normal((T, H, nope), torch.bfloat16, "cuda", w["seed"])
+    kr = workloads.device_normal((T, 1, rope), torch.bfloat16, "cuda", w["seed"] + 1)
+    k = torch.empty((T, H, nope + rope), dtype=torch.float32, device="cuda")
+    m.concat_and_cast_mla_k(k, kn, kr)
+    torch.cuda.synchronize()
+    # closed form over the whole tensor: fp32 bits == bf16 bits << 16
+    kb = k.view(torch.int32)
+    assert torch.equal(kb[:, :, :nope], kn.view(torch.int16).to(torch.int32).bitwise_left_shift(16))
+    rope_bits = kr.view(torch.int16).to(torch.int32).bitwise_left_shift(16)
+    assert torch.equal(kb[:, :, nope:], rope_bits.expand(T, H, rope))
+    del kb, rope_bits
+    # sampled tokens through the oracle concat
+    rng = np.random.default_rng(55)
+    sample = np.sort(rng.choice(T, size=48, replace=False))
+    kn_h = to_host(kn[sample], BF16)
+    kr_h = to_host(kr[sample], BF16)
+    ok = np.zeros((sample.size, H, nope + rope), dtype=np.float32)
+    oracle.concat_and_cast(ok, F32, kn_h, BF16, kr_h, BF16)
+    assert np.array_equal(to_host(k[sample], F32).view(np.uint32), ok.view(np.uint32))
+    # the SWA-remapped K-only bf16 write
+    cache = torch.empty((NB, BS, H, nope + rope), dtype=torch.bfloat16, device="cuda")
+    cache.view(torch.int16).fill_(0x7FA5)
+    slots = torch.from_numpy(w["slot_mapping"]).cuda()
+    swa = torch.from_numpy(w["swa_slot_mapping"]).cuda()
+    m.reshape_and_cache(k, None, cache, None, slots, swa)
+    torch.cuda.synchronize()
+    final = oracle.resolve_slots(w["slot_mapping"], NB, BS, w["swa_slot_mapping"])
+    kept = np.flatnonzero(final >= 0)
+    rows = cache.view(NB * BS, H * (nope + rope))
+    untouched = torch.ones(NB * BS, dtype=torch.bool, device="cuda")
+    untouched[torch.from_numpy(final[kept]).cuda()] = False
+    assert torch.all(rows[untouched].view(torch.int16) == 0x7FA5)
+    # sampled kept tokens: oracle write of their fp32 rows vs the GPU rows at their slots
+    pick = np.sort(rng.choice(kept, size=64, replace=False))
+    src = to_host(k[pick], F32)
+    oc = np.zeros((1, 64, H, nope + rope), dtype=np.uint16)
+    oracle.reshape_and_cache(src, None, F32, oc, None, BF16, np.arange(64, dtype=np.int64))
+    got = to_host(rows[torch.from_numpy(final[pick]).cuda()], BF16)
+    assert np.array_equal(got.reshape(64, -1), oc.reshape(64, -1))
