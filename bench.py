@@ -31,6 +31,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0
 MALL_FLUSH_BYTES = 1 << 30   # > 256 MB Infinity Cache
+COPY_CAL_BYTES = 512 << 20
 
 
 def parse():
@@ -100,7 +101,7 @@ def setup_decode(torch, pkv, workloads, w):
     t["ks"] = None if w.k_scale is None else torch.tensor([w.k_scale], device=dev)
     t["vs"] = None if w.v_scale is None else torch.tensor([w.v_scale], device=dev)
     need = pkv.decode_attention_workspace_size(B, HQ, HKV, D, w.width, BS)
-    t["ws"] = torch.empty(need, dtype=torch.uint8, device=dev)
+    t["ws"] = torch.zeros(need, dtype=torch.uint8, device=dev)
     return t
 
 
@@ -157,6 +158,7 @@ def run_decode(args, torch, pkv, workloads, w, metric_name):
     t = setup_decode(torch, pkv, workloads, w)
     stream = torch.cuda.current_stream()
     if args.profile_steps:
+        copy_calibration(torch, pkv)
         for _ in range(args.profile_steps):
             decode_write(pkv, t, w)
             decode_attn(pkv, t, w)
@@ -250,6 +252,17 @@ def run_decode(args, torch, pkv, workloads, w, metric_name):
     print(json.dumps(res))
 
 
+def copy_calibration(torch, pkv):
+    """Three 512 MiB streaming copies (the reference kernel for profiler byte
+    counters: 512 MiB read and 512 MiB written per launch)."""
+    src = torch.empty(COPY_CAL_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        pkv.hbm_copy(dst, src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def traffic_from_profiles(kernel: str, workload: str):
     """HBM bytes per launch from the committed counter summary, if it was taken on
     the current kernel source; otherwise None."""
@@ -334,6 +347,7 @@ def run_decode_fp8(args, torch, pkv, workloads):
 def generic(args, torch, pkv, step, nbytes, kernel, name, dtype, units, unit_name):
     stream = torch.cuda.current_stream()
     if args.profile_steps:
+        copy_calibration(torch, pkv)
         for _ in range(args.profile_steps):
             step()
         torch.cuda.synchronize()

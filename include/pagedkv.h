@@ -186,7 +186,8 @@ size_t pa_decode_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads,
  *   k_scale, v_scale  device fp32 scalars or NULL (= 1.0).
  *   workspace, workspace_bytes  device scratch of at least
  *            pa_decode_attention_workspace_size(...) bytes, 256-byte aligned;
- *            its contents on entry do not matter.
+ *            it receives the per-split partial results, so its contents on
+ *            entry do not matter. Concurrent calls must not share it.
  * Supported: head_size in {64, 128, 256}; num_q_heads % num_kv_heads == 0;
  *   num_q_heads / num_kv_heads <= 16.
  * Errors: PA_EINVAL, PA_EDTYPE, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_EHIP.

@@ -7,24 +7,33 @@
 // and q head h, softmax over the first ctx_b cached positions of
 // scale * q . K^ (K^ = K * k_scale), weights applied to V^ = V * v_scale.
 //
-// gfx950 design (split-K, two launches):
-//  * Pass 1: workgroup = (KV split, sequence, KV-head group); one wavefront per
-//    KV head, so the waves of a workgroup together read every head of the same
-//    physical blocks, i.e. whole contiguous [block_size, H_KV, D] pages. A
-//    wave's 64 lanes cover RPL = 64 / (D/8) cache rows of one head per load
-//    (8 elements = 16 bytes of bf16 or 8 bytes of fp8 per lane); the QK dot of
-//    a row is reduced over its D/8 lanes with DPP row operations. Each row of
-//    lanes keeps its own online-softmax state (max, sum, accumulators for the
-//    G query heads that share the KV head), updated once per 4 loads; the RPL
-//    row states are merged with lane shuffles at the end of the split.
-//    Split boundaries depend only on logical block indices, so the result is
+// gfx950 design: split-K over logical blocks, then a merge launch.
+//  * Workgroup = (KV-head group, KV split, sequence) with one wavefront per KV
+//    head, so the waves of a workgroup read every head of the same physical
+//    blocks together, i.e. whole contiguous [block_size, H_KV, D] pages.
+//  * Matrix-core path (block_size a multiple of 16, D <= 128): a tile is 16 positions of
+//    one head. QK^T is one v_mfma_f32_16x16x32_bf16 per 32 head dims with the
+//    K tile as A (row = position) and the G query heads of the group as B
+//    columns, so lane l receives the scores of positions 4*(l/16)+r (r<4) for
+//    head l%16. Softmax runs there; P.V runs on the vector ALUs with V in a row
+//    layout (16 lanes per cache row, 4 rows per load) in which lane l needs
+//    exactly the probabilities of row group l/16, handed over by DPP
+//    row_newbcast. The next tile's K/V loads are issued before the current
+//    tile is computed. fp8 K is widened to bf16 exactly for the MFMA.
+//  * Vector path (other block sizes, D = 256): 8 elements per lane, a cache row spread
+//    over D/8 lanes, QK dots reduced with DPP row operations, one online-softmax
+//    state per row of lanes, merged with lane shuffles at the end.
+//  * A sequence that needs one split writes its output directly. Otherwise each
+//    split stores (max, sum, normalised output) per q head in the workspace and
+//    a second, small launch merges them (lanes over splits for the weights,
+//    lanes over dims for the outputs).
+//  * Split boundaries depend only on logical block indices, so the result is
 //    bit-identical under any relabelling of physical blocks.
-//  * Pass 2: one wavefront per (sequence, q head) merges the splits' (max,
-//    sum, normalised output) triples; sequences that fit one split were already
-//    written by pass 1.
-// Scores are kept in the log2 domain (scale * log2(e) folded in) so that the
-// exponentials are single v_exp_f32 instructions.
+// Scores are kept in the log2 domain (scale * log2(e) folded in) so that each
+// exponential is one v_exp_f32.
 #include <math.h>
+
+#include <type_traits>
 
 #include "pa_device.h"
 #include "pa_internal.h"
@@ -32,8 +41,39 @@
 namespace pa {
 namespace {
 
-constexpr int kMaxWaves = 8;       // KV heads (waves) per workgroup
-constexpr int kTargetWgs = 2048;   // pass-1 workgroups aimed for at full length
+#ifndef PA_DECODE_TARGET_WGS
+#define PA_DECODE_TARGET_WGS 1024
+#endif
+#ifndef PA_DECODE_MIN_SPLIT
+#define PA_DECODE_MIN_SPLIT 64
+#endif
+#ifndef PA_DECODE_MAX_SPLIT
+#define PA_DECODE_MAX_SPLIT 256
+#endif
+#ifndef PA_DECODE_NT_K
+#define PA_DECODE_NT_K 0
+#endif
+#ifndef PA_DECODE_NT_V
+#define PA_DECODE_NT_V 1
+#endif
+#ifndef PA_DECODE_PREFETCH
+#define PA_DECODE_PREFETCH 0
+#endif
+#ifndef PA_DECODE_MAX_WAVES
+#define PA_DECODE_MAX_WAVES 4
+#endif
+#ifndef PA_DECODE_WAVES_PER_EU
+#define PA_DECODE_WAVES_PER_EU 0
+#endif
+#if PA_DECODE_WAVES_PER_EU > 0
+#define PA_SPLIT_OCCUPANCY __attribute__((amdgpu_waves_per_eu(PA_DECODE_WAVES_PER_EU, 8)))
+#else
+#define PA_SPLIT_OCCUPANCY
+#endif
+constexpr int kMaxWaves = PA_DECODE_MAX_WAVES;        // KV heads (waves) per workgroup
+constexpr int kTargetWgs = PA_DECODE_TARGET_WGS;      // split workgroups aimed for if every sequence used all W blocks
+constexpr int kMinSplitTokens = PA_DECODE_MIN_SPLIT;  // positions per split, lower bound
+constexpr int kMaxSplitTokens = PA_DECODE_MAX_SPLIT;  // positions per split, upper bound
 
 struct DecArgs {
   void* out;
@@ -59,6 +99,7 @@ struct DecArgs {
   int32_t split_blocks;
   int32_t max_splits;
   int32_t waves_per_wg;
+  int32_t kv_groups;
   int32_t out_f32;
   float scale_log2;        // softmax_scale * log2(e)
 };
@@ -69,253 +110,28 @@ __device__ __forceinline__ int clamp_ctx(const DecArgs& a, int b) {
   return ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
 }
 
-template <Ty C> struct KvRow;
-template <> struct KvRow<Ty::BF16> {
-  using Raw = u32x4;
-  __device__ __forceinline__ static Raw load(const char* p) { return *reinterpret_cast<const u32x4*>(p); }
-  __device__ __forceinline__ static void widen(const Raw& r, float (&f)[8]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[2 * i] = bf16_lo(r[i]);
-      f[2 * i + 1] = bf16_hi(r[i]);
-    }
-  }
-};
-template <> struct KvRow<Ty::FP8> {
-  using Raw = u32x2;
-  __device__ __forceinline__ static Raw load(const char* p) { return *reinterpret_cast<const u32x2*>(p); }
-  __device__ __forceinline__ static void widen(const Raw& r, float (&f)[8]) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const f32x2 lo = fp8x2_lo(r[i]), hi = fp8x2_hi(r[i]);
-      f[4 * i] = lo[0];
-      f[4 * i + 1] = lo[1];
-      f[4 * i + 2] = hi[0];
-      f[4 * i + 3] = hi[1];
-    }
-  }
-};
-
-template <Ty C, int D, int G>
-__global__ __launch_bounds__(512) void decode_split_kernel(DecArgs a) {
-  constexpr int LPR = D / 8;     // lanes per cache row
-  constexpr int RPL = 64 / LPR;  // cache rows per wave-load
-  constexpr int CB = TyInfo<C>::kBytes;
-  using R = KvRow<C>;
-  const int lane = threadIdx.x & 63;
-  const int wave = uniform(threadIdx.x >> 6);
-  const int g = (int)blockIdx.z * a.waves_per_wg + wave;
-  if (g >= a.HKV) return;
-  const int b = blockIdx.y;
-  const int split = blockIdx.x;
-  const int ctx = clamp_ctx(a, b);
-  const int nblk = (ctx + a.block_size - 1) / a.block_size;
-  // an empty sequence still gets one (empty) split, which writes zeros
-  const int nsplit = max(1, (nblk + a.split_blocks - 1) / a.split_blocks);
-  if (split >= nsplit) return;
-  const int j0 = split * a.split_blocks;
-  const int j1 = min(nblk, j0 + a.split_blocks);
-  const int r = lane / LPR, c = lane % LPR;
-
-  // q of the G heads of this group: 8 dims per lane, widened to fp32.
-  float q[G][8];
-  {
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (int64_t)b * a.q_seq_stride + (int64_t)g * G * D + 8 * c;
-#pragma unroll
-    for (int gi = 0; gi < G; ++gi) {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(qp + gi * D);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        q[gi][2 * i] = bf16_lo(w[i]);
-        q[gi][2 * i + 1] = bf16_hi(w[i]);
-      }
-    }
-  }
-  const float ks = a.k_scale ? *a.k_scale : 1.0f;
-  const float vs = a.v_scale ? *a.v_scale : 1.0f;
-  const float sl2 = a.scale_log2 * ks;
-
-  float m[G], l[G], acc[G][8];
-#pragma unroll
-  for (int gi = 0; gi < G; ++gi) {
-    m[gi] = -INFINITY;
-    l[gi] = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) acc[gi][k] = 0.0f;
-  }
-
-  const int64_t row_bytes = (int64_t)a.HKV * D * CB;  // between consecutive offsets of a block
-  const int steps = a.block_size / RPL;
-  const int32_t* bt = a.bt + (int64_t)b * a.W;
-  for (int j = j0; j < j1; ++j) {
-    const int phys = bt[j];
-    if (phys < 0 || (int64_t)phys >= a.num_blocks) continue;  // outside the pool: not attended
-    const int valid = min(a.block_size, ctx - j * a.block_size);
-    const int64_t base = ((int64_t)phys * a.block_stride + (int64_t)g * D + 8 * c) * CB;
-    const char* kb = static_cast<const char*>(a.kc) + base;
-    const char* vb = static_cast<const char*>(a.vc) + base;
-    for (int st0 = 0; st0 < steps; st0 += 4) {
-      typename R::Raw kr[4], vr[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (st0 + u < steps) {
-          const int64_t off = (int64_t)((st0 + u) * RPL + r) * row_bytes;
-          kr[u] = R::load(kb + off);
-          vr[u] = R::load(vb + off);
-        }
-      }
-      float s[G][4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const bool live = (st0 + u < steps) && ((st0 + u) * RPL + r < valid);
-        if (st0 + u < steps) {
-          float kf[8];
-          R::widen(kr[u], kf);
-#pragma unroll
-          for (int gi = 0; gi < G; ++gi) {
-            float part = 0.0f;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) part = fmaf(q[gi][k], kf[k], part);
-            const float dot = group_sum<LPR>(part);
-            s[gi][u] = live ? dot * sl2 : -INFINITY;
-          }
-        } else {
-#pragma unroll
-          for (int gi = 0; gi < G; ++gi) s[gi][u] = -INFINITY;
-        }
-      }
-      float p[G][4];
-#pragma unroll
-      for (int gi = 0; gi < G; ++gi) {
-        const float mx = fmaxf(fmaxf(s[gi][0], s[gi][1]), fmaxf(s[gi][2], s[gi][3]));
-        const float mn = fmaxf(m[gi], mx);
-        const float mu = (mn == -INFINITY) ? 0.0f : mn;
-        const float alpha = __builtin_amdgcn_exp2f(m[gi] - mu);
-        float ps = 0.0f;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          p[gi][u] = __builtin_amdgcn_exp2f(s[gi][u] - mu);
-          ps += p[gi][u];
-        }
-        l[gi] = l[gi] * alpha + ps;
-        m[gi] = mn;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) acc[gi][k] *= alpha;
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (st0 + u < steps) {
-          float vf[8];
-          R::widen(vr[u], vf);
-          if ((st0 + u) * RPL + r >= valid) {
-#pragma unroll
-            for (int k = 0; k < 8; ++k) vf[k] = 0.0f;  // unwritten slots may hold NaN
-          }
-#pragma unroll
-          for (int gi = 0; gi < G; ++gi)
-#pragma unroll
-            for (int k = 0; k < 8; ++k) acc[gi][k] = fmaf(p[gi][u], vf[k], acc[gi][k]);
-        }
-      }
-    }
-  }
-
-  // Merge the RPL row states (rows are LPR lanes apart).
-#pragma unroll
-  for (int msk = LPR; msk < 64; msk <<= 1) {
-#pragma unroll
-    for (int gi = 0; gi < G; ++gi) {
-      const float mo = __shfl_xor(m[gi], msk, 64);
-      const float lo = __shfl_xor(l[gi], msk, 64);
-      const float mn = fmaxf(m[gi], mo);
-      const float mu = (mn == -INFINITY) ? 0.0f : mn;
-      const float a1 = __builtin_amdgcn_exp2f(m[gi] - mu), a2 = __builtin_amdgcn_exp2f(mo - mu);
-      l[gi] = l[gi] * a1 + lo * a2;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float ao = __shfl_xor(acc[gi][k], msk, 64);
-        acc[gi][k] = acc[gi][k] * a1 + ao * a2;
-      }
-      m[gi] = mn;
-    }
-  }
-  if (r != 0) return;
-
-#pragma unroll
-  for (int gi = 0; gi < G; ++gi) {
-    const int h = g * G + gi;
-    const float inv = l[gi] > 0.0f ? vs / l[gi] : 0.0f;
-    float o[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) o[k] = acc[gi][k] * inv;
-    if (nsplit == 1) {
-      if (a.out_f32) {
-        float* op = static_cast<float*>(a.out) + (int64_t)b * a.out_seq_stride + (int64_t)h * D + 8 * c;
-        u32x4 x, y;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          x[k] = __float_as_uint(o[k]);
-          y[k] = __float_as_uint(o[4 + k]);
-        }
-        reinterpret_cast<u32x4*>(op)[0] = x;
-        reinterpret_cast<u32x4*>(op)[1] = y;
-      } else {
-        uint16_t* op = static_cast<uint16_t*>(a.out) + (int64_t)b * a.out_seq_stride + (int64_t)h * D + 8 * c;
-        u32x4 x;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) x[k] = f32_to_bf16(o[2 * k]) | (f32_to_bf16(o[2 * k + 1]) << 16);
-        *reinterpret_cast<u32x4*>(op) = x;
-      }
-    } else {
-      const int64_t slot = ((int64_t)b * a.HQ + h) * a.max_splits + split;
-      if (c == 0) {
-        a.ws_m[slot] = m[gi];
-        a.ws_l[slot] = l[gi];
-      }
-      float* wo = a.ws_o + slot * D + 8 * c;
-      u32x4 x, y;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        x[k] = __float_as_uint(o[k]);
-        y[k] = __float_as_uint(o[4 + k]);
-      }
-      reinterpret_cast<u32x4*>(wo)[0] = x;
-      reinterpret_cast<u32x4*>(wo)[1] = y;
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Split pass, matrix-core variant (block_size a multiple of 16).
-//
-// A tile is 16 consecutive cache positions of one KV head. QK^T of a tile is
-// one v_mfma_f32_16x16x32_bf16 per 32 head dims: A = the K tile (row = token,
-// lane l holds token l%16, dims 8*(l/16)..+8 of the step), B = the group's q
-// heads as columns (columns >= G are zero), so lane l receives the scores of
-// tokens 4*(l/16)+r, r = 0..3, for head l%16. The softmax runs on those lanes;
-// P.V runs on the vector ALUs with V in a row layout (16 lanes per cache row,
-// D/16 dims per lane, 4 rows per load) in which lane l needs exactly the
-// probabilities of row-group l/16 -- DPP row_newbcast hands them over. fp8 K
-// is widened to bf16 exactly before the MFMA.
-// ---------------------------------------------------------------------------
-typedef __bf16 bf16x8 __attribute__((__vector_size__(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+// ------------------------------------------------------------ small helpers
 
 template <int NW> struct Dw { uint32_t w[NW]; };
 
-template <int NW>
+// NW dwords; non-temporal when NT (data read once per call, full lines per
+// instruction), cached otherwise (a line read in parts by successive loads).
+template <int NW, bool NT>
 __device__ __forceinline__ Dw<NW> load_dw(const char* p) {
   Dw<NW> r;
   if constexpr (NW == 1) {
-    r.w[0] = *reinterpret_cast<const uint32_t*>(p);
+    const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+    r.w[0] = NT ? __builtin_nontemporal_load(q) : *q;
   } else if constexpr (NW == 2) {
-    const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+    const u32x2* q = reinterpret_cast<const u32x2*>(p);
+    const u32x2 v = NT ? __builtin_nontemporal_load(q) : *q;
     r.w[0] = v[0];
     r.w[1] = v[1];
   } else {
 #pragma unroll
     for (int i = 0; i < NW / 4; ++i) {
-      const u32x4 v = reinterpret_cast<const u32x4*>(p)[i];
+      const u32x4* q = reinterpret_cast<const u32x4*>(p) + i;
+      const u32x4 v = NT ? __builtin_nontemporal_load(q) : *q;
 #pragma unroll
       for (int k = 0; k < 4; ++k) r.w[4 * i + k] = v[k];
     }
@@ -323,26 +139,20 @@ __device__ __forceinline__ Dw<NW> load_dw(const char* p) {
   return r;
 }
 
-// 8 cache elements -> MFMA bf16 operand (fp8 values are exact in bf16).
-template <Ty C> __device__ __forceinline__ bf16x8 as_bf16x8(const Dw<8 * TyInfo<C>::kBytes / 4>& d);
-template <> __device__ __forceinline__ bf16x8 as_bf16x8<Ty::BF16>(const Dw<4>& d) {
-  const u32x4 v = {d.w[0], d.w[1], d.w[2], d.w[3]};
-  return __builtin_bit_cast(bf16x8, v);
-}
-template <> __device__ __forceinline__ bf16x8 as_bf16x8<Ty::FP8>(const Dw<2>& d) {
-  bf16x8 r;
+template <int NW>
+__device__ __forceinline__ void store_dw(void* p, const uint32_t (&w)[NW]) {
+  if constexpr (NW == 1) {
+    *reinterpret_cast<uint32_t*>(p) = w[0];
+  } else if constexpr (NW == 2) {
+    *reinterpret_cast<u32x2*>(p) = u32x2{w[0], w[1]};
+  } else {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const f32x2 lo = fp8x2_lo(d.w[i]), hi = fp8x2_hi(d.w[i]);
-    r[4 * i] = (__bf16)lo[0];
-    r[4 * i + 1] = (__bf16)lo[1];
-    r[4 * i + 2] = (__bf16)hi[0];
-    r[4 * i + 3] = (__bf16)hi[1];
+    for (int i = 0; i < NW / 4; ++i)
+      reinterpret_cast<u32x4*>(p)[i] = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
   }
-  return r;
 }
 
-// NW dwords of cache elements -> fp32.
+// N cache elements (packed in dwords) -> fp32.
 template <Ty C, int NW, int N>
 __device__ __forceinline__ void widen_dw(const Dw<NW>& d, float (&f)[N]) {
   if constexpr (C == Ty::BF16) {
@@ -365,7 +175,315 @@ __device__ __forceinline__ void widen_dw(const Dw<NW>& d, float (&f)[N]) {
   }
 }
 
-// Value of lane j of this lane's 16-lane row (DPP row_newbcast).
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+
+// N output values of head h at dims d0.. : out (bf16 or fp32).
+template <int D, int N>
+__device__ __forceinline__ void store_out(const DecArgs& a, int b, int h, int d0, const float (&o)[N]) {
+  if (a.out_f32) {
+    uint32_t w[N];
+#pragma unroll
+    for (int k = 0; k < N; ++k) w[k] = __float_as_uint(o[k]);
+    store_dw<N>(static_cast<float*>(a.out) + (int64_t)b * a.out_seq_stride + (int64_t)h * D + d0, w);
+  } else {
+    uint32_t w[N / 2];
+#pragma unroll
+    for (int k = 0; k < N / 2; ++k) w[k] = f32_to_bf16(o[2 * k]) | (f32_to_bf16(o[2 * k + 1]) << 16);
+    store_dw<N / 2>(static_cast<uint16_t*>(a.out) + (int64_t)b * a.out_seq_stride + (int64_t)h * D + d0, w);
+  }
+}
+
+// Normalised result of one split for head h, dims d0..d0+N: straight to the
+// output when the sequence has one split, otherwise to the workspace.
+template <int D, int N>
+__device__ __forceinline__ void store_split(const DecArgs& a, int b, int h, int split, int nsplit, int d0,
+                                            const float (&o)[N], bool write_ml, float m, float l) {
+  if (nsplit == 1) {
+    store_out<D, N>(a, b, h, d0, o);
+    return;
+  }
+  const int64_t slot = ((int64_t)b * a.HQ + h) * a.max_splits + split;
+  if (write_ml) {
+    a.ws_m[slot] = m;
+    a.ws_l[slot] = l;
+  }
+  uint32_t w[N];
+#pragma unroll
+  for (int k = 0; k < N; ++k) w[k] = __float_as_uint(o[k]);
+  store_dw<N>(a.ws_o + slot * D + d0, w);
+}
+
+// Merge of the splits of (sequence b, q head h) by one wave: lane s holds
+// split s's (max, sum) -- one round of loads -- the wave reduces the global max
+// and the weights, then the splits' outputs are loaded 16 at a time (all in
+// flight together) and summed with the weights; lane i holds dims i + 64k.
+template <int D>
+__device__ __forceinline__ void merge_head(const DecArgs& a, int b, int h, int nsplit) {
+  constexpr int PER = D / 64;
+  constexpr int BATCH = 16;
+  const int lane = threadIdx.x & 63;
+  const int64_t base = ((int64_t)b * a.HQ + h) * a.max_splits;
+  float o[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) o[i] = 0.0f;
+  float M = -INFINITY;
+  for (int s = lane; s < nsplit; s += 64) M = fmaxf(M, a.ws_m[base + s]);
+  M = wave_max(M);
+  if (M != -INFINITY) {
+    float den = 0.0f;
+    for (int c = 0; c < nsplit; c += 64) {
+      const int sl = c + lane;
+      const float w = sl < nsplit ? __builtin_amdgcn_exp2f(a.ws_m[base + sl] - M) * a.ws_l[base + sl] : 0.0f;
+      den += w;
+      const int cnt = min(64, nsplit - c);
+      for (int s0 = 0; s0 < cnt; s0 += BATCH) {
+        float v[BATCH][PER];
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+          const float* wo = a.ws_o + (base + c + min(s0 + u, cnt - 1)) * D;
+#pragma unroll
+          for (int i = 0; i < PER; ++i) v[u][i] = wo[lane + 64 * i];
+        }
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+          if (s0 + u < cnt) {
+            const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), s0 + u));
+#pragma unroll
+            for (int i = 0; i < PER; ++i) o[i] = fmaf(ws, v[u][i], o[i]);
+          }
+        }
+      }
+    }
+    const float inv = 1.0f / wave_sum(den);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) o[i] *= inv;
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int64_t at = (int64_t)b * a.out_seq_stride + (int64_t)h * D + lane + 64 * i;
+    if (a.out_f32)
+      static_cast<float*>(a.out)[at] = o[i];
+    else
+      static_cast<uint16_t*>(a.out)[at] = (uint16_t)f32_to_bf16(o[i]);
+  }
+}
+
+// Merge pass: one wave per (sequence, q head), four waves per workgroup.
+// Sequences that fit one split were written by the split pass. (A merge inside
+// the split kernel would need an agent-scope release/acquire per workgroup,
+// i.e. an L2 write-back on its XCD for every split; the kernel boundary gives
+// that ordering for free.)
+template <int D>
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecArgs a) {
+  const int wid = (int)blockIdx.x * 4 + uniform(threadIdx.x >> 6);
+  if (wid >= a.num_seqs * a.HQ) return;
+  const int b = wid / a.HQ, h = wid - b * a.HQ;
+  const int ctx = clamp_ctx(a, b);
+  const int nblk = (ctx + a.block_size - 1) / a.block_size;
+  const int nsplit = (nblk + a.split_blocks - 1) / a.split_blocks;
+  if (nsplit <= 1) return;
+  merge_head<D>(a, b, h, nsplit);
+}
+
+// ---------------------------------------------------------------------------
+// Vector-ALU split kernel (any block size that is a multiple of 64 / (D/8)).
+// ---------------------------------------------------------------------------
+template <Ty C> struct KvRow;
+template <> struct KvRow<Ty::BF16> { static constexpr int kW = 4; };
+template <> struct KvRow<Ty::FP8> { static constexpr int kW = 2; };
+
+template <Ty C, int D, int G>
+__global__ __launch_bounds__(512) void decode_split_valu_kernel(DecArgs a) {
+  constexpr int LPR = D / 8;     // lanes per cache row
+  constexpr int RPL = 64 / LPR;  // cache rows per wave-load
+  constexpr int CB = TyInfo<C>::kBytes;
+  constexpr int KW = KvRow<C>::kW;
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int g = (int)blockIdx.x * a.waves_per_wg + wave;
+  const bool active = g < a.HKV;
+  const int split = blockIdx.y;
+  const int b = blockIdx.z;
+  const int ctx = clamp_ctx(a, b);
+  const int nblk = (ctx + a.block_size - 1) / a.block_size;
+  // an empty sequence still gets one (empty) split, which writes zeros
+  const int nsplit = max(1, (nblk + a.split_blocks - 1) / a.split_blocks);
+  if (split >= nsplit) return;  // uniform over the workgroup
+  const int j0 = split * a.split_blocks;
+  const int j1 = min(nblk, j0 + a.split_blocks);
+  const int r = lane / LPR, c = lane % LPR;
+
+  if (active) {
+    float q[G][8];
+    {
+      const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (int64_t)b * a.q_seq_stride + (int64_t)g * G * D + 8 * c;
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(qp + gi * D);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          q[gi][2 * i] = bf16_lo(w[i]);
+          q[gi][2 * i + 1] = bf16_hi(w[i]);
+        }
+      }
+    }
+    const float ks = a.k_scale ? *a.k_scale : 1.0f;
+    const float vs = a.v_scale ? *a.v_scale : 1.0f;
+    const float sl2 = a.scale_log2 * ks;
+
+    float m[G], l[G], acc[G][8];
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+      m[gi] = -INFINITY;
+      l[gi] = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[gi][k] = 0.0f;
+    }
+
+    const int64_t row_bytes = (int64_t)a.HKV * D * CB;  // between consecutive offsets of a block
+    const int steps = a.block_size / RPL;
+    const int32_t* bt = a.bt + (int64_t)b * a.W;
+    for (int j = j0; j < j1; ++j) {
+      const int phys = bt[j];
+      if (phys < 0 || (int64_t)phys >= a.num_blocks) continue;  // outside the pool: not attended
+      const int valid = min(a.block_size, ctx - j * a.block_size);
+      const int64_t base = ((int64_t)phys * a.block_stride + (int64_t)g * D + 8 * c) * CB;
+      const char* kb = static_cast<const char*>(a.kc) + base;
+      const char* vb = static_cast<const char*>(a.vc) + base;
+      for (int st0 = 0; st0 < steps; st0 += 4) {
+        Dw<KW> kr[4], vr[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (st0 + u < steps) {
+            const int64_t off = (int64_t)((st0 + u) * RPL + r) * row_bytes;
+            kr[u] = load_dw<KW, true>(kb + off);
+            vr[u] = load_dw<KW, true>(vb + off);
+          }
+        }
+        float s[G][4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const bool live = (st0 + u < steps) && ((st0 + u) * RPL + r < valid);
+          if (st0 + u < steps) {
+            float kf[8];
+            widen_dw<C>(kr[u], kf);
+#pragma unroll
+            for (int gi = 0; gi < G; ++gi) {
+              float part = 0.0f;
+#pragma unroll
+              for (int k = 0; k < 8; ++k) part = fmaf(q[gi][k], kf[k], part);
+              const float dot = group_sum<LPR>(part);
+              s[gi][u] = live ? dot * sl2 : -INFINITY;
+            }
+          } else {
+#pragma unroll
+            for (int gi = 0; gi < G; ++gi) s[gi][u] = -INFINITY;
+          }
+        }
+        float p[G][4];
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi) {
+          const float mx = fmaxf(fmaxf(s[gi][0], s[gi][1]), fmaxf(s[gi][2], s[gi][3]));
+          const float mn = fmaxf(m[gi], mx);
+          const float mu = (mn == -INFINITY) ? 0.0f : mn;
+          const float alpha = __builtin_amdgcn_exp2f(m[gi] - mu);
+          float ps = 0.0f;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            p[gi][u] = __builtin_amdgcn_exp2f(s[gi][u] - mu);
+            ps += p[gi][u];
+          }
+          l[gi] = l[gi] * alpha + ps;
+          m[gi] = mn;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) acc[gi][k] *= alpha;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (st0 + u < steps) {
+            float vf[8];
+            widen_dw<C>(vr[u], vf);
+            if ((st0 + u) * RPL + r >= valid) {
+#pragma unroll
+              for (int k = 0; k < 8; ++k) vf[k] = 0.0f;  // unwritten slots may hold NaN
+            }
+#pragma unroll
+            for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+              for (int k = 0; k < 8; ++k) acc[gi][k] = fmaf(p[gi][u], vf[k], acc[gi][k]);
+          }
+        }
+      }
+    }
+
+    // Merge the RPL row states (rows are LPR lanes apart).
+#pragma unroll
+    for (int msk = LPR; msk < 64; msk <<= 1) {
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi) {
+        const float mo = __shfl_xor(m[gi], msk, 64);
+        const float lo = __shfl_xor(l[gi], msk, 64);
+        const float mn = fmaxf(m[gi], mo);
+        const float mu = (mn == -INFINITY) ? 0.0f : mn;
+        const float a1 = __builtin_amdgcn_exp2f(m[gi] - mu), a2 = __builtin_amdgcn_exp2f(mo - mu);
+        l[gi] = l[gi] * a1 + lo * a2;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float ao = __shfl_xor(acc[gi][k], msk, 64);
+          acc[gi][k] = acc[gi][k] * a1 + ao * a2;
+        }
+        m[gi] = mn;
+      }
+    }
+    if (r == 0) {
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi) {
+        const float inv = l[gi] > 0.0f ? vs / l[gi] : 0.0f;
+        float o[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[k] = acc[gi][k] * inv;
+        store_split<D, 8>(a, b, g * G + gi, split, nsplit, 8 * c, o, c == 0, m[gi], l[gi]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Matrix-core split kernel (block_size a multiple of 16).
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((__vector_size__(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// 8 cache elements -> MFMA bf16 operand (fp8 values are exact in bf16).
+template <Ty C> __device__ __forceinline__ bf16x8 as_bf16x8(const Dw<8 * TyInfo<C>::kBytes / 4>& d);
+template <> __device__ __forceinline__ bf16x8 as_bf16x8<Ty::BF16>(const Dw<4>& d) {
+  const u32x4 v = {d.w[0], d.w[1], d.w[2], d.w[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+template <> __device__ __forceinline__ bf16x8 as_bf16x8<Ty::FP8>(const Dw<2>& d) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const f32x2 lo = fp8x2_lo(d.w[i]), hi = fp8x2_hi(d.w[i]);
+    r[4 * i] = (__bf16)lo[0];
+    r[4 * i + 1] = (__bf16)lo[1];
+    r[4 * i + 2] = (__bf16)hi[0];
+    r[4 * i + 3] = (__bf16)hi[1];
+  }
+  return r;
+}
+
+// Value of lane J of this lane's 16-lane row (DPP row_newbcast).
 template <int J>
 __device__ __forceinline__ float row_bcast(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + J, 0xF, 0xF, false));
@@ -393,96 +511,107 @@ __device__ __forceinline__ void bcast_heads(float x, float (&out)[G]) {
   if constexpr (J + 1 < G) bcast_heads<J + 1, G>(x, out);
 }
 
-template <Ty C, int D, int G, int TPI>
-__global__ __launch_bounds__(512) void decode_split_mfma_kernel(DecArgs a) {
-  constexpr int KS = D / 32;               // MFMA steps over the head dim
-  constexpr int EPL = D / 16;              // V dims per lane
+template <Ty C, int D>
+struct Tile {
+  static constexpr int KS = D / 32;                 // MFMA steps over the head dim
+  static constexpr int EPL = D / 16;                // V dims per lane
+  static constexpr int KW = 8 * TyInfo<C>::kBytes / 4;
+  static constexpr int VW = EPL * TyInfo<C>::kBytes / 4;
+  Dw<KW> k[KS];
+  Dw<VW> v[4];
+};
+
+template <Ty C, int D>
+__device__ __forceinline__ void load_tile(Tile<C, D>& t, const char* kc, const char* vc, int64_t blk_el,
+                                          int off, int64_t row_el, int li, int lg) {
   constexpr int CB = TyInfo<C>::kBytes;
-  constexpr int KW = 8 * CB / 4;           // dwords per K operand chunk
-  constexpr int VW = EPL * CB / 4;         // dwords per V chunk
-  static_assert(VW >= 1, "V chunk");
+  const char* kp = kc + (blk_el + (int64_t)(off + li) * row_el + 8 * lg) * CB;
+#pragma unroll
+  for (int s = 0; s < Tile<C, D>::KS; ++s) t.k[s] = load_dw<Tile<C, D>::KW, PA_DECODE_NT_K>(kp + 32 * s * CB);
+  const char* vp = vc + (blk_el + (int64_t)(off + 4 * lg) * row_el + Tile<C, D>::EPL * li) * CB;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) t.v[i] = load_dw<Tile<C, D>::VW, PA_DECODE_NT_V>(vp + (int64_t)i * row_el * CB);
+}
+
+template <Ty C, int D, int G>
+__global__ __launch_bounds__(512) PA_SPLIT_OCCUPANCY void decode_split_mfma_kernel(DecArgs a) {
+  using T = Tile<C, D>;
+  constexpr int KS = T::KS;
+  constexpr int EPL = T::EPL;
   const int lane = threadIdx.x & 63;
   const int li = lane & 15, lg = lane >> 4;
   const int wave = uniform(threadIdx.x >> 6);
-  const int g = (int)blockIdx.z * a.waves_per_wg + wave;
-  if (g >= a.HKV) return;
-  const int b = blockIdx.y;
-  const int split = blockIdx.x;
+  const int g = (int)blockIdx.x * a.waves_per_wg + wave;
+  const bool active = g < a.HKV;
+  const int split = blockIdx.y;
+  const int b = blockIdx.z;
   const int ctx = clamp_ctx(a, b);
   const int nblk = (ctx + a.block_size - 1) / a.block_size;
   const int nsplit = max(1, (nblk + a.split_blocks - 1) / a.split_blocks);
-  if (split >= nsplit) return;
-  const int j0 = split * a.split_blocks;
-  const int j1 = min(nblk, j0 + a.split_blocks);
-  const int p_begin = j0 * a.block_size;
-  const int p_end = min(ctx, j1 * a.block_size);
-  const int n_tiles = p_end > p_begin ? (p_end - p_begin + 15) >> 4 : 0;
+  if (split >= nsplit) return;  // uniform over the workgroup
 
-  bf16x8 qb[KS];
-  {
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (int64_t)b * a.q_seq_stride +
-                         (int64_t)(g * G + (li < G ? li : 0)) * D + 8 * lg;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      u32x4 w = *reinterpret_cast<const u32x4*>(qp + 32 * s);
-      if (li >= G) w = u32x4{0, 0, 0, 0};
-      qb[s] = __builtin_bit_cast(bf16x8, w);
-    }
-  }
-  const float ks = a.k_scale ? *a.k_scale : 1.0f;
-  const float vs = a.v_scale ? *a.v_scale : 1.0f;
-  const float sl2 = a.scale_log2 * ks;
+  if (active) {
+    const int j0 = split * a.split_blocks;
+    const int j1 = min(nblk, j0 + a.split_blocks);
+    const int p_begin = j0 * a.block_size;
+    const int p_end = min(ctx, j1 * a.block_size);
+    const int n_tiles = p_end > p_begin ? (p_end - p_begin + 15) >> 4 : 0;
 
-  float m_run = -INFINITY, l_run = 0.0f;
-  float acc[G][EPL];
+    bf16x8 qb[KS];
+    {
+      const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (int64_t)b * a.q_seq_stride +
+                           (int64_t)(g * G + (li < G ? li : 0)) * D + 8 * lg;
 #pragma unroll
-  for (int j = 0; j < G; ++j)
-#pragma unroll
-    for (int k = 0; k < EPL; ++k) acc[j][k] = 0.0f;
-
-  const int64_t row_el = (int64_t)a.HKV * D;  // elements between consecutive slots of a block
-  const int32_t* bt = a.bt + (int64_t)b * a.W;
-  const char* kc = static_cast<const char*>(a.kc);
-  const char* vc = static_cast<const char*>(a.vc);
-
-  for (int t0 = 0; t0 < n_tiles; t0 += TPI) {
-    Dw<KW> kr[TPI][KS];
-    Dw<VW> vr[TPI][4];
-    bool tv[TPI];
-    int tp0[TPI];
-#pragma unroll
-    for (int tt = 0; tt < TPI; ++tt) {
-      const int p0 = p_begin + (t0 + tt) * 16;
-      tp0[tt] = p0;
-      bool valid = (t0 + tt) < n_tiles;
-      int phys = 0;
-      if (valid) {
-        phys = bt[p0 / a.block_size];
-        valid = phys >= 0 && (int64_t)phys < a.num_blocks;  // outside the pool: not attended
-      }
-      tv[tt] = valid;
-      if (valid) {
-        const int off = p0 % a.block_size;
-        const int64_t blk = (int64_t)phys * a.block_stride + (int64_t)g * D;
-        const char* kp = kc + (blk + (int64_t)(off + li) * row_el + 8 * lg) * CB;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) kr[tt][s] = load_dw<KW>(kp + 32 * s * CB);
-        const char* vp = vc + (blk + (int64_t)(off + 4 * lg) * row_el + EPL * li) * CB;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) vr[tt][i] = load_dw<VW>(vp + i * row_el * CB);
+      for (int s = 0; s < KS; ++s) {
+        u32x4 w = *reinterpret_cast<const u32x4*>(qp + 32 * s);
+        if (li >= G) w = u32x4{0, 0, 0, 0};
+        qb[s] = __builtin_bit_cast(bf16x8, w);
       }
     }
+    const float ks = a.k_scale ? *a.k_scale : 1.0f;
+    const float vs = a.v_scale ? *a.v_scale : 1.0f;
+    const float sl2 = a.scale_log2 * ks;
+
+    float m_run = -INFINITY, l_run = 0.0f;
+    float acc[G][EPL];
 #pragma unroll
-    for (int tt = 0; tt < TPI; ++tt) {
-      if (!tv[tt]) continue;
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+      for (int k = 0; k < EPL; ++k) acc[j][k] = 0.0f;
+
+    const int64_t row_el = (int64_t)a.HKV * D;  // elements between consecutive slots of a block
+    const int32_t* bt = a.bt + (int64_t)b * a.W;
+    const char* kc = static_cast<const char*>(a.kc);
+    const char* vc = static_cast<const char*>(a.vc);
+
+    // Tile t covers positions p_begin + 16t .. +15, all inside one block. Loads
+    // are issued unconditionally so that the compiler keeps the next tile's
+    // loads in flight while the current tile is computed: a tile index past the
+    // end is clamped to the last tile (a cache hit) and a block outside the pool
+    // is read as block 0; both come back flagged as not to be attended.
+    auto fetch = [&](T& tile, int t) -> bool {
+      const int tc = min(t, n_tiles - 1);
+      const int p0 = p_begin + 16 * tc;
+      const int phys = bt[p0 / a.block_size];
+      const bool ok = t < n_tiles && phys >= 0 && (int64_t)phys < a.num_blocks;
+      load_tile<C, D>(tile, kc, vc, (int64_t)(ok ? phys : 0) * a.block_stride + (int64_t)g * D,
+                      p0 % a.block_size, row_el, li, lg);
+      return ok;
+    };
+    // kMask: the tile reaches past the context end (only the last one can).
+    auto compute = [&](const T& tile, int t, auto mask_tag) {
+      constexpr bool kMask = decltype(mask_tag)::value;
       f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int s = 0; s < KS; ++s)
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8<C>(kr[tt][s]), qb[s], sc, 0, 0, 0);
-      const int prow = tp0[tt] + 4 * lg;  // position of this lane's first score / V row
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8<C>(tile.k[s]), qb[s], sc, 0, 0, 0);
+      const int prow = p_begin + 16 * t + 4 * lg;  // position of this lane's first score / V row
       float sr[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sr[r] = (prow + r < p_end) ? sc[r] * sl2 : -INFINITY;
+      for (int r = 0; r < 4; ++r) {
+        sr[r] = sc[r] * sl2;
+        if constexpr (kMask) sr[r] = (prow + r < p_end) ? sr[r] : -INFINITY;
+      }
       float mx = fmaxf(fmaxf(sr[0], sr[1]), fmaxf(sr[2], sr[3]));
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
@@ -502,109 +631,74 @@ __global__ __launch_bounds__(512) void decode_split_mfma_kernel(DecArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float vf[EPL];
-        widen_dw<C>(vr[tt][i], vf);
-        if (prow + i >= p_end) {
+        widen_dw<C>(tile.v[i], vf);
+        if constexpr (kMask) {
+          if (prow + i >= p_end) {
 #pragma unroll
-          for (int k = 0; k < EPL; ++k) vf[k] = 0.0f;  // unwritten slots may hold NaN
+            for (int k = 0; k < EPL; ++k) vf[k] = 0.0f;  // unwritten slots may hold NaN
+          }
         }
         accumulate_row<0, G, EPL>(acc, pr[i], vf);
       }
+    };
+    auto run = [&](const T& tile, int t, bool ok) {
+      if (!ok) return;
+      if (p_begin + 16 * t + 16 <= p_end)
+        compute(tile, t, std::false_type{});
+      else
+        compute(tile, t, std::true_type{});
+    };
+
+    if (n_tiles > 0 && a.num_blocks > 0) {
+#if PA_DECODE_PREFETCH
+      // Two register tiles: the next tile is in flight while one is computed.
+      T ta, tb;
+      bool oka = fetch(ta, 0);
+      for (int t = 0; t < n_tiles; t += 2) {
+        const bool okb = fetch(tb, t + 1);
+        run(ta, t, oka);
+        oka = fetch(ta, t + 2);
+        run(tb, t + 1, okb);
+      }
+#else
+      for (int t = 0; t < n_tiles; ++t) {
+        T ta;
+        const bool ok = fetch(ta, t);
+        run(ta, t, ok);
+      }
+#endif
     }
-  }
 
-  // Sum the four row groups (same running max everywhere, so no rescaling).
+    // Sum the four row groups (same running max everywhere: no rescaling).
 #pragma unroll
-  for (int msk = 16; msk < 64; msk <<= 1) {
-    l_run += __shfl_xor(l_run, msk, 64);
+    for (int msk = 16; msk < 64; msk <<= 1) {
+      l_run += __shfl_xor(l_run, msk, 64);
 #pragma unroll
-    for (int j = 0; j < G; ++j)
+      for (int j = 0; j < G; ++j)
 #pragma unroll
-      for (int k = 0; k < EPL; ++k) acc[j][k] += __shfl_xor(acc[j][k], msk, 64);
-  }
-  float lj[G];
-  bcast_heads<0, G>(l_run, lj);
-  if (lg != 0) return;
-
+        for (int k = 0; k < EPL; ++k) acc[j][k] += __shfl_xor(acc[j][k], msk, 64);
+    }
+    float lj[G];
+    bcast_heads<0, G>(l_run, lj);
+    if (lg == 0) {
 #pragma unroll
-  for (int j = 0; j < G; ++j) {
-    const int h = g * G + j;
-    const float inv = lj[j] > 0.0f ? vs / lj[j] : 0.0f;
-    float o[EPL];
+      for (int j = 0; j < G; ++j) {
+        const float inv = lj[j] > 0.0f ? vs / lj[j] : 0.0f;
+        float o[EPL];
 #pragma unroll
-    for (int k = 0; k < EPL; ++k) o[k] = acc[j][k] * inv;
-    if (nsplit == 1) {
-      if (a.out_f32) {
-        float* op = static_cast<float*>(a.out) + (int64_t)b * a.out_seq_stride + (int64_t)h * D + EPL * li;
-#pragma unroll
-        for (int k = 0; k < EPL; ++k) op[k] = o[k];
-      } else {
-        uint16_t* op = static_cast<uint16_t*>(a.out) + (int64_t)b * a.out_seq_stride + (int64_t)h * D + EPL * li;
-        uint32_t w[EPL / 2];
-#pragma unroll
-        for (int k = 0; k < EPL / 2; ++k) w[k] = f32_to_bf16(o[2 * k]) | (f32_to_bf16(o[2 * k + 1]) << 16);
-#pragma unroll
-        for (int k = 0; k < EPL / 2; ++k) reinterpret_cast<uint32_t*>(op)[k] = w[k];
+        for (int k = 0; k < EPL; ++k) o[k] = acc[j][k] * inv;
+        store_split<D, EPL>(a, b, g * G + j, split, nsplit, EPL * li, o, li == j, m_run, lj[j]);
       }
-    } else {
-      const int64_t slot = ((int64_t)b * a.HQ + h) * a.max_splits + split;
-      if (li == j) {
-        a.ws_m[slot] = m_run;
-        a.ws_l[slot] = lj[j];
-      }
-      float* wo = a.ws_o + slot * D + EPL * li;
-#pragma unroll
-      for (int k = 0; k < EPL; ++k) wo[k] = o[k];
     }
   }
 }
 
-// Pass 2: one wavefront per (sequence, q head); lane i holds dims i, i+64, ...
-template <int D>
-__global__ __launch_bounds__(256) void decode_merge_kernel(DecArgs a) {
-  constexpr int PER = D / 64;
-  const int lane = threadIdx.x & 63;
-  const int wid = (int)blockIdx.x * 4 + uniform(threadIdx.x >> 6);
-  if (wid >= a.num_seqs * a.HQ) return;
-  const int b = wid / a.HQ, h = wid - b * a.HQ;
-  const int ctx = clamp_ctx(a, b);
-  const int nblk = (ctx + a.block_size - 1) / a.block_size;
-  const int nsplit = (nblk + a.split_blocks - 1) / a.split_blocks;
-  if (nsplit <= 1) return;  // written by pass 1
-  float o[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) o[i] = 0.0f;
-  {
-    const int64_t base = ((int64_t)b * a.HQ + h) * a.max_splits;
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, a.ws_m[base + s]);
-    if (M != -INFINITY) {
-      float den = 0.0f;
-      for (int s = 0; s < nsplit; ++s) {
-        const float w = __builtin_amdgcn_exp2f(a.ws_m[base + s] - M) * a.ws_l[base + s];
-        den += w;
-        const float* wo = a.ws_o + (base + s) * D;
-#pragma unroll
-        for (int i = 0; i < PER; ++i) o[i] = fmaf(w, wo[lane + 64 * i], o[i]);
-      }
-      const float inv = 1.0f / den;
-#pragma unroll
-      for (int i = 0; i < PER; ++i) o[i] *= inv;
-    }
-  }
-  if (a.out_f32) {
-    float* op = static_cast<float*>(a.out) + (int64_t)b * a.out_seq_stride + (int64_t)h * D;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) op[lane + 64 * i] = o[i];
-  } else {
-    uint16_t* op = static_cast<uint16_t*>(a.out) + (int64_t)b * a.out_seq_stride + (int64_t)h * D;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) op[lane + 64 * i] = (uint16_t)f32_to_bf16(o[i]);
-  }
-}
-
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
 struct Plan {
   int waves_per_wg, kv_groups, split_blocks, max_splits;
-  size_t off_l, off_o, bytes;
+  size_t off_m, off_l, off_o, bytes;
 };
 
 inline size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -613,18 +707,19 @@ Plan make_plan(int num_seqs, int HQ, int HKV, int D, int W, int bs) {
   Plan p;
   p.waves_per_wg = HKV < kMaxWaves ? HKV : kMaxWaves;
   p.kv_groups = (HKV + p.waves_per_wg - 1) / p.waves_per_wg;
-  // Aim for kTargetWgs workgroups if every sequence used all W blocks, but
-  // never split finer than 4 blocks (per-split merge traffic).
+  // Aim for kTargetWgs workgroups if every sequence used all W blocks, with
+  // splits of kMinSplitTokens..kMaxSplitTokens positions.
   const int64_t per_seq = ((int64_t)kTargetWgs + (int64_t)num_seqs * p.kv_groups - 1) / ((int64_t)num_seqs * p.kv_groups);
   int sb = (int)((W + per_seq - 1) / per_seq);
-  const int min_sb = (64 + bs - 1) / bs;  // at least 64 tokens per split
-  if (sb < min_sb) sb = min_sb;
+  const int lo = (kMinSplitTokens + bs - 1) / bs, hi = kMaxSplitTokens / bs > lo ? kMaxSplitTokens / bs : lo;
+  sb = sb < lo ? lo : (sb > hi ? hi : sb);
   if (sb > W) sb = W;
   if (sb < 1) sb = 1;
   p.split_blocks = sb;
   p.max_splits = (W + sb - 1) / sb;
   const size_t n = (size_t)num_seqs * HQ * p.max_splits;
-  p.off_l = round256(n * sizeof(float));
+  p.off_m = 0;
+  p.off_l = p.off_m + round256(n * sizeof(float));
   p.off_o = p.off_l + round256(n * sizeof(float));
   p.bytes = p.off_o + round256(n * (size_t)D * sizeof(float));
   return p;
@@ -632,11 +727,16 @@ Plan make_plan(int num_seqs, int HQ, int HKV, int D, int W, int bs) {
 
 template <Ty C, int D, int G>
 void launch_split(const DecArgs& a, const Plan& p, hipStream_t st) {
-  dim3 grid(p.max_splits, a.num_seqs, p.kv_groups);
-  if (a.block_size % 16 == 0)
-    decode_split_mfma_kernel<C, D, G, (D >= 256 ? 1 : 2)><<<grid, 64 * p.waves_per_wg, 0, st>>>(a);
+  // kv-head groups fastest: sibling workgroups read the same pages together
+  dim3 grid(p.kv_groups, p.max_splits, a.num_seqs);
+  // The matrix-core kernel needs 16-position tiles inside a block; at D = 256
+  // its register tiles would spill, so that head size stays on the vector path.
+  if (a.block_size % 16 == 0 && D <= 128)
+    decode_split_mfma_kernel<C, D, G><<<grid, 64 * p.waves_per_wg, 0, st>>>(a);
   else
-    decode_split_kernel<C, D, G><<<grid, 64 * p.waves_per_wg, 0, st>>>(a);
+    decode_split_valu_kernel<C, D, G><<<grid, 64 * p.waves_per_wg, 0, st>>>(a);
+  if (p.max_splits > 1)
+    decode_merge_kernel<D><<<(unsigned)(((int64_t)a.num_seqs * a.HQ + 3) / 4), 256, 0, st>>>(a);
 }
 
 template <Ty C, int D>
@@ -656,16 +756,6 @@ bool launch_d(int D, int G, const DecArgs& a, const Plan& p, hipStream_t st) {
     case 64: return launch_g<C, 64>(G, a, p, st);
     case 128: return launch_g<C, 128>(G, a, p, st);
     case 256: return launch_g<C, 256>(G, a, p, st);
-    default: return false;
-  }
-}
-
-bool launch_merge(int D, const DecArgs& a, hipStream_t st) {
-  const unsigned grid = (unsigned)(((int64_t)a.num_seqs * a.HQ + 3) / 4);
-  switch (D) {
-    case 64: decode_merge_kernel<64><<<grid, 256, 0, st>>>(a); return true;
-    case 128: decode_merge_kernel<128><<<grid, 256, 0, st>>>(a); return true;
-    case 256: decode_merge_kernel<256><<<grid, 256, 0, st>>>(a); return true;
     default: return false;
   }
 }
@@ -743,7 +833,7 @@ extern "C" pa_status pa_decode_attention(void* out, pa_dtype out_dtype, int64_t 
   a.ctx_lens = context_lens;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
-  a.ws_m = static_cast<float*>(workspace);
+  a.ws_m = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.off_m);
   a.ws_l = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.off_l);
   a.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.off_o);
   a.out_seq_stride = out_seq_stride;
@@ -758,6 +848,7 @@ extern "C" pa_status pa_decode_attention(void* out, pa_dtype out_dtype, int64_t 
   a.split_blocks = p.split_blocks;
   a.max_splits = p.max_splits;
   a.waves_per_wg = p.waves_per_wg;
+  a.kv_groups = p.kv_groups;
   a.out_f32 = out_dtype == PA_F32;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
 
@@ -766,11 +857,5 @@ extern "C" pa_status pa_decode_attention(void* out, pa_dtype out_dtype, int64_t 
   const bool ok = cache_dtype == PA_BF16 ? launch_d<Ty::BF16>(head_size, G, a, p, st)
                                          : launch_d<Ty::FP8>(head_size, G, a, p, st);
   if (!ok) return fail(PA_EUNSUPPORTED, "%s: no kernel for this shape", fn);
-  s = after_launch(fn);
-  if (s != PA_OK) return s;
-  if (p.max_splits > 1) {
-    launch_merge(head_size, a, st);
-    s = after_launch("pa_decode_attention (merge)");
-  }
-  return s;
+  return after_launch(fn);
 }

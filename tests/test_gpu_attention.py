@@ -74,6 +74,8 @@ CASES = [
     ("G2 D256 bf16", [2, 33, 600], 8, 4, 256, 16, BF16, 40),
     ("G4 D256 fp8 bs32", [40, 129, 1000], 8, 2, 256, 32, FP8, 40),
     ("G1 D128 bf16 16 kv heads", [70, 3], 16, 16, 128, 16, BF16, 8),
+    ("G1 D128 bf16 12 kv heads (idle waves)", [300, 40, 129], 12, 12, 128, 16, BF16, 20),
+    ("G2 D128 fp8 bs32", [31, 32, 33, 700], 16, 8, 128, 32, FP8, 24),
     ("G2 D128 bf16 one seq long", [4096], 16, 8, 128, 16, BF16, 256),
     ("G2 D128 bf16 many short", list(range(1, 65)), 16, 8, 128, 16, BF16, 4),
 ]
@@ -149,15 +151,15 @@ def test_block_relabelling_is_bit_identical(cache_dt):
 
 
 def test_repeated_calls_reuse_workspace():
-    """Two calls in a row with one workspace (second with fewer sequences) match the
+    """Calls in a row with one workspace (later ones with fewer sequences) match the
     oracle: the workspace carries nothing between calls."""
     say("decode_attention workspace reuse")
     m = pkv()
     q, kc, vc, bt, ctx = make_case(33, [900, 17, 2500, 64, 1], 16, 8, 128, 16, BF16, width=160)
     need = m.decode_attention_workspace_size(5, 16, 8, 128, 160, 16)
-    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")  # garbage on entry
     dk, dv = to_dev(kc, BF16), to_dev(vc, BF16)
-    for n in (5, 3):
+    for n in (5, 3, 5, 1, 5):
         qq = to_dev(q[:n], BF16)
         out = torch.empty_like(qq)
         m.decode_attention(out, qq, dk, dv, torch.from_numpy(bt[:n].copy()).cuda(),
