@@ -32,30 +32,56 @@ __device__ __forceinline__ f32x2 fp8x2_hi(uint32_t w) { return __builtin_amdgcn_
 
 // ------------------------------------------------------------------ encoding
 
-// fp32 -> bf16, round to nearest even on the 16 dropped bits; overflow
-// carries into the exponent and gives inf; NaN keeps sign and top payload and
-// gets the quiet bit.
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  uint32_t rne = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-  uint32_t nan = (u >> 16) | 0x40u;
-  return ((u & 0x7FFFFFFFu) > 0x7F800000u) ? nan : rne;
+// fp32 -> bf16, round to nearest even; overflow gives inf; a NaN keeps its
+// sign and top payload bits and gets the quiet bit. gfx950's v_cvt_pk_bf16_f32
+// does exactly this (checked against the integer definition on all 2^32 inputs).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) { return f32x2_to_bf16x2(f, 0.0f) & 0xFFFFu; }
 
-// fp32 -> OCP e4m3fn, round to nearest even. |y| > 464 (past the midpoint
-// above 448), infinities and NaN give 0x7F with the sign of y.
-__device__ __forceinline__ uint32_t f32_to_fp8(float y) {
-  uint32_t u = __float_as_uint(y);
-  uint32_t sign = (u >> 24) & 0x80u;
-  uint32_t a = u & 0x7FFFFFFFu;
-  // normal range [2^-6, 464]: keep 3 mantissa bits, RNE on the 20 dropped bits,
-  // rebias the exponent from 127 to 7
-  uint32_t normal = ((a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
-  // below 2^-6 the grid step is 2^-9: the code is |y| * 2^9 rounded to even
-  uint32_t sub = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
-  uint32_t code = (a < 0x3C800000u) ? sub : normal;
-  code = (a > 0x43E80000u) ? 0x7Fu : code;
-  return sign | code;
+// fp32 -> OCP e4m3fn, round to nearest even; |y| > 464 (past the midpoint
+// above 448) and infinities give 0x7F with the sign of y -- gfx950's
+// v_cvt_pk_fp8_f32 does both; it encodes every NaN as 0xFF, so a NaN is first
+// replaced by 480 with the NaN's sign (checked on all 2^32 inputs).
+__device__ __forceinline__ float fp8_nan_fix(float y) {
+  return (y != y) ? __uint_as_float((__float_as_uint(y) & 0x80000000u) | 0x43F00000u) : y;
+}
+// four values -> four e4m3fn codes, value i in byte i
+__device__ __forceinline__ uint32_t f32x4_to_fp8x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_nan_fix(a), fp8_nan_fix(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_nan_fix(c), fp8_nan_fix(d), w, true);
+  return (uint32_t)w;
+}
+__device__ __forceinline__ uint32_t f32_to_fp8(float y) { return f32x4_to_fp8x4(y, 0.0f, 0.0f, 0.0f) & 0xFFu; }
+
+// x / s for a per-tensor scale, as an IEEE fp32 division: x * RN64(1/s) in
+// fp64 rounded once to fp32 equals the correctly rounded quotient whenever that
+// quotient is a normal number (a bf16 or fp32 x over an fp32 s is never an fp32
+// rounding midpoint and lies at least ~2^-49 (relative) away from one, while the
+// fp64 product is within 2^-52); subnormal quotients take the real division.
+__device__ __forceinline__ bool needs_exact_division(float q) {
+  const float aq = fabsf(q);
+  return aq != 0.0f && aq <= 1.17549435e-38f;
+}
+template <int N>
+__device__ __forceinline__ void div_by_scale(float (&f)[N], float s, double rcp) {
+  float q[N];
+  bool any = false;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    q[i] = (float)((double)f[i] * rcp);
+    any |= needs_exact_division(q[i]);
+  }
+  if (__builtin_expect(any, 0)) {
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if (needs_exact_division(q[i])) q[i] = f[i] / s;
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) f[i] = q[i];
 }
 
 // 8 source elements widened to fp32.
@@ -95,7 +121,7 @@ template <> struct Store8<Ty::BF16> {
   __device__ __forceinline__ static void store(void* p, const float (&f)[8]) {
     u32x4 v;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = f32_to_bf16(f[2 * i]) | (f32_to_bf16(f[2 * i + 1]) << 16);
+    for (int i = 0; i < 4; ++i) v[i] = f32x2_to_bf16x2(f[2 * i], f[2 * i + 1]);
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
   }
 };
@@ -116,9 +142,7 @@ template <> struct Store8<Ty::FP8> {
   __device__ __forceinline__ static void store(void* p, const float (&f)[8]) {
     u32x2 v;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      v[i] = f32_to_fp8(f[4 * i]) | (f32_to_fp8(f[4 * i + 1]) << 8) |
-             (f32_to_fp8(f[4 * i + 2]) << 16) | (f32_to_fp8(f[4 * i + 3]) << 24);
+    for (int i = 0; i < 2; ++i) v[i] = f32x4_to_fp8x4(f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3]);
     __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p));
   }
 };

@@ -13,7 +13,10 @@
 // and the cache, so each lane moves 8-element vectors (16-byte loads of bf16,
 // 8- or 16-byte stores) and a wave stores whole contiguous rows. Rows longer
 // than 64 lanes x kU vectors are split over gridDim.y. Loads and stores are
-// non-temporal: the data is streamed exactly once.
+// non-temporal: the data is streamed exactly once. The division by a scale is
+// a multiply by the fp64 reciprocal (exact for normal quotients, see
+// div_by_scale) and the encodes are the hardware packed converts, which keeps
+// the vector ALU work per element small enough for the copy to stay HBM-bound.
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -82,16 +85,13 @@ __device__ __forceinline__ void store_raw<Ty::F32>(void* p, const F32x8& r) {
 }
 
 template <Ty S, Ty C, bool kScale>
-__device__ __forceinline__ void encode_store(void* dst, const typename Load8<S>::Raw& r, float scale) {
+__device__ __forceinline__ void encode_store(void* dst, const typename Load8<S>::Raw& r, float scale, double rcp) {
   if constexpr (S == C && !kScale) {
     store_raw<S>(dst, r);  // bit copy keeps -0 and NaN payloads
   } else {
     float f[8];
     Load8<S>::widen(r, f);
-    if constexpr (kScale) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) f[i] = f[i] / scale;  // IEEE fp32 division
-    }
+    if constexpr (kScale) div_by_scale<8>(f, scale, rcp);  // = IEEE fp32 f / scale, element-wise
     Store8<C>::store(dst, f);
   }
 }
@@ -110,9 +110,14 @@ __global__ __launch_bounds__(256) void rac_vec_kernel(RacArgs a) {
   const int v0 = (int)blockIdx.y * (64 * kU) + lane;
   const bool has_v = a.value != nullptr;
   float ks = 1.0f, vs = 1.0f;
+  double rk = 1.0, rv = 1.0;
   if constexpr (kScale) {
     ks = *a.k_scale;
-    if (has_v) vs = *a.v_scale;
+    rk = 1.0 / (double)ks;
+    if (has_v) {
+      vs = *a.v_scale;
+      rv = 1.0 / (double)vs;
+    }
   }
   using L = Load8<S>;
   const char* kp = static_cast<const char*>(a.key) + t * a.key_stride * SB;
@@ -134,14 +139,14 @@ __global__ __launch_bounds__(256) void rac_vec_kernel(RacArgs a) {
 #pragma unroll
   for (int u = 0; u < kU; ++u) {
     const int v = v0 + u * 64;
-    if (v < nvec) encode_store<S, C, kScale>(kc + (int64_t)v * 8 * CB, kr[u], ks);
+    if (v < nvec) encode_store<S, C, kScale>(kc + (int64_t)v * 8 * CB, kr[u], ks, rk);
   }
   if (has_v) {
     char* vc = static_cast<char*>(a.value_cache) + dst_row * CB;
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int v = v0 + u * 64;
-      if (v < nvec) encode_store<S, C, kScale>(vc + (int64_t)v * 8 * CB, vr[u], vs);
+      if (v < nvec) encode_store<S, C, kScale>(vc + (int64_t)v * 8 * CB, vr[u], vs, rv);
     }
   }
 }
