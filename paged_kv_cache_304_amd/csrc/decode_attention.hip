@@ -18,8 +18,9 @@
 //    head l%16. Softmax runs there; P.V runs on the vector ALUs with V in a row
 //    layout (16 lanes per cache row, 4 rows per load) in which lane l needs
 //    exactly the probabilities of row group l/16, handed over by DPP
-//    row_newbcast. The next tile's K/V loads are issued before the current
-//    tile is computed. fp8 K is widened to bf16 exactly for the MFMA.
+//    row_newbcast. K is read in whole-row 1 KB wave loads and re-laid out for
+//    the MFMA through a swizzled per-wave LDS tile; fp8 K is widened to bf16
+//    exactly for the MFMA.
 //  * Vector path (other block sizes, D = 256): 8 elements per lane, a cache row spread
 //    over D/8 lanes, QK dots reduced with DPP row operations, one online-softmax
 //    state per row of lanes, merged with lane shuffles at the end.
@@ -42,16 +43,16 @@ namespace pa {
 namespace {
 
 #ifndef PA_DECODE_TARGET_WGS
-#define PA_DECODE_TARGET_WGS 1024
+#define PA_DECODE_TARGET_WGS 8192
 #endif
 #ifndef PA_DECODE_MIN_SPLIT
 #define PA_DECODE_MIN_SPLIT 64
 #endif
 #ifndef PA_DECODE_MAX_SPLIT
-#define PA_DECODE_MAX_SPLIT 256
+#define PA_DECODE_MAX_SPLIT 128
 #endif
-#ifndef PA_DECODE_NT_K
-#define PA_DECODE_NT_K 0
+#ifndef PA_DECODE_K_DMA
+#define PA_DECODE_K_DMA 1
 #endif
 #ifndef PA_DECODE_NT_V
 #define PA_DECODE_NT_V 1
@@ -60,7 +61,7 @@ namespace {
 #define PA_DECODE_PREFETCH 0
 #endif
 #ifndef PA_DECODE_MAX_WAVES
-#define PA_DECODE_MAX_WAVES 4
+#define PA_DECODE_MAX_WAVES 2
 #endif
 #ifndef PA_DECODE_WAVES_PER_EU
 #define PA_DECODE_WAVES_PER_EU 0
@@ -511,26 +512,92 @@ __device__ __forceinline__ void bcast_heads(float x, float (&out)[G]) {
   if constexpr (J + 1 < G) bcast_heads<J + 1, G>(x, out);
 }
 
+// One tile = 16 cache positions of one KV head. K is read in row layout (each
+// 1 KB wave load covers whole rows, the access pattern that streams at full
+// HBM rate) and re-laid out through a per-wave LDS tile into the MFMA operand
+// layout; V stays in registers in the row layout the P.V step uses.
 template <Ty C, int D>
 struct Tile {
-  static constexpr int KS = D / 32;                 // MFMA steps over the head dim
-  static constexpr int EPL = D / 16;                // V dims per lane
-  static constexpr int KW = 8 * TyInfo<C>::kBytes / 4;
-  static constexpr int VW = EPL * TyInfo<C>::kBytes / 4;
-  Dw<KW> k[KS];
-  Dw<VW> v[4];
+  static constexpr int CB = TyInfo<C>::kBytes;
+  static constexpr int RB = D * CB;        // bytes of one head's cache row
+  static constexpr int KB = 16 * RB;       // bytes of a K tile
+  static constexpr int NI = KB / 1024;     // 1 KB wave loads per K tile
+  static constexpr int NC = RB / 16;       // 16-byte chunks per row (LDS swizzle period)
+  static constexpr int KS = D / 32;        // MFMA steps over the head dim
+  static constexpr int EPL = D / 16;       // V dims per lane
+  static constexpr int VW = EPL * CB / 4;  // dwords per V chunk
+  static_assert(KB % 1024 == 0, "K tile must be whole 1 KB wave loads");
+#if !PA_DECODE_K_DMA
+  u32x4 k[NI];   // load i, lane l: tile bytes [1024 i + 16 l, +16)
+#endif
+  Dw<VW> v[4];   // row 4 (l/16) + i of the tile, dims EPL*(l%16) ..
 };
 
 template <Ty C, int D>
 __device__ __forceinline__ void load_tile(Tile<C, D>& t, const char* kc, const char* vc, int64_t blk_el,
-                                          int off, int64_t row_el, int li, int lg) {
-  constexpr int CB = TyInfo<C>::kBytes;
-  const char* kp = kc + (blk_el + (int64_t)(off + li) * row_el + 8 * lg) * CB;
+                                          int off, int64_t row_el, int lane, char* lds) {
+  using T = Tile<C, D>;
+  constexpr int CB = T::CB;
+  const char* kb = kc + (blk_el + (int64_t)off * row_el) * CB;
 #pragma unroll
-  for (int s = 0; s < Tile<C, D>::KS; ++s) t.k[s] = load_dw<Tile<C, D>::KW, PA_DECODE_NT_K>(kp + 32 * s * CB);
-  const char* vp = vc + (blk_el + (int64_t)(off + 4 * lg) * row_el + Tile<C, D>::EPL * li) * CB;
+  for (int i = 0; i < T::NI; ++i) {
+    const int byte = 1024 * i + 16 * lane;
+    const int row = byte / T::RB;
+#if PA_DECODE_K_DMA
+    // straight into this wave's LDS tile: lane l fills LDS slot 1024 i + 16 l,
+    // so it fetches the chunk that the swizzle places there
+    const int pos = (byte % T::RB) / 16;
+    const int col = (pos ^ (row & (T::NC - 1))) * 16;
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kb + (int64_t)row * row_el * CB + col),
+                                     (__attribute__((address_space(3))) void*)(lds + 1024 * i), 16, 0, 0);
+#else
+    const int col = byte % T::RB;
+    t.k[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + (int64_t)row * row_el * CB + col));
+#endif
+  }
+  const int li = lane & 15, lg = lane >> 4;
+  const char* vp = vc + (blk_el + (int64_t)(off + 4 * lg) * row_el + T::EPL * li) * CB;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) t.v[i] = load_dw<Tile<C, D>::VW, PA_DECODE_NT_V>(vp + (int64_t)i * row_el * CB);
+  for (int i = 0; i < 4; ++i) t.v[i] = load_dw<T::VW, PA_DECODE_NT_V>(vp + (int64_t)i * row_el * CB);
+}
+
+// K tile -> this wave's LDS tile, row-major with the 16-byte chunks of row r
+// XOR-swizzled by r, so that the 16 rows read at one column land in distinct banks.
+template <Ty C, int D>
+__device__ __forceinline__ void stage_k(const Tile<C, D>& t, char* lds, int lane) {
+  using T = Tile<C, D>;
+#if PA_DECODE_K_DMA
+  // the loads wrote LDS directly; the compiler does not track that, so wait
+  // for every outstanding vector memory operation before the tile is read
+  (void)t;
+  (void)lane;
+  (void)lds;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#else
+#pragma unroll
+  for (int i = 0; i < T::NI; ++i) {
+    const int byte = 1024 * i + 16 * lane;
+    const int row = byte / T::RB, c16 = (byte % T::RB) / 16;
+    *reinterpret_cast<u32x4*>(lds + row * T::RB + ((c16 ^ (row & (T::NC - 1))) * 16)) = t.k[i];
+  }
+#endif
+}
+
+// MFMA A operand of step s: dims [32 s + 8 lg, +8) of tile row li.
+template <Ty C, int D>
+__device__ __forceinline__ bf16x8 k_operand(const char* lds, int s, int li, int lg) {
+  using T = Tile<C, D>;
+  const int byte = (32 * s + 8 * lg) * T::CB;
+  const char* p = lds + li * T::RB + (((byte / 16) ^ (li & (T::NC - 1))) * 16) + (byte % 16);
+  if constexpr (C == Ty::BF16) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+  } else {
+    const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+    Dw<2> d;
+    d.w[0] = w[0];
+    d.w[1] = w[1];
+    return as_bf16x8<C>(d);
+  }
 }
 
 template <Ty C, int D, int G>
@@ -545,29 +612,36 @@ __global__ __launch_bounds__(512) PA_SPLIT_OCCUPANCY void decode_split_mfma_kern
   const bool active = g < a.HKV;
   const int split = blockIdx.y;
   const int b = blockIdx.z;
-  const int ctx = clamp_ctx(a, b);
+  __shared__ __attribute__((aligned(16))) char k_lds[kMaxWaves * T::KB];
+  // Start-up loads are issued together (one memory round trip): the context
+  // length, this split's block-table entries (one per lane; a split spans <= 64
+  // blocks) and q; none of their addresses depends on the context length.
+  const int ctx_raw = a.ctx_lens[b];
+  const int j0 = split * a.split_blocks;
+  const int bt_lane = (lane < a.split_blocks && j0 + lane < a.W) ? a.bt[(int64_t)b * a.W + j0 + lane] : -1;
+  bf16x8 qb[KS];
+  {
+    const int gq = g < a.HKV ? g : a.HKV - 1;
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (int64_t)b * a.q_seq_stride +
+                         (int64_t)(gq * G + (li < G ? li : 0)) * D + 8 * lg;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      u32x4 w = *reinterpret_cast<const u32x4*>(qp + 32 * s);
+      if (li >= G) w = u32x4{0, 0, 0, 0};
+      qb[s] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+  const int cap = a.W * a.block_size;
+  const int ctx = ctx_raw < 0 ? 0 : (ctx_raw > cap ? cap : ctx_raw);
   const int nblk = (ctx + a.block_size - 1) / a.block_size;
   const int nsplit = max(1, (nblk + a.split_blocks - 1) / a.split_blocks);
   if (split >= nsplit) return;  // uniform over the workgroup
 
   if (active) {
-    const int j0 = split * a.split_blocks;
     const int j1 = min(nblk, j0 + a.split_blocks);
     const int p_begin = j0 * a.block_size;
     const int p_end = min(ctx, j1 * a.block_size);
     const int n_tiles = p_end > p_begin ? (p_end - p_begin + 15) >> 4 : 0;
-
-    bf16x8 qb[KS];
-    {
-      const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (int64_t)b * a.q_seq_stride +
-                           (int64_t)(g * G + (li < G ? li : 0)) * D + 8 * lg;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        u32x4 w = *reinterpret_cast<const u32x4*>(qp + 32 * s);
-        if (li >= G) w = u32x4{0, 0, 0, 0};
-        qb[s] = __builtin_bit_cast(bf16x8, w);
-      }
-    }
     const float ks = a.k_scale ? *a.k_scale : 1.0f;
     const float vs = a.v_scale ? *a.v_scale : 1.0f;
     const float sl2 = a.scale_log2 * ks;
@@ -580,9 +654,9 @@ __global__ __launch_bounds__(512) PA_SPLIT_OCCUPANCY void decode_split_mfma_kern
       for (int k = 0; k < EPL; ++k) acc[j][k] = 0.0f;
 
     const int64_t row_el = (int64_t)a.HKV * D;  // elements between consecutive slots of a block
-    const int32_t* bt = a.bt + (int64_t)b * a.W;
     const char* kc = static_cast<const char*>(a.kc);
     const char* vc = static_cast<const char*>(a.vc);
+    char* my_lds = k_lds + wave * T::KB;
 
     // Tile t covers positions p_begin + 16t .. +15, all inside one block. Loads
     // are issued unconditionally so that the compiler keeps the next tile's
@@ -592,19 +666,20 @@ __global__ __launch_bounds__(512) PA_SPLIT_OCCUPANCY void decode_split_mfma_kern
     auto fetch = [&](T& tile, int t) -> bool {
       const int tc = min(t, n_tiles - 1);
       const int p0 = p_begin + 16 * tc;
-      const int phys = bt[p0 / a.block_size];
+      const int phys = __builtin_amdgcn_readlane(bt_lane, (16 * tc) / a.block_size);
       const bool ok = t < n_tiles && phys >= 0 && (int64_t)phys < a.num_blocks;
       load_tile<C, D>(tile, kc, vc, (int64_t)(ok ? phys : 0) * a.block_stride + (int64_t)g * D,
-                      p0 % a.block_size, row_el, li, lg);
+                      p0 % a.block_size, row_el, lane, my_lds);
       return ok;
     };
     // kMask: the tile reaches past the context end (only the last one can).
     auto compute = [&](const T& tile, int t, auto mask_tag) {
       constexpr bool kMask = decltype(mask_tag)::value;
+      stage_k<C, D>(tile, my_lds, lane);
       f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int s = 0; s < KS; ++s)
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8<C>(tile.k[s]), qb[s], sc, 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<C, D>(my_lds, s, li, lg), qb[s], sc, 0, 0, 0);
       const int prow = p_begin + 16 * t + 4 * lg;  // position of this lane's first score / V row
       float sr[4];
 #pragma unroll
@@ -711,7 +786,9 @@ Plan make_plan(int num_seqs, int HQ, int HKV, int D, int W, int bs) {
   // splits of kMinSplitTokens..kMaxSplitTokens positions.
   const int64_t per_seq = ((int64_t)kTargetWgs + (int64_t)num_seqs * p.kv_groups - 1) / ((int64_t)num_seqs * p.kv_groups);
   int sb = (int)((W + per_seq - 1) / per_seq);
-  const int lo = (kMinSplitTokens + bs - 1) / bs, hi = kMaxSplitTokens / bs > lo ? kMaxSplitTokens / bs : lo;
+  const int lo = (kMinSplitTokens + bs - 1) / bs;
+  int hi = kMaxSplitTokens / bs > lo ? kMaxSplitTokens / bs : lo;
+  if (hi > 64) hi = 64;  // the matrix-core kernel keeps a split's table entries in one wave's lanes
   sb = sb < lo ? lo : (sb > hi ? hi : sb);
   if (sb > W) sb = W;
   if (sb < 1) sb = 1;
