@@ -7,33 +7,40 @@
 // and q head h, softmax over the first ctx_b cached positions of
 // scale * q . K^ (K^ = K * k_scale), weights applied to V^ = V * v_scale.
 //
-// gfx950 design: split-K over logical blocks, then a merge launch.
-//  * Workgroup = (KV-head group, KV split, sequence) with one wavefront per KV
-//    head, so the waves of a workgroup read every head of the same physical
-//    blocks together, i.e. whole contiguous [block_size, H_KV, D] pages.
-//  * Matrix-core path (block_size a multiple of 16, D <= 128): a tile is 16 positions of
-//    one head. QK^T is one v_mfma_f32_16x16x32_bf16 per 32 head dims with the
-//    K tile as A (row = position) and the G query heads of the group as B
-//    columns, so lane l receives the scores of positions 4*(l/16)+r (r<4) for
-//    head l%16. Softmax runs there; P.V runs on the vector ALUs with V in a row
-//    layout (16 lanes per cache row, 4 rows per load) in which lane l needs
-//    exactly the probabilities of row group l/16, handed over by DPP
-//    row_newbcast. K is read in whole-row 1 KB wave loads and re-laid out for
-//    the MFMA through a swizzled per-wave LDS tile; fp8 K is widened to bf16
-//    exactly for the MFMA.
-//  * Vector path (other block sizes, D = 256): 8 elements per lane, a cache row spread
-//    over D/8 lanes, QK dots reduced with DPP row operations, one online-softmax
-//    state per row of lanes, merged with lane shuffles at the end.
-//  * A sequence that needs one split writes its output directly. Otherwise each
-//    split stores (max, sum, normalised output) per q head in the workspace and
-//    a second, small launch merges them (lanes over splits for the weights,
-//    lanes over dims for the outputs).
-//  * Split boundaries depend only on logical block indices, so the result is
+// gfx950 design: split-K over logical positions, then a merge launch.
+//  * A workgroup serves one group of KV heads with one wavefront per head, so
+//    its waves read every head of the same physical blocks together.
+//  * Matrix-core path (block_size a multiple of 16, D <= 128): a persistent
+//    kernel. Exactly as many workgroups as the chip holds at once are
+//    launched (the hardware hands workgroups to the XCDs round-robin and
+//    stalls every XCD when the next one's XCD is full, so a grid of uneven
+//    split workgroups leaves compute units idle); each scans the context
+//    lengths and takes equal ranges of the flattened (sequence, 16-position
+//    tile) list. A tile is 16 positions of one head: QK^T is one
+//    v_mfma_f32_16x16x32_bf16 per 32 head dims with the K tile as A (row =
+//    position) and the G query heads of the group as B columns, so lane l
+//    receives the scores of positions 4*(l/16)+r (r<4) for head l%16. Softmax
+//    runs there; P.V runs on the vector ALUs with V in a row layout (16 lanes
+//    per cache row, 4 rows per load) in which lane l needs exactly the
+//    probabilities of row group l/16, handed over by DPP row_newbcast. K tiles
+//    and q rows are fetched straight into LDS (K in whole-row 1 KB wave loads,
+//    re-laid out by an XOR swizzle for the MFMA operand reads); fp8 K is
+//    widened to bf16 exactly for the MFMA.
+//  * Vector path (other block sizes, D = 256): one workgroup per (head group,
+//    split, sequence); 8 elements per lane, a cache row spread over D/8
+//    lanes, QK dots reduced with DPP row operations, one online-softmax state
+//    per row of lanes, merged with lane shuffles at the end.
+//  * A sequence that needs one split (chunk) writes its output directly.
+//    Otherwise each piece stores (max, sum, normalised output) per q head in
+//    the workspace and a second, small launch merges them (lanes over pieces
+//    for the weights, lanes over dims for the outputs).
+//  * Piece boundaries depend only on the context lengths, so the result is
 //    bit-identical under any relabelling of physical blocks.
 // Scores are kept in the log2 domain (scale * log2(e) folded in) so that each
 // exponential is one v_exp_f32.
 #include <math.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "pa_device.h"
@@ -57,19 +64,8 @@ namespace {
 #ifndef PA_DECODE_NT_V
 #define PA_DECODE_NT_V 1
 #endif
-#ifndef PA_DECODE_PREFETCH
-#define PA_DECODE_PREFETCH 0
-#endif
 #ifndef PA_DECODE_MAX_WAVES
 #define PA_DECODE_MAX_WAVES 2
-#endif
-#ifndef PA_DECODE_WAVES_PER_EU
-#define PA_DECODE_WAVES_PER_EU 0
-#endif
-#if PA_DECODE_WAVES_PER_EU > 0
-#define PA_SPLIT_OCCUPANCY __attribute__((amdgpu_waves_per_eu(PA_DECODE_WAVES_PER_EU, 8)))
-#else
-#define PA_SPLIT_OCCUPANCY
 #endif
 constexpr int kMaxWaves = PA_DECODE_MAX_WAVES;        // KV heads (waves) per workgroup
 constexpr int kTargetWgs = PA_DECODE_TARGET_WGS;      // split workgroups aimed for if every sequence used all W blocks
@@ -88,6 +84,7 @@ struct DecArgs {
   float* ws_m;
   float* ws_l;
   float* ws_o;
+  int32_t* ws_n;           // persistent kernel: chunks per sequence (null for the grid kernel)
   int64_t out_seq_stride;  // elements
   int64_t q_seq_stride;    // elements
   int64_t block_stride;    // elements
@@ -101,6 +98,7 @@ struct DecArgs {
   int32_t max_splits;
   int32_t waves_per_wg;
   int32_t kv_groups;
+  int32_t slots;           // persistent kernel: workgroups per KV-head group
   int32_t out_f32;
   float scale_log2;        // softmax_scale * log2(e)
 };
@@ -280,16 +278,35 @@ __device__ __forceinline__ void merge_head(const DecArgs& a, int b, int h, int n
 }
 
 // Merge pass: one wave per (sequence, q head), four waves per workgroup.
-// Sequences that fit one split were written by the split pass. (A merge inside
-// the split kernel would need an agent-scope release/acquire per workgroup,
-// i.e. an L2 write-back on its XCD for every split; the kernel boundary gives
-// that ordering for free.)
+// Sequences that fit one split (chunk) were written by the split pass; after
+// the persistent kernel the merge pass also writes the zeros of empty
+// sequences. (A merge inside the split kernel would need an agent-scope
+// release/acquire per workgroup, i.e. an L2 write-back on its XCD for every
+// split; the kernel boundary gives that ordering for free.)
 template <int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecArgs a) {
   const int wid = (int)blockIdx.x * 4 + uniform(threadIdx.x >> 6);
   if (wid >= a.num_seqs * a.HQ) return;
   const int b = wid / a.HQ, h = wid - b * a.HQ;
   const int ctx = clamp_ctx(a, b);
+  if (a.ws_n) {
+    if (ctx == 0) {
+      const float z[D / 64] = {};
+      const int lane = threadIdx.x & 63;
+#pragma unroll
+      for (int i = 0; i < D / 64; ++i) {
+        const int64_t at = (int64_t)b * a.out_seq_stride + (int64_t)h * D + lane + 64 * i;
+        if (a.out_f32)
+          static_cast<float*>(a.out)[at] = z[i];
+        else
+          static_cast<uint16_t*>(a.out)[at] = 0;
+      }
+      return;
+    }
+    const int n = a.ws_n[b];
+    if (n > 1) merge_head<D>(a, b, h, n);
+    return;
+  }
   const int nblk = (ctx + a.block_size - 1) / a.block_size;
   const int nsplit = (nblk + a.split_blocks - 1) / a.split_blocks;
   if (nsplit <= 1) return;
@@ -565,7 +582,6 @@ __device__ __forceinline__ void load_tile(Tile<C, D>& t, const char* kc, const c
 // XOR-swizzled by r, so that the 16 rows read at one column land in distinct banks.
 template <Ty C, int D>
 __device__ __forceinline__ void stage_k(const Tile<C, D>& t, char* lds, int lane) {
-  using T = Tile<C, D>;
 #if PA_DECODE_K_DMA
   // the loads wrote LDS directly; the compiler does not track that, so wait
   // for every outstanding vector memory operation before the tile is read
@@ -574,6 +590,7 @@ __device__ __forceinline__ void stage_k(const Tile<C, D>& t, char* lds, int lane
   (void)lds;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #else
+  using T = Tile<C, D>;
 #pragma unroll
   for (int i = 0; i < T::NI; ++i) {
     const int byte = 1024 * i + 16 * lane;
@@ -600,171 +617,243 @@ __device__ __forceinline__ bf16x8 k_operand(const char* lds, int s, int li, int 
   }
 }
 
+// Persistent matrix-core kernel. The work of one KV-head group is the list of
+// (sequence, 16-position tile) pairs in sequence order, T tiles in all. Each of
+// the `slots` workgroups of a group takes ranges of RT consecutive tiles (RT <= 64,
+// ranges r = slot, slot + slots, ...), so every workgroup streams the same
+// number of tiles and no workgroup is launched without work. A range cuts the
+// sequences it touches into segments; the c-th range touching a sequence
+// yields its chunk c, stored in the workspace for the merge pass, or written
+// straight to the output when the sequence has a single chunk. Chunk
+// boundaries depend only on the context lengths (never on physical block ids
+// or on the processing order), so results are reproducible.
+constexpr int kRangeMaxTiles = 64;  // a segment's blocks then fit one 64-lane table window
+constexpr int kRangeMinTiles = 8;   // bounds the chunks per sequence (workspace size)
+constexpr int kSegMax = kRangeMaxTiles;  // each segment holds >= 1 tile of the range
+
+__device__ __forceinline__ int tiles_of(int ctx) { return (ctx + 15) >> 4; }
+
+// Waves per SIMD the persistent kernel is compiled for (its register budget):
+// the natural allocation of each shape, except that MFMA accumulator registers
+// must not push the D = 128, G <= 2 shapes past 128 registers.
+constexpr int persistent_waves_per_eu(int D, int G) {
+  return D == 64 ? (G <= 2 ? 5 : (G == 4 ? 4 : 3)) : (G <= 2 ? 4 : (G == 4 ? 3 : 2));
+}
+
 template <Ty C, int D, int G>
-__global__ __launch_bounds__(512) PA_SPLIT_OCCUPANCY void decode_split_mfma_kernel(DecArgs a) {
+__global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(persistent_waves_per_eu(D, G), 8)))
+void decode_persistent_kernel(DecArgs a) {
   using T = Tile<C, D>;
   constexpr int KS = T::KS;
   constexpr int EPL = T::EPL;
-  const int lane = threadIdx.x & 63;
+  constexpr int QB = G * D * 2;           // bytes of the group's q rows
+  constexpr int QI = (QB + 1023) / 1024;  // 1 KB wave loads per q buffer
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
   const int li = lane & 15, lg = lane >> 4;
-  const int wave = uniform(threadIdx.x >> 6);
-  const int g = (int)blockIdx.x * a.waves_per_wg + wave;
+  const int wave = uniform(tid >> 6);
+  const int nthr = 64 * a.waves_per_wg;
+  const int gr = (int)blockIdx.x % a.kv_groups;
+  const int slot = (int)blockIdx.x / a.kv_groups;
+  const int g = gr * a.waves_per_wg + wave;
   const bool active = g < a.HKV;
-  const int split = blockIdx.y;
-  const int b = blockIdx.z;
+
   __shared__ __attribute__((aligned(16))) char k_lds[kMaxWaves * T::KB];
-  // Start-up loads are issued together (one memory round trip): the context
-  // length, this split's block-table entries (one per lane; a split spans <= 64
-  // blocks) and q; none of their addresses depends on the context length.
-  const int ctx_raw = a.ctx_lens[b];
-  const int j0 = split * a.split_blocks;
-  const int bt_lane = (lane < a.split_blocks && j0 + lane < a.W) ? a.bt[(int64_t)b * a.W + j0 + lane] : -1;
-  bf16x8 qb[KS];
-  {
-    const int gq = g < a.HKV ? g : a.HKV - 1;
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (int64_t)b * a.q_seq_stride +
-                         (int64_t)(gq * G + (li < G ? li : 0)) * D + 8 * lg;
+  __shared__ __attribute__((aligned(16))) char q_lds[kMaxWaves * 2 * QB];
+  __shared__ int seg_b[kSegMax], seg_t0[kSegMax], seg_t1[kSegMax], seg_ctx[kSegMax], seg_k[kSegMax], seg_n[kSegMax];
+  __shared__ int64_t wave_tiles[kMaxWaves];
+  __shared__ int seg_count;
+
+  // Tile counts of all sequences and their prefix sums: thread i owns a
+  // contiguous run of sequences; a wave scan plus the per-wave totals give the
+  // first tile index of each run.
+  const int per = (a.num_seqs + nthr - 1) / nthr;
+  const int b_lo = min(a.num_seqs, tid * per), b_hi = min(a.num_seqs, b_lo + per);
+  int64_t mine = 0;
+  for (int b = b_lo; b < b_hi; ++b) mine += tiles_of(clamp_ctx(a, b));
+  int64_t incl = mine;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      u32x4 w = *reinterpret_cast<const u32x4*>(qp + 32 * s);
-      if (li >= G) w = u32x4{0, 0, 0, 0};
-      qb[s] = __builtin_bit_cast(bf16x8, w);
-    }
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t y = __shfl_up(incl, (unsigned)o, 64);
+    if (lane >= o) incl += y;
   }
-  const int cap = a.W * a.block_size;
-  const int ctx = ctx_raw < 0 ? 0 : (ctx_raw > cap ? cap : ctx_raw);
-  const int nblk = (ctx + a.block_size - 1) / a.block_size;
-  const int nsplit = max(1, (nblk + a.split_blocks - 1) / a.split_blocks);
-  if (split >= nsplit) return;  // uniform over the workgroup
+  if (lane == 63) wave_tiles[wave] = incl;
+  __syncthreads();
+  int64_t total = 0, before = 0;
+  for (int w = 0; w < a.waves_per_wg; ++w) {
+    const int64_t v = wave_tiles[w];
+    total += v;
+    if (w < wave) before += v;
+  }
+  const int64_t run_first = before + incl - mine;
+  if (total == 0) return;  // uniform: every sequence is empty (the merge pass writes zeros)
+  const int64_t per_round = (int64_t)kRangeMaxTiles * a.slots;
+  const int64_t rounds = (total + per_round - 1) / per_round;
+  int64_t RT = (total + rounds * a.slots - 1) / (rounds * a.slots);  // tiles per range
+  if (RT < kRangeMinTiles) RT = kRangeMinTiles;
+  const int64_t R = (total + RT - 1) / RT;
 
-  if (active) {
-    const int j1 = min(nblk, j0 + a.split_blocks);
-    const int p_begin = j0 * a.block_size;
-    const int p_end = min(ctx, j1 * a.block_size);
-    const int n_tiles = p_end > p_begin ? (p_end - p_begin + 15) >> 4 : 0;
-    const float ks = a.k_scale ? *a.k_scale : 1.0f;
-    const float vs = a.v_scale ? *a.v_scale : 1.0f;
-    const float sl2 = a.scale_log2 * ks;
+  const float ks = a.k_scale ? *a.k_scale : 1.0f;
+  const float vs = a.v_scale ? *a.v_scale : 1.0f;
+  const float sl2 = a.scale_log2 * ks;
+  const int64_t row_el = (int64_t)a.HKV * D;  // elements between consecutive slots of a block
+  const char* kc = static_cast<const char*>(a.kc);
+  const char* vc = static_cast<const char*>(a.vc);
+  char* my_lds = k_lds + wave * T::KB;
 
-    float m_run = -INFINITY, l_run = 0.0f;
-    float acc[G][EPL];
-#pragma unroll
-    for (int j = 0; j < G; ++j)
-#pragma unroll
-      for (int k = 0; k < EPL; ++k) acc[j][k] = 0.0f;
-
-    const int64_t row_el = (int64_t)a.HKV * D;  // elements between consecutive slots of a block
-    const char* kc = static_cast<const char*>(a.kc);
-    const char* vc = static_cast<const char*>(a.vc);
-    char* my_lds = k_lds + wave * T::KB;
-
-    // Tile t covers positions p_begin + 16t .. +15, all inside one block. Loads
-    // are issued unconditionally so that the compiler keeps the next tile's
-    // loads in flight while the current tile is computed: a tile index past the
-    // end is clamped to the last tile (a cache hit) and a block outside the pool
-    // is read as block 0; both come back flagged as not to be attended.
-    auto fetch = [&](T& tile, int t) -> bool {
-      const int tc = min(t, n_tiles - 1);
-      const int p0 = p_begin + 16 * tc;
-      const int phys = __builtin_amdgcn_readlane(bt_lane, (16 * tc) / a.block_size);
-      const bool ok = t < n_tiles && phys >= 0 && (int64_t)phys < a.num_blocks;
-      load_tile<C, D>(tile, kc, vc, (int64_t)(ok ? phys : 0) * a.block_stride + (int64_t)g * D,
-                      p0 % a.block_size, row_el, lane, my_lds);
-      return ok;
-    };
-    // kMask: the tile reaches past the context end (only the last one can).
-    auto compute = [&](const T& tile, int t, auto mask_tag) {
-      constexpr bool kMask = decltype(mask_tag)::value;
-      stage_k<C, D>(tile, my_lds, lane);
-      f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int s = 0; s < KS; ++s)
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<C, D>(my_lds, s, li, lg), qb[s], sc, 0, 0, 0);
-      const int prow = p_begin + 16 * t + 4 * lg;  // position of this lane's first score / V row
-      float sr[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        sr[r] = sc[r] * sl2;
-        if constexpr (kMask) sr[r] = (prow + r < p_end) ? sr[r] : -INFINITY;
+  for (int64_t r = slot; r < R; r += a.slots) {
+    // Segment list of range r: [U0, U1) intersected with each sequence.
+    const int64_t U0 = r * RT, U1 = min(total, U0 + RT);
+    if (tid == 0) seg_count = 0;
+    __syncthreads();
+    if (run_first < U1 && run_first + mine > U0) {
+      int64_t S = run_first;
+      for (int b = b_lo; b < b_hi && S < U1; ++b) {
+        const int ctx = clamp_ctx(a, b);
+        const int nt = tiles_of(ctx);
+        if (nt > 0 && S + nt > U0) {
+          const int i = atomicAdd(&seg_count, 1);
+          const int64_t lo = max(U0, S), hi = min(U1, S + nt);
+          seg_b[i] = b;
+          seg_t0[i] = (int)(lo - S);
+          seg_t1[i] = (int)(hi - S);
+          seg_ctx[i] = ctx;
+          seg_k[i] = (int)(lo / RT - S / RT);
+          seg_n[i] = (int)((S + nt - 1) / RT - S / RT + 1);
+        }
+        S += nt;
       }
-      float mx = fmaxf(fmaxf(sr[0], sr[1]), fmaxf(sr[2], sr[3]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mn = fmaxf(m_run, mx);
-      const float mu = (mn == -INFINITY) ? 0.0f : mn;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - mu);
-      float pr[4];
-      float ps = 0.0f;
+    }
+    __syncthreads();
+    const int nseg = seg_count;
+
+    if (active) {
+      // q rows of segment i into q buffer `buf` (straight to LDS), and this
+      // lane's block-table entry of the segment's 64-block window.
+      auto issue = [&](int i, int buf) -> int {
+        const int b = seg_b[i];
+        const int wb0 = (16 * seg_t0[i]) / a.block_size;
+        const char* qs = static_cast<const char*>(a.q) + ((int64_t)b * a.q_seq_stride + (int64_t)g * G * D) * 2;
+        char* qd = q_lds + (wave * 2 + buf) * QB;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pr[r] = __builtin_amdgcn_exp2f(sr[r] - mu);
-        ps += pr[r];
-      }
-      l_run = l_run * alpha + ps;
-      m_run = mn;
-      rescale_heads<0, G, EPL>(acc, alpha);
+        for (int j = 0; j < QI; ++j) {
+          const int byte = 1024 * j + 16 * lane;
+          if (byte < QB)
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(qs + byte),
+                                             (__attribute__((address_space(3))) void*)(qd + 1024 * j), 16, 0, 0);
+        }
+        return (wb0 + lane < a.W) ? a.bt[(int64_t)b * a.W + wb0 + lane] : -1;
+      };
+
+      int bt_cur = nseg > 0 ? issue(0, 0) : -1;
+      for (int i = 0; i < nseg; ++i) {
+        const int bt_nxt = (i + 1 < nseg) ? issue(i + 1, (i + 1) & 1) : -1;
+        const int b = seg_b[i], t0 = seg_t0[i], t1 = seg_t1[i];
+        const int chunk = seg_k[i], nch = seg_n[i];
+        const int p_end = min(seg_ctx[i], 16 * t1);
+        const int wb0 = (16 * t0) / a.block_size;
+        // B operand rows: lane column li holds head li of the group (lanes
+        // past G repeat a head; their columns are never read).
+        const char* qrow = q_lds + (wave * 2 + (i & 1)) * QB + ((li & (G - 1)) * D + 8 * lg) * 2;
+
+        float m_run = -INFINITY, l_run = 0.0f;
+        float acc[G][EPL];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float vf[EPL];
-        widen_dw<C>(tile.v[i], vf);
-        if constexpr (kMask) {
-          if (prow + i >= p_end) {
+        for (int j = 0; j < G; ++j)
 #pragma unroll
-            for (int k = 0; k < EPL; ++k) vf[k] = 0.0f;  // unwritten slots may hold NaN
+          for (int k = 0; k < EPL; ++k) acc[j][k] = 0.0f;
+
+        auto fetch = [&](T& tile, int t) -> bool {
+          const int phys = __builtin_amdgcn_readlane(bt_cur, (16 * t) / a.block_size - wb0);
+          const bool ok = phys >= 0 && (int64_t)phys < a.num_blocks;
+          load_tile<C, D>(tile, kc, vc, (int64_t)(ok ? phys : 0) * a.block_stride + (int64_t)g * D,
+                          (16 * t) % a.block_size, row_el, lane, my_lds);
+          return ok;
+        };
+        // kMask: the tile reaches past the context end (only a sequence's last one can).
+        auto compute = [&](const T& tile, int t, auto mask_tag) {
+          constexpr bool kMask = decltype(mask_tag)::value;
+          stage_k<C, D>(tile, my_lds, lane);
+          f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int s = 0; s < KS; ++s) {
+            const bf16x8 qb = *reinterpret_cast<const bf16x8*>(qrow + 64 * s);
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<C, D>(my_lds, s, li, lg), qb, sc, 0, 0, 0);
+          }
+          const int prow = 16 * t + 4 * lg;  // position of this lane's first score / V row
+          float sr[4];
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            sr[r4] = sc[r4] * sl2;
+            if constexpr (kMask) sr[r4] = (prow + r4 < p_end) ? sr[r4] : -INFINITY;
+          }
+          float mx = fmaxf(fmaxf(sr[0], sr[1]), fmaxf(sr[2], sr[3]));
+          mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+          mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+          const float mn = fmaxf(m_run, mx);
+          const float mu = (mn == -INFINITY) ? 0.0f : mn;
+          const float alpha = __builtin_amdgcn_exp2f(m_run - mu);
+          float pr[4];
+          float ps = 0.0f;
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            pr[r4] = __builtin_amdgcn_exp2f(sr[r4] - mu);
+            ps += pr[r4];
+          }
+          l_run = l_run * alpha + ps;
+          m_run = mn;
+          rescale_heads<0, G, EPL>(acc, alpha);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            float vf[EPL];
+            widen_dw<C>(tile.v[v], vf);
+            if constexpr (kMask) {
+              if (prow + v >= p_end) {
+#pragma unroll
+                for (int k = 0; k < EPL; ++k) vf[k] = 0.0f;  // unwritten slots may hold NaN
+              }
+            }
+            accumulate_row<0, G, EPL>(acc, pr[v], vf);
+          }
+        };
+
+        for (int t = t0; t < t1; ++t) {
+          T tile;
+          const bool ok = fetch(tile, t);
+          if (ok) {
+            if (16 * t + 16 <= p_end)
+              compute(tile, t, std::false_type{});
+            else
+              compute(tile, t, std::true_type{});
           }
         }
-        accumulate_row<0, G, EPL>(acc, pr[i], vf);
-      }
-    };
-    auto run = [&](const T& tile, int t, bool ok) {
-      if (!ok) return;
-      if (p_begin + 16 * t + 16 <= p_end)
-        compute(tile, t, std::false_type{});
-      else
-        compute(tile, t, std::true_type{});
-    };
 
-    if (n_tiles > 0 && a.num_blocks > 0) {
-#if PA_DECODE_PREFETCH
-      // Two register tiles: the next tile is in flight while one is computed.
-      T ta, tb;
-      bool oka = fetch(ta, 0);
-      for (int t = 0; t < n_tiles; t += 2) {
-        const bool okb = fetch(tb, t + 1);
-        run(ta, t, oka);
-        oka = fetch(ta, t + 2);
-        run(tb, t + 1, okb);
-      }
-#else
-      for (int t = 0; t < n_tiles; ++t) {
-        T ta;
-        const bool ok = fetch(ta, t);
-        run(ta, t, ok);
-      }
-#endif
-    }
-
-    // Sum the four row groups (same running max everywhere: no rescaling).
+        // Sum the four row groups (same running max everywhere: no rescaling).
 #pragma unroll
-    for (int msk = 16; msk < 64; msk <<= 1) {
-      l_run += __shfl_xor(l_run, msk, 64);
+        for (int msk = 16; msk < 64; msk <<= 1) {
+          l_run += __shfl_xor(l_run, msk, 64);
 #pragma unroll
-      for (int j = 0; j < G; ++j)
+          for (int j = 0; j < G; ++j)
 #pragma unroll
-        for (int k = 0; k < EPL; ++k) acc[j][k] += __shfl_xor(acc[j][k], msk, 64);
-    }
-    float lj[G];
-    bcast_heads<0, G>(l_run, lj);
-    if (lg == 0) {
+            for (int k = 0; k < EPL; ++k) acc[j][k] += __shfl_xor(acc[j][k], msk, 64);
+        }
+        float lj[G];
+        bcast_heads<0, G>(l_run, lj);
+        if (lg == 0) {
 #pragma unroll
-      for (int j = 0; j < G; ++j) {
-        const float inv = lj[j] > 0.0f ? vs / lj[j] : 0.0f;
-        float o[EPL];
+          for (int j = 0; j < G; ++j) {
+            const float inv = lj[j] > 0.0f ? vs / lj[j] : 0.0f;
+            float o[EPL];
 #pragma unroll
-        for (int k = 0; k < EPL; ++k) o[k] = acc[j][k] * inv;
-        store_split<D, EPL>(a, b, g * G + j, split, nsplit, EPL * li, o, li == j, m_run, lj[j]);
+            for (int k = 0; k < EPL; ++k) o[k] = acc[j][k] * inv;
+            store_split<D, EPL>(a, b, g * G + j, chunk, nch, EPL * li, o, li == j, m_run, lj[j]);
+          }
+        }
+        if (chunk == 0 && g == 0 && lane == 0) a.ws_n[b] = nch;
+        bt_cur = bt_nxt;
       }
     }
+    __syncthreads();  // the segment list is rebuilt for the next range
   }
 }
 
@@ -772,63 +861,110 @@ __global__ __launch_bounds__(512) PA_SPLIT_OCCUPANCY void decode_split_mfma_kern
 // Host side
 // ---------------------------------------------------------------------------
 struct Plan {
+  bool persistent;  // matrix-core persistent kernel (block_size % 16 == 0, D <= 128)
   int waves_per_wg, kv_groups, split_blocks, max_splits;
-  size_t off_m, off_l, off_o, bytes;
+  size_t off_n, off_m, off_l, off_o, bytes;
 };
 
 inline size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 Plan make_plan(int num_seqs, int HQ, int HKV, int D, int W, int bs) {
   Plan p;
+  p.persistent = bs % 16 == 0 && D <= 128;
   p.waves_per_wg = HKV < kMaxWaves ? HKV : kMaxWaves;
   p.kv_groups = (HKV + p.waves_per_wg - 1) / p.waves_per_wg;
-  // Aim for kTargetWgs workgroups if every sequence used all W blocks, with
-  // splits of kMinSplitTokens..kMaxSplitTokens positions.
-  const int64_t per_seq = ((int64_t)kTargetWgs + (int64_t)num_seqs * p.kv_groups - 1) / ((int64_t)num_seqs * p.kv_groups);
-  int sb = (int)((W + per_seq - 1) / per_seq);
-  const int lo = (kMinSplitTokens + bs - 1) / bs;
-  int hi = kMaxSplitTokens / bs > lo ? kMaxSplitTokens / bs : lo;
-  if (hi > 64) hi = 64;  // the matrix-core kernel keeps a split's table entries in one wave's lanes
-  sb = sb < lo ? lo : (sb > hi ? hi : sb);
-  if (sb > W) sb = W;
-  if (sb < 1) sb = 1;
-  p.split_blocks = sb;
-  p.max_splits = (W + sb - 1) / sb;
+  if (p.persistent) {
+    // a sequence of n tiles meets at most ceil(n / kRangeMinTiles) + 1 ranges
+    const int64_t nt_max = ((int64_t)W * bs + 15) / 16;
+    p.split_blocks = 0;
+    p.max_splits = (int)((nt_max + kRangeMinTiles - 1) / kRangeMinTiles + 1);
+  } else {
+    // Aim for kTargetWgs workgroups if every sequence used all W blocks, with
+    // splits of kMinSplitTokens..kMaxSplitTokens positions.
+    const int64_t per_seq = ((int64_t)kTargetWgs + (int64_t)num_seqs * p.kv_groups - 1) / ((int64_t)num_seqs * p.kv_groups);
+    int sb = (int)((W + per_seq - 1) / per_seq);
+    const int lo = (kMinSplitTokens + bs - 1) / bs;
+    int hi = kMaxSplitTokens / bs > lo ? kMaxSplitTokens / bs : lo;
+    sb = sb < lo ? lo : (sb > hi ? hi : sb);
+    if (sb > W) sb = W;
+    if (sb < 1) sb = 1;
+    p.split_blocks = sb;
+    p.max_splits = (W + sb - 1) / sb;
+  }
   const size_t n = (size_t)num_seqs * HQ * p.max_splits;
-  p.off_m = 0;
+  p.off_n = 0;
+  p.off_m = p.persistent ? round256((size_t)num_seqs * sizeof(int32_t)) : 0;
   p.off_l = p.off_m + round256(n * sizeof(float));
   p.off_o = p.off_l + round256(n * sizeof(float));
   p.bytes = p.off_o + round256(n * (size_t)D * sizeof(float));
   return p;
 }
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// Resident workgroups per compute unit of the persistent kernel at this
+// workgroup size (a property of the kernel binary, cached).
 template <Ty C, int D, int G>
-void launch_split(const DecArgs& a, const Plan& p, hipStream_t st) {
-  // kv-head groups fastest: sibling workgroups read the same pages together
+int persistent_occupancy(int waves_per_wg) {
+  static std::atomic<int> cache[kMaxWaves + 1];
+  const int c = cache[waves_per_wg].load(std::memory_order_relaxed);
+  if (c > 0) return c;
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_persistent_kernel<C, D, G>, 64 * waves_per_wg, 0) != hipSuccess)
+    return 0;
+  cache[waves_per_wg].store(nb, std::memory_order_relaxed);
+  return nb;
+}
+
+template <Ty C, int D, int G>
+bool launch_split(DecArgs& a, const Plan& p, hipStream_t st) {
+  if (p.persistent) {
+    if constexpr (D <= 128) {
+      const int cus = device_cus(), occ = persistent_occupancy<C, D, G>(p.waves_per_wg);
+      if (cus <= 0 || occ <= 0) return false;
+      const int64_t resident = (int64_t)cus * occ;
+      a.slots = (int)(resident / p.kv_groups > 1 ? resident / p.kv_groups : 1);
+      decode_persistent_kernel<C, D, G><<<(unsigned)(a.slots * p.kv_groups), 64 * p.waves_per_wg, 0, st>>>(a);
+      decode_merge_kernel<D><<<(unsigned)(((int64_t)a.num_seqs * a.HQ + 3) / 4), 256, 0, st>>>(a);
+      return true;
+    }
+    return false;
+  }
+  // Vector path: one workgroup per (KV-head group, split, sequence), kv-head
+  // groups fastest so that sibling workgroups read the same pages together.
   dim3 grid(p.kv_groups, p.max_splits, a.num_seqs);
-  // The matrix-core kernel needs 16-position tiles inside a block; at D = 256
-  // its register tiles would spill, so that head size stays on the vector path.
-  if (a.block_size % 16 == 0 && D <= 128)
-    decode_split_mfma_kernel<C, D, G><<<grid, 64 * p.waves_per_wg, 0, st>>>(a);
-  else
-    decode_split_valu_kernel<C, D, G><<<grid, 64 * p.waves_per_wg, 0, st>>>(a);
+  decode_split_valu_kernel<C, D, G><<<grid, 64 * p.waves_per_wg, 0, st>>>(a);
   if (p.max_splits > 1)
     decode_merge_kernel<D><<<(unsigned)(((int64_t)a.num_seqs * a.HQ + 3) / 4), 256, 0, st>>>(a);
+  return true;
 }
 
 template <Ty C, int D>
-bool launch_g(int G, const DecArgs& a, const Plan& p, hipStream_t st) {
+bool launch_g(int G, DecArgs& a, const Plan& p, hipStream_t st) {
   switch (G) {
-    case 1: launch_split<C, D, 1>(a, p, st); return true;
-    case 2: launch_split<C, D, 2>(a, p, st); return true;
-    case 4: launch_split<C, D, 4>(a, p, st); return true;
-    case 8: launch_split<C, D, 8>(a, p, st); return true;
+    case 1: return launch_split<C, D, 1>(a, p, st);
+    case 2: return launch_split<C, D, 2>(a, p, st);
+    case 4: return launch_split<C, D, 4>(a, p, st);
+    case 8: return launch_split<C, D, 8>(a, p, st);
     default: return false;
   }
 }
 
 template <Ty C>
-bool launch_d(int D, int G, const DecArgs& a, const Plan& p, hipStream_t st) {
+bool launch_d(int D, int G, DecArgs& a, const Plan& p, hipStream_t st) {
   switch (D) {
     case 64: return launch_g<C, 64>(G, a, p, st);
     case 128: return launch_g<C, 128>(G, a, p, st);
@@ -913,6 +1049,7 @@ extern "C" pa_status pa_decode_attention(void* out, pa_dtype out_dtype, int64_t 
   a.ws_m = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.off_m);
   a.ws_l = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.off_l);
   a.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.off_o);
+  a.ws_n = p.persistent ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + p.off_n) : nullptr;
   a.out_seq_stride = out_seq_stride;
   a.q_seq_stride = q_seq_stride;
   a.block_stride = block_stride;
@@ -926,6 +1063,7 @@ extern "C" pa_status pa_decode_attention(void* out, pa_dtype out_dtype, int64_t 
   a.max_splits = p.max_splits;
   a.waves_per_wg = p.waves_per_wg;
   a.kv_groups = p.kv_groups;
+  a.slots = 0;
   a.out_f32 = out_dtype == PA_F32;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
 

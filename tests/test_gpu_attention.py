@@ -78,6 +78,12 @@ CASES = [
     ("G2 D128 fp8 bs32", [31, 32, 33, 700], 16, 8, 128, 32, FP8, 24),
     ("G2 D128 bf16 one seq long", [4096], 16, 8, 128, 16, BF16, 256),
     ("G2 D128 bf16 many short", list(range(1, 65)), 16, 8, 128, 16, BF16, 4),
+    ("G2 D128 bf16 bs64", [1, 63, 64, 65, 3000], 16, 8, 128, 64, BF16, 48),
+    ("G4 D64 fp8 bs128", [129, 5, 2100], 8, 2, 64, 128, FP8, 20),
+    # 300 sequences (several per scan thread), every third one empty, lengths
+    # that cut the tile ranges at many different offsets
+    ("G2 D128 bf16 300 seqs with empties", [0 if i % 3 == 0 else 1 + (i * 37) % 700 for i in range(300)],
+     16, 8, 128, 16, BF16, 44),
 ]
 
 
@@ -230,3 +236,33 @@ def test_mixed_decode_fp8_b256_full():
     ref = oracle.decode_attention(h["q"], BF16, h["kc"], h["vc"], FP8, w.block_tables,
                                   w.context_lens, w.softmax_scale, w.k_scale, w.v_scale)
     assert_attention_close(widen_out(out), ref, w.name)
+
+
+def test_long_contexts_several_ranges_per_workgroup():
+    """40 sequences of 16,384 positions (fp8, 8 KV heads): more tiles per KV-head
+    group than 64 per resident workgroup of a 256-CU device, so workgroups take
+    several ranges; 8 sampled sequences are compared with the oracle."""
+    m = pkv()
+    B, HQ, HKV, D, BS, L = 40, 16, 8, 128, 16, 16384
+    W = L // BS
+    NB = B * W + 16
+    say(f"decode_attention long contexts B={B} ctx={L} fp8 pool={NB} blocks")
+    rng = workloads.rng_for(40)
+    perm = rng.permutation(NB).astype(np.int32)
+    ctx = np.full(B, L, dtype=np.int32)
+    ctx[7] = L - 5
+    bt = workloads.deal_block_tables(perm, ctx, BS, W)
+    kc = workloads.device_normal((NB, BS, HKV, D), torch.float8_e4m3fn, "cuda", 4001, std=20.0)
+    vc = workloads.device_normal((NB, BS, HKV, D), torch.float8_e4m3fn, "cuda", 4002, std=25.0)
+    q = workloads.device_normal((B, HQ, D), torch.bfloat16, "cuda", 4003)
+    ks = torch.tensor([0.05], dtype=torch.float32, device="cuda")
+    vs = torch.tensor([0.04], dtype=torch.float32, device="cuda")
+    out = torch.empty((B, HQ, D), dtype=torch.float32, device="cuda")
+    m.decode_attention(out, q, kc, vc, torch.from_numpy(bt).cuda(), torch.from_numpy(ctx).cuda(),
+                       0.088, ks, vs)
+    torch.cuda.synchronize()
+    sub = np.array([0, 7, 13, 20, 26, 31, 38, 39])
+    ref = oracle.decode_attention(to_host(q, BF16)[sub], BF16, to_host(kc, FP8), to_host(vc, FP8), FP8,
+                                  bt[sub], ctx[sub], 0.088, 0.05, 0.04)
+    assert_attention_close(out.cpu().numpy()[sub].astype(np.float64), ref, "long contexts",
+                           out_bf16=False)
