@@ -67,6 +67,9 @@ namespace {
 #ifndef PA_DECODE_MAX_WAVES
 #define PA_DECODE_MAX_WAVES 2
 #endif
+#ifndef PA_DECODE_PRIO
+#define PA_DECODE_PRIO 1
+#endif
 constexpr int kMaxWaves = PA_DECODE_MAX_WAVES;        // KV heads (waves) per workgroup
 constexpr int kTargetWgs = PA_DECODE_TARGET_WGS;      // split workgroups aimed for if every sequence used all W blocks
 constexpr int kMinSplitTokens = PA_DECODE_MIN_SPLIT;  // positions per split, lower bound
@@ -701,6 +704,25 @@ void decode_persistent_kernel(DecArgs a) {
   const char* vc = static_cast<const char*>(a.vc);
   char* my_lds = k_lds + wave * T::KB;
 
+#if PA_DECODE_PRIO
+  // Issue priority from the share of this workgroup's tiles still to do. The
+  // sequencer favours older waves, so without this the workgroups placed last
+  // on a compute unit fall behind and finish alone, with too few loads in
+  // flight to keep HBM busy; a wave that is behind now wins the arbitration.
+  int64_t my_tiles = 0;
+  for (int64_t r = slot; r < R; r += a.slots) my_tiles += min(total, (r + 1) * RT) - r * RT;
+  int64_t tiles_left = my_tiles;
+  auto set_priority = [&]() {
+    const int p = (int)((4 * tiles_left) / (my_tiles + 1));
+    switch (p) {
+      case 0: __builtin_amdgcn_s_setprio(0); break;
+      case 1: __builtin_amdgcn_s_setprio(1); break;
+      case 2: __builtin_amdgcn_s_setprio(2); break;
+      default: __builtin_amdgcn_s_setprio(3); break;
+    }
+  };
+#endif
+
   for (int64_t r = slot; r < R; r += a.slots) {
     // Segment list of range r: [U0, U1) intersected with each sequence.
     const int64_t U0 = r * RT, U1 = min(total, U0 + RT);
@@ -818,6 +840,10 @@ void decode_persistent_kernel(DecArgs a) {
         };
 
         for (int t = t0; t < t1; ++t) {
+#if PA_DECODE_PRIO
+          set_priority();
+          --tiles_left;
+#endif
           T tile;
           const bool ok = fetch(tile, t);
           if (ok) {
