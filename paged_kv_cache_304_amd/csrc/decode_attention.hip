@@ -225,39 +225,91 @@ __device__ __forceinline__ void store_split(const DecArgs& a, int b, int h, int 
   store_dw<N>(a.ws_o + slot * D + d0, w);
 }
 
-// Merge of the splits of (sequence b, q head h) by one wave: lane s holds
-// split s's (max, sum) -- one round of loads -- the wave reduces the global max
-// and the weights, then the splits' outputs are loaded 16 at a time (all in
-// flight together) and summed with the weights; lane i holds dims i + 64k.
+// Merge pass: one wave per (sequence, q head), four waves per workgroup. Lane
+// s holds piece s's (max, sum); the wave reduces the global max and the
+// weights, then sums the pieces' outputs (lane i holds dims i + 64k) with the
+// weights broadcast by readlane. The context length, the piece count, the
+// first 64 (max, sum) pairs and the first kFirst outputs are all loaded
+// together before the count is known (entries past the count are never used),
+// so the common case costs one memory round trip. Sequences that fit one
+// piece were written by the split pass; after the persistent kernel this pass
+// also writes the zeros of empty sequences. (A merge inside the split kernel
+// would need an agent-scope release/acquire per workgroup, i.e. an L2
+// write-back on its XCD for every piece; the kernel boundary gives that
+// ordering for free.)
 template <int D>
-__device__ __forceinline__ void merge_head(const DecArgs& a, int b, int h, int nsplit) {
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecArgs a) {
   constexpr int PER = D / 64;
-  constexpr int BATCH = 16;
+  constexpr int kFirst = 4;   // outputs loaded before the piece count is known
+  constexpr int kBatch = 16;  // outputs per later round of loads
+  const int wid = (int)blockIdx.x * 4 + uniform(threadIdx.x >> 6);
+  if (wid >= a.num_seqs * a.HQ) return;
+  const int b = wid / a.HQ, h = wid - b * a.HQ;
   const int lane = threadIdx.x & 63;
   const int64_t base = ((int64_t)b * a.HQ + h) * a.max_splits;
+
+  const int ctx_raw = a.ctx_lens[b];
+  const int n_raw = a.ws_n ? a.ws_n[b] : 0;
+  const int cap0 = min(64, a.max_splits);
+  const float m0 = lane < cap0 ? a.ws_m[base + lane] : -INFINITY;
+  const float l0 = lane < cap0 ? a.ws_l[base + lane] : 0.0f;
+  const int nb0 = min(kFirst, a.max_splits);
+  float v0[kFirst][PER];
+#pragma unroll
+  for (int u = 0; u < kFirst; ++u) {
+    const float* wo = a.ws_o + (base + min(u, nb0 - 1)) * D;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) v0[u][i] = wo[lane + 64 * i];
+  }
+
+  const int cap = a.W * a.block_size;
+  const int ctx = ctx_raw < 0 ? 0 : (ctx_raw > cap ? cap : ctx_raw);
+  int n;
+  if (a.ws_n) {
+    n = ctx == 0 ? 0 : n_raw;  // count written by the persistent kernel (not for empty sequences)
+  } else {
+    const int nblk = (ctx + a.block_size - 1) / a.block_size;
+    n = (nblk + a.split_blocks - 1) / a.split_blocks;
+    if (n <= 1) return;  // written by the split pass (zeros included)
+  }
+  if (n == 1) return;
+
   float o[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) o[i] = 0.0f;
-  float M = -INFINITY;
-  for (int s = lane; s < nsplit; s += 64) M = fmaxf(M, a.ws_m[base + s]);
+  float M = lane < n ? m0 : -INFINITY;
+  for (int s = 64 + lane; s < n; s += 64) M = fmaxf(M, a.ws_m[base + s]);
   M = wave_max(M);
   if (M != -INFINITY) {
     float den = 0.0f;
-    for (int c = 0; c < nsplit; c += 64) {
+    for (int c = 0; c < n; c += 64) {
       const int sl = c + lane;
-      const float w = sl < nsplit ? __builtin_amdgcn_exp2f(a.ws_m[base + sl] - M) * a.ws_l[base + sl] : 0.0f;
+      float w = 0.0f;
+      if (sl < n) w = __builtin_amdgcn_exp2f((c == 0 ? m0 : a.ws_m[base + sl]) - M) * (c == 0 ? l0 : a.ws_l[base + sl]);
       den += w;
-      const int cnt = min(64, nsplit - c);
-      for (int s0 = 0; s0 < cnt; s0 += BATCH) {
-        float v[BATCH][PER];
+      const int cnt = min(64, n - c);
+      int s_begin = 0;
+      if (c == 0) {
 #pragma unroll
-        for (int u = 0; u < BATCH; ++u) {
+        for (int u = 0; u < kFirst; ++u) {
+          if (u < cnt) {
+            const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), u));
+#pragma unroll
+            for (int i = 0; i < PER; ++i) o[i] = fmaf(ws, v0[u][i], o[i]);
+          }
+        }
+        s_begin = kFirst;
+      }
+      for (int s0 = s_begin; s0 < cnt; s0 += kBatch) {
+        float v[kBatch][PER];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
           const float* wo = a.ws_o + (base + c + min(s0 + u, cnt - 1)) * D;
 #pragma unroll
           for (int i = 0; i < PER; ++i) v[u][i] = wo[lane + 64 * i];
         }
 #pragma unroll
-        for (int u = 0; u < BATCH; ++u) {
+        for (int u = 0; u < kBatch; ++u) {
           if (s0 + u < cnt) {
             const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), s0 + u));
 #pragma unroll
@@ -270,6 +322,7 @@ __device__ __forceinline__ void merge_head(const DecArgs& a, int b, int h, int n
 #pragma unroll
     for (int i = 0; i < PER; ++i) o[i] *= inv;
   }
+  // n == 0 (empty sequence) or no attended position: zeros
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int64_t at = (int64_t)b * a.out_seq_stride + (int64_t)h * D + lane + 64 * i;
@@ -278,42 +331,6 @@ __device__ __forceinline__ void merge_head(const DecArgs& a, int b, int h, int n
     else
       static_cast<uint16_t*>(a.out)[at] = (uint16_t)f32_to_bf16(o[i]);
   }
-}
-
-// Merge pass: one wave per (sequence, q head), four waves per workgroup.
-// Sequences that fit one split (chunk) were written by the split pass; after
-// the persistent kernel the merge pass also writes the zeros of empty
-// sequences. (A merge inside the split kernel would need an agent-scope
-// release/acquire per workgroup, i.e. an L2 write-back on its XCD for every
-// split; the kernel boundary gives that ordering for free.)
-template <int D>
-__global__ __launch_bounds__(256) void decode_merge_kernel(DecArgs a) {
-  const int wid = (int)blockIdx.x * 4 + uniform(threadIdx.x >> 6);
-  if (wid >= a.num_seqs * a.HQ) return;
-  const int b = wid / a.HQ, h = wid - b * a.HQ;
-  const int ctx = clamp_ctx(a, b);
-  if (a.ws_n) {
-    if (ctx == 0) {
-      const float z[D / 64] = {};
-      const int lane = threadIdx.x & 63;
-#pragma unroll
-      for (int i = 0; i < D / 64; ++i) {
-        const int64_t at = (int64_t)b * a.out_seq_stride + (int64_t)h * D + lane + 64 * i;
-        if (a.out_f32)
-          static_cast<float*>(a.out)[at] = z[i];
-        else
-          static_cast<uint16_t*>(a.out)[at] = 0;
-      }
-      return;
-    }
-    const int n = a.ws_n[b];
-    if (n > 1) merge_head<D>(a, b, h, n);
-    return;
-  }
-  const int nblk = (ctx + a.block_size - 1) / a.block_size;
-  const int nsplit = (nblk + a.split_blocks - 1) / a.split_blocks;
-  if (nsplit <= 1) return;
-  merge_head<D>(a, b, h, nsplit);
 }
 
 // ---------------------------------------------------------------------------
