@@ -6,8 +6,8 @@ and the two share no code: the arithmetic lives in ``pagedkv_oracle.c`` (plain
 C, fp64 for attention, exact bit arithmetic for the encodes), and this module
 only marshals numpy arrays into it.
 
-Every function states the passage it follows; the readings R1..R7 are listed in
-the header of ``pagedkv_oracle.c``.
+Every function states the passage it follows; the readings R1..R7 and R10 are
+listed in the header of ``pagedkv_oracle.c``.
 """
 from __future__ import annotations
 
@@ -66,6 +66,9 @@ def _load():
     lib.orc_decode_attention.argtypes = [P, P, I32, I64, P, P, I32, I64, I32, I64, P, I32, P, I32,
                                          I32, I32, I32, F64, P, P]
     lib.orc_decode_attention.restype = None
+    lib.orc_prefill_attention.argtypes = [P, P, I32, I64, P, I32, P, P, I32, I64, I32, I64, P, I32,
+                                          P, I32, I32, I32, F64, P, P]
+    lib.orc_prefill_attention.restype = None
     _lib = lib
     return lib
 
@@ -200,4 +203,37 @@ def decode_attention(q, q_dtype: int, key_cache, value_cache, cache_dtype: int, 
                              _ptr(key_cache), _ptr(value_cache), cache_dtype, NB, BS,
                              block_stride, _ptr(bt), bt.shape[1], _ptr(cl), B, HQ, HKV, D,
                              float(softmax_scale), _ptr(ks), _ptr(vs))
+    return out
+
+
+def prefill_attention(q, q_dtype: int, cu_seqlens_q, key_cache, value_cache, cache_dtype: int,
+                      block_tables, context_lens, softmax_scale: float, k_scale=None,
+                      v_scale=None) -> np.ndarray:
+    """fp64 chunked-prefill paged attention, unrounded (R10).
+
+    ``q`` is a packed ``[T, H_Q, D]`` storage array whose rows cu_seqlens_q[b] ..
+    cu_seqlens_q[b+1]-1 are sequence b's queries (the last positions of its
+    context); caches are ``[NB, BS, H_KV, D]``; ``block_tables`` int32 ``[B, W]``;
+    ``context_lens`` int32 ``[B]``.
+    """
+    lib = _load()
+    T, HQ, D = q.shape
+    NB, BS, HKV, D2 = key_cache.shape
+    assert D == D2 and HQ % HKV == 0
+    assert T == 0 or (q.strides[1] // q.itemsize == D and q.strides[2] == q.itemsize)
+    cu = np.ascontiguousarray(cu_seqlens_q, dtype=np.int32)
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+    B = cl.shape[0]
+    assert cu.shape[0] == B + 1 and bt.shape[0] == B
+    assert cu[0] == 0 and cu[-1] == T and np.all(np.diff(cu) >= 0)
+    block_stride = key_cache.strides[0] // key_cache.itemsize
+    assert value_cache.strides == key_cache.strides
+    out = np.zeros((T, HQ, D), dtype=np.float64)
+    ks, vs = _scalar_f32(k_scale), _scalar_f32(v_scale)
+    tok_stride = q.strides[0] // q.itemsize if T else HQ * D
+    lib.orc_prefill_attention(out.ctypes.data, _ptr(q), q_dtype, tok_stride, _ptr(cu), B,
+                              _ptr(key_cache), _ptr(value_cache), cache_dtype, NB, BS,
+                              block_stride, _ptr(bt), bt.shape[1], _ptr(cl), HQ, HKV, D,
+                              float(softmax_scale), _ptr(ks), _ptr(vs))
     return out

@@ -2,8 +2,8 @@
  * CPU oracle for the paged KV cache hot path.
  *
  * TEST INFRASTRUCTURE ONLY. This file states, as plainly as possible, what the
- * cache write, the MLA-style K concat and single-token paged decode attention
- * compute, so that the GPU kernels can be checked against it. Only the test
+ * cache write, the MLA-style K concat, single-token paged decode attention and
+ * chunked-prefill (variable-length, causal) paged attention compute, so that the GPU kernels can be checked against it. Only the test
  * suite, the smoke check and the benchmark's CPU-baseline leg may load it; the
  * product library never links or calls it, and it shares no source, header,
  * table or helper with the HIP path.
@@ -18,6 +18,12 @@
  *    the decode dataflow (the new token is written before attention) and the
  *    block allocation paragraph (a block is [block_size, H_KV, d_h]; blocks are
  *    physically scattered and found through a table).
+ *  - "nano-vLLM Qwen3 reading notes", section 2.4 (the LM head): queries of a
+ *    prefill batch are packed token-major and delimited by cu_seqlens_q
+ *    (prefix sums of the per-sequence query counts); section 2.6 names the
+ *    variable-length flash path of prefill.
+ *  - "PagedAttention principle" page, autoregressive dataflow section: prefill
+ *    computes causal attention over the prompt while caching its K/V.
  *  - SGLang cache_ops.py (Triton): concat_and_cast_mha_k (per-head k_nope with
  *    one shared k_rope, cast at the store) and reshape_and_cache_flash (source
  *    token strides, optional second-stage SWA slot remap, optional division by
@@ -47,6 +53,13 @@
  *      and v_scale. context_lens is clamped to [0, W*block_size]; ctx == 0
  *      gives an all-zero output; a position whose table entry lies outside
  *      [0, num_blocks) does not take part (memory-safety superset).
+ *  R10 Chunked prefill: sequence b contributes n_b = cu_seqlens_q[b+1] -
+ *      cu_seqlens_q[b] query tokens, the last n_b positions of its context
+ *      (their K/V are already in the cache), so query i sits at position
+ *      p = ctx_b - n_b + i and attends causally to cached positions 0..p
+ *      through block_tables[b] (the same clamping, dequantisation, GQA mapping
+ *      and table-entry rule as R7). A query with p < 0 (n_b > ctx_b) has no
+ *      key and gives zeros. n_b = 1 is exactly R7's decode step.
  *
  * Build: gcc -O2 -std=c11 -fopenmp -ffp-contract=off -fPIC -shared
  * (no fast-math: IEEE single division and round-to-nearest are required).
@@ -339,4 +352,72 @@ void orc_decode_attention(double* out, const void* q, int q_dt, int64_t q_seq_st
       for (int d = 0; d < head_size; ++d) o[d] /= l;
       free(s);
     }
+}
+
+/* Chunked-prefill paged attention (R10): for sequence b with n_b queries and
+ * clamped context length L, query i (packed row t = cu_seqlens_q[b] + i) sits
+ * at position p = L - n_b + i and
+ *   out[t, h, :] = softmax_{j <= p}(scale * q[t,h,:].K^[j,g,:]) . V^[j,g,:]
+ * with g = h / (num_q_heads / num_kv_heads); zeros when p < 0 or when no
+ * position takes part. q is [T, H_Q, D] with token stride q_token_stride;
+ * out is [T, H_Q, D] fp64. Rows of cu_seqlens_q are non-decreasing. */
+void orc_prefill_attention(double* out, const void* q, int q_dt, int64_t q_token_stride,
+                           const int32_t* cu_seqlens_q, int num_seqs,
+                           const void* key_cache, const void* value_cache, int cache_dt,
+                           int64_t num_blocks, int block_size, int64_t block_stride,
+                           const int32_t* block_tables, int W, const int32_t* context_lens,
+                           int num_q_heads, int num_kv_heads, int head_size,
+                           double softmax_scale, const float* k_scale, const float* v_scale) {
+  int group = num_q_heads / num_kv_heads;
+  double ks = k_scale ? (double)*k_scale : 1.0;
+  double vs = v_scale ? (double)*v_scale : 1.0;
+  for (int b = 0; b < num_seqs; ++b) {
+    int64_t t0 = cu_seqlens_q[b], n = (int64_t)cu_seqlens_q[b + 1] - t0;
+    int64_t L = context_lens[b];
+    if (L < 0) L = 0;
+    if (L > (int64_t)W * block_size) L = (int64_t)W * block_size;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int64_t i = 0; i < n; ++i)
+      for (int h = 0; h < num_q_heads; ++h) {
+        int g = h / group;
+        int64_t p = L - n + i; /* this query's position */
+        double* o = out + ((t0 + i) * num_q_heads + h) * (int64_t)head_size;
+        for (int d = 0; d < head_size; ++d) o[d] = 0.0;
+        if (p < 0) continue;
+        const int64_t qb = (t0 + i) * q_token_stride + (int64_t)h * head_size;
+        /* pass 1: scores of positions 0..p and their maximum */
+        double m = -INFINITY;
+        double* s = (double*)malloc(sizeof(double) * (size_t)(p + 1));
+        for (int64_t j = 0; j <= p; ++j) {
+          int64_t row = orc_gather_row(block_tables, b, W, j, block_size, block_stride,
+                                       num_kv_heads, head_size, g, num_blocks);
+          if (row < 0) {
+            s[j] = -INFINITY;
+            continue;
+          }
+          double dot = 0.0;
+          for (int d = 0; d < head_size; ++d)
+            dot += orc_load_f64(q, qb + d, q_dt) * (orc_load_f64(key_cache, row + d, cache_dt) * ks);
+          s[j] = softmax_scale * dot;
+          if (s[j] > m) m = s[j];
+        }
+        if (m == -INFINITY) {
+          free(s);
+          continue;
+        }
+        /* pass 2: weights, their sum, and the weighted sum of V^ */
+        double l = 0.0;
+        for (int64_t j = 0; j <= p; ++j) {
+          if (s[j] == -INFINITY) continue;
+          double w = exp(s[j] - m);
+          l += w;
+          int64_t row = orc_gather_row(block_tables, b, W, j, block_size, block_stride,
+                                       num_kv_heads, head_size, g, num_blocks);
+          for (int d = 0; d < head_size; ++d)
+            o[d] += w * (orc_load_f64(value_cache, row + d, cache_dt) * vs);
+        }
+        for (int d = 0; d < head_size; ++d) o[d] /= l;
+        free(s);
+      }
+  }
 }
