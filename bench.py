@@ -40,7 +40,8 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="decode_b64",
-                   choices=["decode_b64", "prefill_fp8", "decode_fp8_b256", "mla_concat_swa"])
+                   choices=["decode_b64", "prefill_fp8", "decode_fp8_b256", "mla_concat_swa",
+                            "prefill_chunks"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--profile-steps", type=int, default=0,
                    help="only run this many untimed steps (for rocprofv3 runs)")
@@ -338,6 +339,106 @@ def oracle_free_resolve(w):
     return fin
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
+
+
+def prefill_flops(w) -> int:
+    """Algorithmic flops of one chunked-prefill call: every (query, q head) pair
+    does a D-long dot product and a D-long weighted sum (2 flops each per element)
+    for every position it attends to (its own included)."""
+    total = 0
+    cu, ctx = w["cu_seqlens_q"], w["context_lens"]
+    for b in range(w["num_seqs"]):
+        n, L = int(cu[b + 1] - cu[b]), int(ctx[b])
+        pos = L - n + np.arange(n)
+        total += int(np.maximum(pos + 1, 0).sum())
+    return total * w["num_q_heads"] * w["head_size"] * 4
+
+
+def run_prefill_chunks(args, torch, pkv, workloads):
+    w = workloads.prefill_chunks()
+    B, HQ, HKV, D, BS, NB, T = (w["num_seqs"], w["num_q_heads"], w["num_kv_heads"], w["head_size"],
+                                w["block_size"], w["num_blocks"], w["num_tokens"])
+    kc = workloads.device_normal((NB, BS, HKV, D), torch.bfloat16, "cuda", w["seed"])
+    vc = workloads.device_normal((NB, BS, HKV, D), torch.bfloat16, "cuda", w["seed"] + 1)
+    q = workloads.device_normal((T, HQ, D), torch.bfloat16, "cuda", w["seed"] + 2)
+    out = torch.empty_like(q)
+    cu = torch.from_numpy(w["cu_seqlens_q"]).cuda()
+    bt = torch.from_numpy(w["block_tables"]).cuda()
+    cl = torch.from_numpy(w["context_lens"]).cuda()
+
+    def step():
+        pkv.prefill_attention(out, q, cu, kc, vc, bt, cl, w["softmax_scale"])
+
+    flops = prefill_flops(w)
+    kv_bytes = int(2 * int(w["context_lens"].astype(np.int64).sum()) * HKV * D * 2)
+    stream = torch.cuda.current_stream()
+    if args.profile_steps:
+        copy_calibration(torch, pkv)
+        for _ in range(args.profile_steps):
+            step()
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_steps": args.profile_steps, "workload": w["name"]}))
+        return
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    tm = Timer(torch, stream)
+    for _ in range(args.steps):
+        tm.start()
+        step()
+        tm.stop()
+    torch.cuda.synchronize()
+    call_ms = tm.mean_ms()
+    tflops = flops / (call_ms * 1e-3) / 1e12
+    res = {
+        "metric": "chunked-prefill paged attention TFLOP/s (1 MI355X)",
+        "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) K/V/q of Qwen3-0.6B shapes)",
+        "config": {"workload": w["name"], "num_seqs": B, "num_tokens": T, "num_q_heads": HQ,
+                   "num_kv_heads": HKV, "head_size": D, "block_size": BS,
+                   "context_lens": f"{int(w['context_lens'].min())}..{int(w['context_lens'].max())}",
+                   "flops_per_step": flops, "kv_bytes_per_step": kv_bytes},
+        "tokens_per_s": round(T / (ms * 1e-3), 1),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": traffic_from_profiles("prefill_attention", w["name"])},
+        "kv_read_GBps": round(kv_bytes / (call_ms * 1e-3) / 1e9, 1),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        res["cpu_baseline"] = cpu_baseline_prefill(torch, q, kc, vc, w, oracle)
+    print(json.dumps(res))
+
+
+def cpu_baseline_prefill(torch, q, kc, vc, w, oracle):
+    """The oracle on the whole call (every sequence, row and head; about ten
+    seconds on 16 host cores), reported in the metric's unit."""
+    import time
+    qh = q.view(torch.int16).cpu().numpy().view(np.uint16)
+    kh = kc.view(torch.int16).cpu().numpy().view(np.uint16)
+    vh = vc.view(torch.int16).cpu().numpy().view(np.uint16)
+    t = time.perf_counter()
+    oracle.prefill_attention(qh, oracle.BF16, w["cu_seqlens_q"], kh, vh, oracle.BF16,
+                             w["block_tables"], w["context_lens"], w["softmax_scale"])
+    dt = time.perf_counter() - t
+    flops = prefill_flops(w)
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cpu_cores(),
+            "kind": "oracle",
+            "sample": f"the whole call ({w['num_tokens']} query rows x {w['num_q_heads']} heads, "
+                      f"{flops / 1e9:.1f} GFLOP) in {dt:.1f} s"}
+
+
 def run_decode_fp8(args, torch, pkv, workloads):
     w = workloads.mixed_decode_fp8()
     return run_decode(args, torch, pkv, workloads, w,
@@ -400,6 +501,8 @@ def main():
         run_decode_fp8(args, torch, pkv, workloads)
     elif args.workload == "prefill_fp8":
         run_prefill_fp8(args, torch, pkv, workloads)
+    elif args.workload == "prefill_chunks":
+        run_prefill_chunks(args, torch, pkv, workloads)
     else:
         run_mla(args, torch, pkv, workloads)
 

@@ -8,6 +8,9 @@
  *   pa_concat_and_cast_mla_k  per-head k_nope ++ shared k_rope -> K, with a cast
  *   pa_decode_attention       one query token per sequence against its paged
  *                             K/V, read back through a block table (GQA)
+ * and the prefill side of the same cache:
+ *   pa_prefill_attention      packed chunks of query tokens per sequence,
+ *                             causal, against the same paged K/V
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller. The library
@@ -188,8 +191,9 @@ size_t pa_decode_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads,
  *            pa_decode_attention_workspace_size(...) bytes, 256-byte aligned;
  *            it receives the per-split partial results, so its contents on
  *            entry do not matter. Concurrent calls must not share it.
- * Supported: head_size in {64, 128, 256}; num_q_heads % num_kv_heads == 0;
- *   num_q_heads / num_kv_heads <= 16.
+ * Supported: head_size in {64, 128, 256}; num_q_heads % num_kv_heads == 0 with
+ *   num_q_heads / num_kv_heads in {1, 2, 4, 8}; block_size a multiple of
+ *   64 / (head_size / 8).
  * Errors: PA_EINVAL, PA_EDTYPE, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_EHIP.
  * num_seqs == 0 is a valid no-op.
  */
@@ -203,6 +207,55 @@ pa_status pa_decode_attention(void* out, pa_dtype out_dtype, int64_t out_seq_str
                               int32_t head_size, float softmax_scale, const float* k_scale,
                               const float* v_scale, void* workspace, size_t workspace_bytes,
                               void* stream);
+
+/*
+ * pa_prefill_attention -- chunked-prefill (variable-length, causal) paged
+ * attention with GQA: many query tokens per sequence against the sequence's
+ * paged K/V, the other half of an engine's attention next to decode.
+ *
+ * Defined by: "nano-vLLM Qwen3 reading notes", section 2.4 (prefill queries
+ * are packed token-major and delimited by cu_seqlens_q, the prefix sums of
+ * the per-sequence query counts) and section 2.6 (the variable-length flash
+ * path of prefill); "PagedAttention principle" page, autoregressive dataflow
+ * section (prefill attends causally over the prompt while caching its K/V).
+ *
+ * Sequence b owns packed query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1,
+ * n_b of them: the LAST n_b positions of its context (their K/V are already
+ * in the cache, written by pa_reshape_and_cache). With
+ * L = clamp(context_lens[b], 0, max_blocks_per_seq*block_size), query i sits
+ * at position p = L - n_b + i and, for q head h (g = h / G),
+ *   out[row, h] = sum_{j<=p} softmax_j(softmax_scale * q[row,h,:].K^[j,g,:]) V^[j,g,:]
+ * with K^ = K * k_scale, V^ = V * v_scale, positions gathered through
+ * block_tables[b] exactly as in pa_decode_attention (an entry outside
+ * [0, num_blocks) removes its positions). A query with p < 0 (n_b > L) has no
+ * key and gets zeros. n_b == 1 is the decode step of pa_decode_attention.
+ *
+ * Arguments
+ *   out      [num_tokens, num_q_heads, head_size], token stride
+ *            out_token_stride; out_dtype PA_BF16 or PA_F32.
+ *   q        [num_tokens, num_q_heads, head_size], token stride q_token_stride;
+ *            q_dtype PA_BF16.
+ *   cu_seqlens_q  int32 [num_seqs + 1], device: 0 = cu[0] <= cu[1] <= ... <=
+ *            cu[num_seqs] = num_tokens (values are clamped into [0, num_tokens]
+ *            for memory safety; rows no sequence owns are not written).
+ *   key_cache, value_cache, block_tables, context_lens, k_scale, v_scale: as
+ *            for pa_decode_attention; cache_dtype PA_BF16.
+ * No workspace: each query row's softmax is completed inside one workgroup.
+ * Supported: head_size in {64, 128}; num_q_heads / num_kv_heads in
+ *   {1, 2, 4, 8}; block_size a multiple of 16.
+ * Errors: PA_EINVAL, PA_EDTYPE, PA_EUNSUPPORTED, PA_EHIP. num_seqs == 0 or
+ * num_tokens == 0 is a valid no-op.
+ */
+pa_status pa_prefill_attention(void* out, pa_dtype out_dtype, int64_t out_token_stride,
+                               const void* q, pa_dtype q_dtype, int64_t q_token_stride,
+                               int64_t num_tokens, const int32_t* cu_seqlens_q,
+                               const void* key_cache, const void* value_cache,
+                               pa_dtype cache_dtype, int64_t num_blocks, int32_t block_size,
+                               int64_t block_stride, const int32_t* block_tables,
+                               int32_t max_blocks_per_seq, const int32_t* context_lens,
+                               int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_size, float softmax_scale, const float* k_scale,
+                               const float* v_scale, void* stream);
 
 /*
  * pa_hbm_copy -- streaming device-to-device copy of `bytes` bytes

@@ -13,5 +13,6 @@ from .ops import (  # noqa: F401
     decode_attention,
     decode_attention_workspace_size,
     hbm_copy,
+    prefill_attention,
     reshape_and_cache,
 )

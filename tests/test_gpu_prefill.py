@@ -1,0 +1,185 @@
+"""GPU parity of chunked-prefill paged attention against the fp64 oracle.
+
+Tolerance (derived from the kernel's arithmetic; the decode bound is stated
+for one query token): the decode bound 2e-3 + 2e-3*|o| for fp32 accumulation
+and exponentials, plus the bf16 rounding of the probabilities fed to the
+matrix-core P.V product: each p_j carries a relative error of at most 2^-9,
+so |delta o| <= 2^-9 * sum_j p_j |v_j| / l, a quantity the oracle gives
+exactly when run on |V|. bf16 outputs additionally get half a bf16 ulp.
+
+Cases: ragged chunks on cached prefixes and whole prompts over every group
+size, both head sizes and block sizes 16..64 (48 included), many sequences
+with empties, chunks longer than their context, bad table entries and
+NaN-filled unwritten slots, bit-identical output under block relabelling, and
+a full-size prefill batch."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity_util import bf16_half_ulp, say, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+BF16, F32 = oracle.BF16, oracle.F32
+NAN_BF16 = 0x7FC0
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def pkv():
+    import paged_kv_cache_304_amd as m
+    return m
+
+
+def make_case(seed, ctx, nq, hq, hkv, d, bs, spare=4, width=None):
+    """Caches holding each sequence's first ctx_b positions (NaN in every slot no
+    sequence owns), packed queries, cu_seqlens."""
+    rng = np.random.default_rng(seed)
+    ctx = np.asarray(ctx, dtype=np.int32)
+    nq = np.asarray(nq, dtype=np.int32)
+    nblk = [-(-int(c) // bs) for c in ctx]
+    nb = sum(nblk) + spare
+    W = width or max(max(nblk), 1)
+    perm = rng.permutation(nb).astype(np.int32)
+    bt = workloads.deal_block_tables(perm, ctx, bs, W)
+    kc = workloads.normal_bf16_bits(rng, (nb, bs, hkv, d))
+    vc = workloads.normal_bf16_bits(rng, (nb, bs, hkv, d))
+    owned = np.zeros((nb, bs), dtype=bool)
+    for b, c in enumerate(ctx):
+        pos = np.arange(int(c))
+        owned[bt[b, pos // bs], pos % bs] = True
+    kc[~owned] = NAN_BF16
+    vc[~owned] = NAN_BF16
+    cu = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    q = workloads.normal_bf16_bits(rng, (int(cu[-1]), hq, d))
+    return q, kc, vc, bt, ctx, cu
+
+
+def gpu_prefill(q, kc, vc, bt, ctx, cu, scale, out_dt=BF16):
+    m = pkv()
+    dq = to_dev(q, BF16)
+    out = torch.full(dq.shape, float("nan"), dtype=torch.float32 if out_dt == F32 else torch.bfloat16,
+                     device="cuda")
+    m.prefill_attention(out, dq, torch.from_numpy(cu).cuda(), to_dev(kc, BF16), to_dev(vc, BF16),
+                        torch.from_numpy(bt).cuda(), torch.from_numpy(ctx).cuda(), scale)
+    torch.cuda.synchronize()
+    return out
+
+
+def abs_values(cache_bits):
+    return cache_bits & np.uint16(0x7FFF)   # |x| of bf16 (NaN stays NaN)
+
+
+def check_close(got, ref, ref_abs, what, out_bf16):
+    assert got.shape == ref.shape
+    assert np.all(np.isfinite(got)), f"{what}: non-finite GPU output"
+    tol = 2e-3 + 2e-3 * np.abs(ref) + 2.0 ** -9 * ref_abs * 1.001
+    if out_bf16:
+        tol = tol + bf16_half_ulp(ref)
+    err = np.abs(got - ref)
+    bad = err > tol
+    if bad.any():
+        i = np.unravel_index(np.argmax(err - tol), err.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())} of {err.size} outside the bound; worst at {i}: "
+                             f"gpu {got[i]!r} oracle {ref[i]!r} tol {tol[i]!r}")
+
+
+def run_and_check(name, q, kc, vc, bt, ctx, cu, scale):
+    ref = oracle.prefill_attention(q, BF16, cu, kc, vc, BF16, bt, ctx, scale)
+    ref_abs = oracle.prefill_attention(q, BF16, cu, kc, abs_values(vc), BF16, bt, ctx, scale)
+    for out_dt in (F32, BF16):
+        got = gpu_prefill(q, kc, vc, bt, ctx, cu, scale, out_dt).float().cpu().numpy().astype(np.float64)
+        check_close(got, ref, ref_abs, f"{name} out={'f32' if out_dt == F32 else 'bf16'}",
+                    out_dt == BF16)
+
+
+CASES = [
+    # name, ctx, nq, hq, hkv, d, bs, width
+    ("G2 D128 whole prompts", [1, 17, 64, 65, 200], [1, 17, 64, 65, 200], 16, 8, 128, 16, None),
+    ("G2 D128 chunks on prefixes", [100, 700, 64, 1000, 129], [37, 128, 64, 1, 129], 16, 8, 128, 16, None),
+    ("G1 D128", [300, 90], [130, 90], 8, 8, 128, 16, None),
+    ("G4 D128", [513, 33], [200, 33], 16, 4, 128, 16, None),
+    ("G8 D128", [260, 7], [70, 7], 16, 2, 128, 16, None),
+    ("G2 D64", [400, 150], [129, 64], 8, 4, 64, 16, None),
+    ("G8 D64", [333, 20], [40, 20], 8, 1, 64, 16, None),
+    ("G2 D128 bs32", [310, 96], [100, 96], 16, 8, 128, 32, None),
+    ("G2 D128 bs48", [250, 49], [80, 49], 16, 8, 128, 48, None),
+    ("G4 D64 bs64", [700, 65], [300, 65], 8, 2, 64, 64, None),
+    ("G2 D128 chunk longer than context, empty sequences",
+     [5, 0, 40, 0, 3], [20, 0, 40, 3, 1], 16, 8, 128, 16, 4),
+    ("G2 D128 300 sequences",
+     [1 + (i * 53) % 300 for i in range(300)], [(0 if i % 7 == 0 else 1 + (i * 13) % 40) for i in range(300)],
+     16, 8, 128, 16, None),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_prefill_matches_oracle(case):
+    name, ctx, nq, hq, hkv, d, bs, width = case
+    nq = [min(n, c) if "longer" not in name else n for n, c in zip(nq, ctx)]
+    say(f"prefill_attention {name} B={len(ctx)} T={sum(nq)} H_Q={hq} H_KV={hkv} D={d} bs={bs}")
+    q, kc, vc, bt, ctx, cu = make_case(zlib.crc32(name.encode()), ctx, nq, hq, hkv, d, bs, width=width)
+    run_and_check(name, q, kc, vc, bt, ctx, cu, float(np.float32(1.0 / np.sqrt(d))))
+
+
+def test_bad_table_entries_and_clamped_lengths():
+    """An entry outside the pool drops its positions; a length past the table is clamped."""
+    say("prefill_attention bad table entries")
+    q, kc, vc, bt, ctx, cu = make_case(77, [90, 64, 48], [50, 64, 40], 16, 8, 128, 16, width=6)
+    bt = bt.copy()
+    bt[0, 2] = kc.shape[0] + 3
+    bt[1, 0] = -7
+    ctx = np.array([90, 64, 9999], dtype=np.int32)   # sequence 2: clamped to 6*16 = 96, past its 3 full blocks
+    bt[2, 3:] = kc.shape[0] + 100                    # the clamped range reads past its blocks: dropped
+    run_and_check("bad entries", q, kc, vc, bt, ctx, cu, 0.09)
+
+
+def test_block_relabelling_is_bit_identical():
+    say("prefill_attention block relabelling")
+    q, kc, vc, bt, ctx, cu = make_case(21, [300, 1234, 64], [100, 300, 64], 16, 8, 128, 16, spare=20)
+    a = gpu_prefill(q, kc, vc, bt, ctx, cu, 0.088)
+    perm = np.random.default_rng(1).permutation(kc.shape[0])
+    kc2, vc2 = np.empty_like(kc), np.empty_like(vc)
+    kc2[perm], vc2[perm] = kc, vc
+    bt2 = np.where(bt >= 0, perm[np.maximum(bt, 0)], -1).astype(np.int32)
+    b = gpu_prefill(q, kc2, vc2, bt2, ctx, cu, 0.088)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_full_size_prefill_batch():
+    """The prefill measurement workload (16 sequences, 512-token chunks on
+    prefixes U{0..3584}, Qwen3-0.6B heads) in the launch the benchmark times;
+    three sequences' outputs (every row and head) against the oracle."""
+    m = pkv()
+    w = workloads.prefill_chunks()
+    say(f"prefill_attention full size {w['name']} T={w['num_tokens']}")
+    B, HQ, HKV, D, BS, NB = (w["num_seqs"], w["num_q_heads"], w["num_kv_heads"], w["head_size"],
+                             w["block_size"], w["num_blocks"])
+    kc = workloads.device_normal((NB, BS, HKV, D), torch.bfloat16, "cuda", w["seed"])
+    vc = workloads.device_normal((NB, BS, HKV, D), torch.bfloat16, "cuda", w["seed"] + 1)
+    q = workloads.device_normal((w["num_tokens"], HQ, D), torch.bfloat16, "cuda", w["seed"] + 2)
+    out = torch.empty_like(q)
+    m.prefill_attention(out, q, torch.from_numpy(w["cu_seqlens_q"]).cuda(), kc, vc,
+                        torch.from_numpy(w["block_tables"]).cuda(),
+                        torch.from_numpy(w["context_lens"]).cuda(), w["softmax_scale"])
+    torch.cuda.synchronize()
+    qh, kh, vh = to_host(q, BF16), to_host(kc, BF16), to_host(vc, BF16)
+    cu = w["cu_seqlens_q"]
+    got_all = out.float().cpu().numpy().astype(np.float64)
+    for b in (0, 7, 15):
+        rows = slice(int(cu[b]), int(cu[b + 1]))
+        sub = (qh[rows], np.array([0, rows.stop - rows.start], dtype=np.int32), w["block_tables"][b:b + 1],
+               w["context_lens"][b:b + 1])
+        ref = oracle.prefill_attention(sub[0], BF16, sub[1], kh, vh, BF16, sub[2], sub[3],
+                                       w["softmax_scale"])
+        ref_abs = oracle.prefill_attention(sub[0], BF16, sub[1], kh, abs_values(vh), BF16, sub[2],
+                                           sub[3], w["softmax_scale"])
+        check_close(got_all[rows], ref, ref_abs, f"{w['name']} sequence {b}", True)

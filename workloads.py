@@ -229,3 +229,27 @@ def mla_concat_swa(num_tokens: int = 16384, num_heads: int = 128, nope_dim: int 
                 num_heads=num_heads, nope_dim=nope_dim, rope_dim=rope_dim,
                 block_size=block_size, num_blocks=-(-num_tokens // block_size),
                 seed=torch_seed(rng))
+
+
+def prefill_chunks(num_seqs: int = 16, chunk: int = 512, prefix_hi: int = 3584,
+                   workload_id: int = 6, num_q_heads: int = 16, num_kv_heads: int = 8,
+                   head_size: int = 128, block_size: int = 16, num_blocks: int = 4096) -> dict:
+    """Chunked prefill, Qwen3-0.6B heads: 16 sequences each appending a 512-token
+    chunk to a cached prefix of U{0..3584} tokens (context = prefix + chunk); the
+    chunk's K/V are already in the bf16 pool (4,096 blocks); packed queries with
+    cu_seqlens_q. Caches and q are drawn on the device from the returned seed."""
+    rng = rng_for(workload_id)
+    prefix = rng.integers(0, prefix_hi + 1, size=num_seqs)
+    ctx = (prefix + chunk).astype(np.int32)
+    nblk = -(-ctx // block_size)
+    width = int(-(-(prefix_hi + chunk) // block_size))
+    perm = rng.permutation(num_blocks).astype(np.int32)
+    assert int(nblk.sum()) <= num_blocks
+    bt = deal_block_tables(perm, ctx, block_size, width)
+    cu = np.arange(num_seqs + 1, dtype=np.int32) * chunk
+    return dict(name=f"prefill_chunks_{num_seqs}x{chunk}_bf16", num_seqs=num_seqs,
+                num_tokens=num_seqs * chunk, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
+                head_size=head_size, block_size=block_size, num_blocks=num_blocks,
+                context_lens=ctx, block_tables=bt, cu_seqlens_q=cu,
+                softmax_scale=float(np.float32(1.0 / np.sqrt(head_size))),
+                seed=torch_seed(rng))
