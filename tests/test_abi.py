@@ -151,6 +151,43 @@ def test_workspace_size_is_pure_and_validates(L):
     assert f(64, 12, 8, 128, 256, 16) == 0
 
 
+def prefill(L, **over):
+    a = dict(out=1 << 20, odt=L.PA_BF16, os=2048, q=1 << 21, qdt=L.PA_BF16, qs=2048, T=100,
+             cu=1 << 27, kc=1 << 22, vc=1 << 23, cdt=L.PA_BF16, NB=16, BS=16, bstride=16 * 8 * 128,
+             bt=1 << 24, W=4, cl=1 << 25, B=2, HQ=16, HKV=8, D=128, scale=0.088, ks=None, vs=None)
+    a.update(over)
+    return L.lib.pa_prefill_attention(a["out"], a["odt"], a["os"], a["q"], a["qdt"], a["qs"], a["T"],
+                                      a["cu"], a["kc"], a["vc"], a["cdt"], a["NB"], a["BS"],
+                                      a["bstride"], a["bt"], a["W"], a["cl"], a["B"], a["HQ"],
+                                      a["HKV"], a["D"], a["scale"], a["ks"], a["vs"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(HQ=12), "PA_EINVAL"),              # 12 % 8
+    (dict(HQ=24, HKV=8), "PA_EUNSUPPORTED"),  # G = 3
+    (dict(D=256), "PA_EUNSUPPORTED"),
+    (dict(BS=8), "PA_EUNSUPPORTED"),          # not a multiple of 16
+    (dict(T=-1), "PA_EINVAL"),
+    (dict(B=-1), "PA_EINVAL"),
+    (dict(odt=3), "PA_EDTYPE"),
+    (dict(qdt=2), "PA_EDTYPE"),
+    (dict(cdt=3), "PA_EDTYPE"),              # fp8 prefill is not built
+    (dict(scale=float("inf")), "PA_EINVAL"),
+    (dict(qs=100), "PA_EINVAL"),
+    (dict(bstride=10), "PA_EINVAL"),
+    (dict(cu=None), "PA_EINVAL"),
+    (dict(out=(1 << 20) + 2), "PA_EINVAL"),  # misaligned out
+])
+def test_prefill_attention_rejects(L, over, code):
+    assert prefill(L, **over) == getattr(L, code)
+    assert L.last_error()
+
+
+def test_prefill_attention_empty_is_noop(L):
+    assert prefill(L, T=0, q=None, out=None) == L.PA_OK
+    assert prefill(L, B=0, cu=None) == L.PA_OK
+
+
 def test_hbm_copy_rejects(L):
     assert L.lib.pa_hbm_copy(None, 1 << 20, 64, None) == L.PA_EINVAL
     assert L.lib.pa_hbm_copy(1 << 20, (1 << 20) + 16, 64, None) == L.PA_EINVAL  # overlap
