@@ -41,7 +41,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="decode_b64",
                    choices=["decode_b64", "prefill_fp8", "decode_fp8_b256", "mla_concat_swa",
-                            "prefill_chunks"])
+                            "mla_fused", "prefill_chunks"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--profile-steps", type=int, default=0,
                    help="only run this many untimed steps (for rocprofv3 runs)")
@@ -332,6 +332,31 @@ def run_mla(args, torch, pkv, workloads):
                    "mla_concat_16384x128_then_swa_write", "bf16", T, "tokens_per_s")
 
 
+def run_mla_fused(args, torch, pkv, workloads):
+    """The same MLA K assembly and SWA write as run_mla, fused into one kernel that
+    writes the bf16 cache rows straight from k_nope / k_rope."""
+    w = workloads.mla_concat_swa()
+    T, H, nope, rope, BS, NB = (w["num_tokens"], w["num_heads"], w["nope_dim"], w["rope_dim"],
+                                w["block_size"], w["num_blocks"])
+    kn = workloads.device_normal((T, H, nope), torch.bfloat16, "cuda", w["seed"])
+    kr = workloads.device_normal((T, 1, rope), torch.bfloat16, "cuda", w["seed"] + 1)
+    cache = torch.empty((NB, BS, H, nope + rope), dtype=torch.bfloat16, device="cuda")
+    slots = torch.from_numpy(w["slot_mapping"]).cuda()
+    swa = torch.from_numpy(w["swa_slot_mapping"]).cuda()
+
+    def step():
+        pkv.concat_and_cache_mla_k(kn, kr, cache, slots, swa)
+
+    final = oracle_free_resolve(w)
+    kept = int((final >= 0).sum())
+    kept1 = int((w["slot_mapping"] >= 0).sum())
+    # kept tokens read their k_nope and k_rope rows; every token reads its slot,
+    # tokens past stage one read their SWA entry; kept rows are written once
+    nbytes = 8 * T + 8 * kept1 + kept * (H * nope * 2 + rope * 2) + kept * H * (nope + rope) * 2
+    return generic(args, torch, pkv, step, nbytes, "concat_and_cast",
+                   "mla_fused_concat_and_cache_16384x128_swa", "bf16", T, "tokens_per_s")
+
+
 def oracle_free_resolve(w):
     """Final slot per token for the MLA workload's two-stage table (host bookkeeping)."""
     s = w["slot_mapping"]
@@ -503,6 +528,8 @@ def main():
         run_prefill_fp8(args, torch, pkv, workloads)
     elif args.workload == "prefill_chunks":
         run_prefill_chunks(args, torch, pkv, workloads)
+    elif args.workload == "mla_fused":
+        run_mla_fused(args, torch, pkv, workloads)
     else:
         run_mla(args, torch, pkv, workloads)
 

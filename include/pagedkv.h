@@ -6,6 +6,7 @@
  *   pa_reshape_and_cache      token-major K/V -> paged cache, through a slot
  *                             mapping (optional SWA remap, optional fp8 scale)
  *   pa_concat_and_cast_mla_k  per-head k_nope ++ shared k_rope -> K, with a cast
+ *   pa_concat_and_cache_mla_k the same K assembled straight into the paged cache
  *   pa_decode_attention       one query token per sequence against its paged
  *                             K/V, read back through a block table (GQA)
  * and the prefill side of the same cache:
@@ -145,6 +146,41 @@ pa_status pa_concat_and_cast_mla_k(void* k, pa_dtype k_dtype, int64_t k_stride0,
                                    const void* k_rope, pa_dtype rope_dtype, int64_t rope_stride0,
                                    int64_t num_tokens, int32_t num_heads, int32_t nope_dim,
                                    int32_t rope_dim, void* stream);
+
+/*
+ * pa_concat_and_cache_mla_k -- the MLA K assembly written straight into the
+ * paged cache: per-head k_nope ++ shared k_rope, cast, scattered through the
+ * slot mapping, with no K intermediate in device memory.
+ *
+ * Defined by: the composition of concat_and_cast_mha_k and
+ * reshape_and_cache_flash (K only) of SGLang's cache_ops.py, the two ops the
+ * hot path runs back to back for an MLA-style K. The result is bit-identical
+ * to pa_concat_and_cast_mla_k into an fp32 K followed by
+ * pa_reshape_and_cache(K, NULL, key_cache, NULL, ..., slot_mapping,
+ * swa_slot_mapping, swa_len, k_scale, NULL): each element is widened exactly
+ * to fp32, divided by *k_scale when k_scale is given, and rounded once to the
+ * cache type; slot resolution and skips are those of pa_reshape_and_cache.
+ *
+ * Arguments
+ *   k_nope   [num_tokens, num_heads, nope_dim], strides (nope_stride0,
+ *            nope_stride1, 1); src_dtype PA_BF16 or PA_F32.
+ *   k_rope   [num_tokens, 1, rope_dim], token stride rope_stride0; src_dtype.
+ *   key_cache [num_blocks, block_size, num_heads, nope_dim + rope_dim], block
+ *            stride block_stride, inner part contiguous; cache_dtype PA_BF16,
+ *            PA_F32 or PA_FP8_E4M3FN.
+ *   slot_mapping, swa_slot_mapping, swa_len, k_scale: as pa_reshape_and_cache.
+ * Supported: nope_dim and rope_dim multiples of 8, (nope_dim + rope_dim) <= 2048;
+ *   16-byte aligned source rows, cache blocks aligned to 16 bytes (8 for fp8).
+ * Errors: PA_EINVAL, PA_EDTYPE, PA_EUNSUPPORTED, PA_EHIP. num_tokens == 0 or
+ * num_blocks == 0 is a valid no-op.
+ */
+pa_status pa_concat_and_cache_mla_k(const void* k_nope, pa_dtype src_dtype, int64_t nope_stride0,
+                                    int64_t nope_stride1, const void* k_rope, int64_t rope_stride0,
+                                    int64_t num_tokens, int32_t num_heads, int32_t nope_dim,
+                                    int32_t rope_dim, void* key_cache, pa_dtype cache_dtype,
+                                    int64_t num_blocks, int32_t block_size, int64_t block_stride,
+                                    const int64_t* slot_mapping, const int64_t* swa_slot_mapping,
+                                    int64_t swa_len, const float* k_scale, void* stream);
 
 /*
  * pa_decode_attention_workspace_size -- bytes of device workspace that

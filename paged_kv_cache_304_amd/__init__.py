@@ -9,6 +9,7 @@ fallback implementation.
 """
 from ._lib import LIB_PATH, PagedKVError, abi_version, lib  # noqa: F401
 from .ops import (  # noqa: F401
+    concat_and_cache_mla_k,
     concat_and_cast_mla_k,
     decode_attention,
     decode_attention_workspace_size,

@@ -17,6 +17,7 @@ STATUS_NAMES = {PA_OK: "PA_OK", PA_EINVAL: "PA_EINVAL", PA_EDTYPE: "PA_EDTYPE",
 
 # Every symbol the header declares.
 EXPORTS = ("pa_last_error", "pa_abi_version", "pa_reshape_and_cache", "pa_concat_and_cast_mla_k",
+           "pa_concat_and_cache_mla_k",
            "pa_decode_attention_workspace_size", "pa_decode_attention", "pa_prefill_attention",
            "pa_hbm_copy")
 
@@ -45,6 +46,9 @@ def _load() -> ctypes.CDLL:
     L.pa_concat_and_cast_mla_k.argtypes = [P, I32, I64, I64, P, I32, I64, I64, P, I32, I64, I64,
                                            I32, I32, I32, P]
     L.pa_concat_and_cast_mla_k.restype = I32
+    L.pa_concat_and_cache_mla_k.argtypes = [P, I32, I64, I64, P, I64, I64, I32, I32, I32, P, I32, I64,
+                                            I32, I64, P, P, I64, P, P]
+    L.pa_concat_and_cache_mla_k.restype = I32
     L.pa_decode_attention_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32]
     L.pa_decode_attention_workspace_size.restype = SZ
     L.pa_decode_attention.argtypes = [P, I32, I64, P, I32, I64, P, P, I32, I64, I32, I64, P, I32, P,

@@ -197,4 +197,24 @@ __device__ __forceinline__ float group_sum(float x) {
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// ------------------------------------------------------- slot resolution
+
+// Final cache slot of token t, or -1 when the token is skipped: a negative
+// first-stage slot (tested before the optional second-stage table is read), a
+// first-stage slot past that table, a negative second-stage slot, or a slot
+// outside the pool's num_blocks * block_size slots. With a wave-uniform t every
+// load is a scalar load.
+template <bool kSwa>
+__device__ __forceinline__ int64_t resolve_token_slot(const int64_t* slot_mapping, const int64_t* swa,
+                                                      int64_t swa_len, int64_t pool_slots, int64_t t) {
+  int64_t s = slot_mapping[t];
+  if (s < 0) return -1;
+  if constexpr (kSwa) {
+    if (s >= swa_len) return -1;
+    s = swa[s];
+    if (s < 0) return -1;
+  }
+  return s < pool_slots ? s : -1;
+}
+
 }  // namespace pa

@@ -45,18 +45,10 @@ struct RacArgs {
   int32_t row_elems;     // num_heads * head_size
 };
 
-// Final slot of token t, or -1 when the token is skipped. t is wave-uniform,
-// so every load here is a scalar load.
+// Final slot of token t, or -1 when the token is skipped (t is wave-uniform).
 template <bool kSwa>
 __device__ __forceinline__ int64_t resolve_slot(const RacArgs& a, int64_t t) {
-  int64_t s = a.slot_mapping[t];
-  if (s < 0) return -1;
-  if constexpr (kSwa) {
-    if (s >= a.swa_len) return -1;
-    s = a.swa[s];
-    if (s < 0) return -1;
-  }
-  return s < a.pool_slots ? s : -1;
+  return resolve_token_slot<kSwa>(a.slot_mapping, a.swa, a.swa_len, a.pool_slots, t);
 }
 
 __device__ __forceinline__ int64_t row_offset(const RacArgs& a, int64_t s) {

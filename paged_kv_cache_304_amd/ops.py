@@ -102,6 +102,39 @@ def concat_and_cast_mla_k(k: torch.Tensor, k_nope: torch.Tensor, k_rope: torch.T
         _code(k_rope, "k_rope"), k_rope.stride(0), T, H, nope, rope, _stream(stream)))
 
 
+def concat_and_cache_mla_k(k_nope: torch.Tensor, k_rope: torch.Tensor, key_cache: torch.Tensor,
+                           slot_mapping: torch.Tensor,
+                           swa_slot_mapping: Optional[torch.Tensor] = None,
+                           k_scale: Optional[torch.Tensor] = None, stream=None) -> None:
+    """k_nope [T, H, nope] ++ k_rope [T, 1, rope], cast and written straight into
+    ``key_cache`` [NB, BS, H, nope + rope] through the slot mapping (optional SWA
+    table and k_scale as in reshape_and_cache)."""
+    _on_gpu(k_nope, k_rope, key_cache, slot_mapping, swa_slot_mapping, k_scale)
+    T, H, nope = k_nope.shape
+    rope = k_rope.shape[2]
+    NB, BS, H2, kd = key_cache.shape
+    if k_rope.shape[:2] != (T, 1) or H2 != H or kd != nope + rope:
+        raise ValueError("k_nope [T, H, nope], k_rope [T, 1, rope], key_cache [NB, BS, H, nope + rope]")
+    if k_nope.dtype != k_rope.dtype:
+        raise ValueError("k_nope and k_rope dtypes differ")
+    if k_nope.stride(2) != 1 or (rope > 0 and k_rope.stride(2) != 1):
+        raise ValueError("source rows must be contiguous")
+    if key_cache.stride(3) != 1 or key_cache.stride(2) != kd or key_cache.stride(1) != H * kd:
+        raise ValueError("cache inner [BS, H, nope + rope] must be contiguous")
+    if slot_mapping.dtype != torch.int64 or not slot_mapping.is_contiguous() or slot_mapping.numel() != T:
+        raise ValueError("slot_mapping must be contiguous int64 [T]")
+    swa_len = 0
+    if swa_slot_mapping is not None:
+        if swa_slot_mapping.dtype != torch.int64 or not swa_slot_mapping.is_contiguous():
+            raise ValueError("swa_slot_mapping must be contiguous int64")
+        swa_len = swa_slot_mapping.numel()
+    check(lib.pa_concat_and_cache_mla_k(
+        k_nope.data_ptr(), _code(k_nope, "k_nope"), k_nope.stride(0), k_nope.stride(1),
+        k_rope.data_ptr(), k_rope.stride(0), T, H, nope, rope, key_cache.data_ptr(),
+        _code(key_cache, "key_cache"), NB, BS, key_cache.stride(0), slot_mapping.data_ptr(),
+        _ptr(swa_slot_mapping), swa_len, _ptr(k_scale), _stream(stream)))
+
+
 def decode_attention_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int,
                                     head_size: int, max_blocks_per_seq: int,
                                     block_size: int) -> int:

@@ -264,3 +264,68 @@ def test_mla_concat_then_swa_write_full_size():
     oracle.reshape_and_cache(src, None, F32, oc, None, BF16, np.arange(64, dtype=np.int64))
     got = to_host(rows[torch.from_numpy(final[pick]).cuda()], BF16)
     assert np.array_equal(got.reshape(64, -1), oc.reshape(64, -1))
+
+
+FUSED_CASES = [
+    # name, src, cache, T, H, nope, rope, swa, k_scale
+    ("bf16->bf16 SWA", BF16, BF16, 40, 8, 32, 16, True, None),
+    ("bf16->fp8 scaled", BF16, FP8, 33, 4, 64, 32, False, 0.05),
+    ("f32->bf16", F32, BF16, 25, 3, 16, 8, False, None),
+    ("bf16->f32 SWA", BF16, F32, 30, 5, 16, 8, True, None),
+    ("f32->fp8 scaled SWA", F32, FP8, 28, 6, 24, 8, True, 0.04),
+    ("no rope part", BF16, BF16, 12, 4, 32, 0, False, None),
+    ("MLA shape 128 heads", BF16, BF16, 9, 128, 128, 64, True, None),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
+def test_fused_concat_and_cache_matches_oracle_bit_exact(case):
+    """The fused MLA K write equals the oracle's concat into fp32 followed by its
+    K-only cache write (whole caches compared, skipped slots untouched)."""
+    name, src, cdt, T, H, nope, rope, use_swa, ks = case
+    say(f"concat_and_cache_mla_k {name} T={T} H={H} nope={nope} rope={rope}")
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    kn = draw_src(rng, (T, H, nope), src)
+    kr = draw_src(rng, (T, 1, rope), src) if rope else np.zeros((T, 1, 0), dtype=kn.dtype)
+    kd, BS = nope + rope, 8
+    NB = (T + BS - 1) // BS + 2
+    slots = rng.permutation(NB * BS)[:T].astype(np.int64)
+    slots[rng.random(T) < 0.15] = -1
+    swa = None
+    if use_swa:
+        swa = rng.permutation(NB * BS).astype(np.int64)
+        swa[rng.random(NB * BS) < 0.1] = -1
+    k32 = np.zeros((T, H, kd), dtype=np.float32)
+    oracle.concat_and_cast(k32, F32, kn, src, kr, src)
+    oc = sentinel((NB, BS, H, kd), cdt, 0x5A)
+    gc = to_dev(oc, cdt)
+    oracle.reshape_and_cache(k32, None, F32, oc, None, cdt, slots, swa, ks)
+    pkv().concat_and_cache_mla_k(to_dev(kn, src), to_dev(kr, src), gc, torch.from_numpy(slots).cuda(),
+                                 None if swa is None else torch.from_numpy(swa).cuda(),
+                                 None if ks is None else torch.tensor([ks], dtype=torch.float32, device="cuda"))
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(gc, cdt).view(np.uint8), oc.view(np.uint8))
+
+
+def test_fused_mla_write_full_size_equals_unfused_path():
+    """16,384 tokens x 128 heads through the SWA table: the fused write leaves the
+    cache bit-identical to concat (fp32) + K-only write, checked over the whole pool."""
+    w = workloads.mla_concat_swa()
+    T, H, nope, rope, BS, NB = (w["num_tokens"], w["num_heads"], w["nope_dim"], w["rope_dim"],
+                                w["block_size"], w["num_blocks"])
+    say(f"concat_and_cache_mla_k full size T={T} H={H}")
+    m = pkv()
+    kn = workloads.device_normal((T, H, nope), torch.bfloat16, "cuda", w["seed"])
+    kr = workloads.device_normal((T, 1, rope), torch.bfloat16, "cuda", w["seed"] + 1)
+    slots = torch.from_numpy(w["slot_mapping"]).cuda()
+    swa = torch.from_numpy(w["swa_slot_mapping"]).cuda()
+    fused = torch.empty((NB, BS, H, nope + rope), dtype=torch.bfloat16, device="cuda")
+    fused.view(torch.int16).fill_(0x7FA5)
+    m.concat_and_cache_mla_k(kn, kr, fused, slots, swa)
+    k = torch.empty((T, H, nope + rope), dtype=torch.float32, device="cuda")
+    m.concat_and_cast_mla_k(k, kn, kr)
+    unfused = torch.empty_like(fused)
+    unfused.view(torch.int16).fill_(0x7FA5)
+    m.reshape_and_cache(k, None, unfused, None, slots, swa)
+    torch.cuda.synchronize()
+    assert torch.equal(fused.view(torch.int16), unfused.view(torch.int16))
