@@ -1,8 +1,8 @@
 """Benchmark of the paged KV cache hot path on one MI355X.
 
-A step is one decode step of a single Qwen3-0.6B-shaped layer: the cache write
-of the 64 new tokens (pa_reshape_and_cache, bf16) followed by paged decode
-attention over the whole batch (pa_decode_attention), inputs resident in HBM.
+A step is one decode step of a single Qwen3-0.6B-shaped layer, issued as one
+library call (pa_decode_step): the cache write of the 64 new tokens (bf16)
+followed by paged decode attention over the whole batch, inputs resident in HBM.
 Default workload: batch 64, H_Q=16, H_KV=8, d_h=128, block_size 16, context
 lengths uniform in [512, 4096], 32,768-block bf16 pool.
 
@@ -119,6 +119,12 @@ def decode_attn(pkv, t, w):
                          t["ks"], t["vs"], workspace=t["ws"])
 
 
+def decode_step(pkv, t, w):
+    """The whole step in one library call: the write, then the attention."""
+    pkv.decode_step(t["new_k"], t["new_v"], t["slots"], t["out"], t["q"], t["kc"], t["vc"], t["bt"],
+                    t["cl"], w.softmax_scale, t["ks"], t["vs"], workspace=t["ws"])
+
+
 def decode_bytes(w):
     """Algorithmic HBM bytes of one attention call and of the new-token write."""
     ctx = w.context_lens.astype(np.int64)
@@ -161,22 +167,19 @@ def run_decode(args, torch, pkv, workloads, w, metric_name):
     if args.profile_steps:
         copy_calibration(torch, pkv)
         for _ in range(args.profile_steps):
-            decode_write(pkv, t, w)
-            decode_attn(pkv, t, w)
+            decode_step(pkv, t, w)
         torch.cuda.synchronize()
         print(json.dumps({"profile_steps": args.profile_steps, "workload": w.name}))
         return
     for _ in range(args.warmup):
-        decode_write(pkv, t, w)
-        decode_attn(pkv, t, w)
+        decode_step(pkv, t, w)
     torch.cuda.synchronize()
     # (1) the contract: K back-to-back steps between two synchronisations
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record(stream)
     for _ in range(args.steps):
-        decode_write(pkv, t, w)
-        decode_attn(pkv, t, w)
+        decode_step(pkv, t, w)
     t1.record(stream)
     torch.cuda.synchronize()
     ms_per_step = t0.elapsed_time(t1) / args.steps

@@ -9,6 +9,8 @@
  *   pa_concat_and_cache_mla_k the same K assembled straight into the paged cache
  *   pa_decode_attention       one query token per sequence against its paged
  *                             K/V, read back through a block table (GQA)
+ *   pa_decode_step            the new tokens' write and decode attention in
+ *                             one call
  * and the prefill side of the same cache:
  *   pa_prefill_attention      packed chunks of query tokens per sequence,
  *                             causal, against the same paged K/V
@@ -243,6 +245,52 @@ pa_status pa_decode_attention(void* out, pa_dtype out_dtype, int64_t out_seq_str
                               int32_t head_size, float softmax_scale, const float* k_scale,
                               const float* v_scale, void* workspace, size_t workspace_bytes,
                               void* stream);
+
+/*
+ * pa_decode_step -- one decode step in one call: the new tokens' K/V are
+ * written into the paged caches and single-token decode attention runs over
+ * the contexts that now include them. Launch shapes depend on host arguments
+ * only (graph-capturable; no allocation, no host synchronisation).
+ *
+ * Defined by: "PagedAttention principle" page, autoregressive dataflow section
+ * (a decode step computes the new token's q/k/v, writes the KV cache, then
+ * computes attention), i.e. pa_reshape_and_cache followed by
+ * pa_decode_attention. The result equals that sequence of calls:
+ *   pa_reshape_and_cache(new_k, new_v, new_dtype, num_seqs, num_kv_heads,
+ *       head_size, new_k_stride, new_v_stride, key_cache, value_cache,
+ *       cache_dtype, num_blocks, block_size, block_stride, new_slots, NULL, 0,
+ *       k_scale, v_scale, stream);
+ *   pa_decode_attention(out, ..., context_lens, ..., workspace, ...);
+ * where context_lens[b] already counts the new token (position
+ * context_lens[b] - 1). Both kernels go on `stream`, write first; every
+ * argument is checked before either is enqueued, so an error leaves no work
+ * queued. (Reading the new rows from new_k/new_v inside the attention kernel
+ * instead of from the cache was measured slower on gfx950: it costs the
+ * persistent kernel registers in its inner loop.)
+ *
+ * Arguments
+ *   new_k, new_v  [num_seqs, num_kv_heads, head_size], sequence strides
+ *            new_k_stride / new_v_stride (elements); new_dtype PA_BF16.
+ *   new_slots  int64 [num_seqs], device: each new token's cache slot
+ *            (negative or outside the pool = not written, as in
+ *            pa_reshape_and_cache).
+ *   k_scale, v_scale  both or neither: the write divides by them, the
+ *            attention multiplies by them.
+ *   everything else as pa_decode_attention (same workspace size).
+ * Supported: every shape and cache type of pa_decode_attention.
+ * Errors: PA_EINVAL, PA_EDTYPE, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_EHIP.
+ */
+pa_status pa_decode_step(const void* new_k, const void* new_v, pa_dtype new_dtype,
+                         int64_t new_k_stride, int64_t new_v_stride, const int64_t* new_slots,
+                         void* out, pa_dtype out_dtype, int64_t out_seq_stride, const void* q,
+                         pa_dtype q_dtype, int64_t q_seq_stride, void* key_cache,
+                         void* value_cache, pa_dtype cache_dtype, int64_t num_blocks,
+                         int32_t block_size, int64_t block_stride, const int32_t* block_tables,
+                         int32_t max_blocks_per_seq, const int32_t* context_lens,
+                         int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_size, float softmax_scale, const float* k_scale,
+                         const float* v_scale, void* workspace, size_t workspace_bytes,
+                         void* stream);
 
 /*
  * pa_prefill_attention -- chunked-prefill (variable-length, causal) paged

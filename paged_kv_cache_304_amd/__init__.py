@@ -13,6 +13,7 @@ from .ops import (  # noqa: F401
     concat_and_cast_mla_k,
     decode_attention,
     decode_attention_workspace_size,
+    decode_step,
     hbm_copy,
     prefill_attention,
     reshape_and_cache,

@@ -18,7 +18,8 @@ STATUS_NAMES = {PA_OK: "PA_OK", PA_EINVAL: "PA_EINVAL", PA_EDTYPE: "PA_EDTYPE",
 # Every symbol the header declares.
 EXPORTS = ("pa_last_error", "pa_abi_version", "pa_reshape_and_cache", "pa_concat_and_cast_mla_k",
            "pa_concat_and_cache_mla_k",
-           "pa_decode_attention_workspace_size", "pa_decode_attention", "pa_prefill_attention",
+           "pa_decode_attention_workspace_size", "pa_decode_attention", "pa_decode_step",
+           "pa_prefill_attention",
            "pa_hbm_copy")
 
 
@@ -54,6 +55,9 @@ def _load() -> ctypes.CDLL:
     L.pa_decode_attention.argtypes = [P, I32, I64, P, I32, I64, P, P, I32, I64, I32, I64, P, I32, P,
                                       I32, I32, I32, I32, F, P, P, P, SZ, P]
     L.pa_decode_attention.restype = I32
+    L.pa_decode_step.argtypes = [P, P, I32, I64, I64, P, P, I32, I64, P, I32, I64, P, P, I32, I64, I32,
+                                 I64, P, I32, P, I32, I32, I32, I32, F, P, P, P, SZ, P]
+    L.pa_decode_step.restype = I32
     L.pa_prefill_attention.argtypes = [P, I32, I64, P, I32, I64, I64, P, P, P, I32, I64, I32, I64, P,
                                        I32, P, I32, I32, I32, I32, F, P, P, P]
     L.pa_prefill_attention.restype = I32

@@ -1046,17 +1046,24 @@ extern "C" size_t pa_decode_attention_workspace_size(int32_t num_seqs, int32_t n
   return p.bytes;
 }
 
-extern "C" pa_status pa_decode_attention(void* out, pa_dtype out_dtype, int64_t out_seq_stride, const void* q,
-                                         pa_dtype q_dtype, int64_t q_seq_stride, const void* key_cache,
-                                         const void* value_cache, pa_dtype cache_dtype, int64_t num_blocks,
-                                         int32_t block_size, int64_t block_stride, const int32_t* block_tables,
-                                         int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
-                                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_size,
-                                         float softmax_scale, const float* k_scale, const float* v_scale,
-                                         void* workspace, size_t workspace_bytes, void* stream) {
-  using namespace pa;
-  clear_error();
-  const char* fn = "pa_decode_attention";
+namespace pa {
+namespace {
+
+// The new tokens of a decode step (one per sequence, bf16 rows of H_KV*head_size).
+struct NewTokens {
+  const void* k;
+  const void* v;
+  const int64_t* slots;
+  int64_t k_stride, v_stride;
+};
+
+pa_status decode_common(const char* fn, void* out, pa_dtype out_dtype, int64_t out_seq_stride, const void* q,
+                        pa_dtype q_dtype, int64_t q_seq_stride, const void* key_cache, const void* value_cache,
+                        pa_dtype cache_dtype, int64_t num_blocks, int32_t block_size, int64_t block_stride,
+                        const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                        int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_size,
+                        float softmax_scale, const float* k_scale, const float* v_scale, void* workspace,
+                        size_t workspace_bytes, const NewTokens* nt, void* stream) {
   pa_status s = check_sizes(fn, num_seqs, num_q_heads, num_kv_heads, head_size, max_blocks_per_seq, block_size);
   if (s != PA_OK) return s;
   if (out_dtype != PA_BF16 && out_dtype != PA_F32) return fail(PA_EDTYPE, "%s: out dtype %s not supported", fn, dtype_name(out_dtype));
@@ -1068,9 +1075,16 @@ extern "C" pa_status pa_decode_attention(void* out, pa_dtype out_dtype, int64_t 
   if (out_seq_stride < row || q_seq_stride < row) return fail(PA_EINVAL, "%s: sequence strides smaller than H_Q*head_size", fn);
   if (num_blocks < 0) return fail(PA_EINVAL, "%s: num_blocks < 0", fn);
   if (block_stride < (int64_t)block_size * num_kv_heads * head_size) return fail(PA_EINVAL, "%s: block_stride too small", fn);
+  if (nt) {
+    if ((k_scale == nullptr) != (v_scale == nullptr)) return fail(PA_EINVAL, "%s: give both scales or neither", fn);
+    const int64_t kv_row = (int64_t)num_kv_heads * head_size;
+    if (nt->k_stride < kv_row || nt->v_stride < kv_row)
+      return fail(PA_EINVAL, "%s: new-token strides smaller than H_KV*head_size", fn);
+  }
   if (num_seqs == 0) return PA_OK;
   if (!out || !q || !key_cache || !value_cache || !block_tables || !context_lens)
     return fail(PA_EINVAL, "%s: null pointer argument", fn);
+  if (nt && (!nt->k || !nt->v || !nt->slots)) return fail(PA_EINVAL, "%s: null new-token pointer", fn);
   const int cb = dtype_bytes(cache_dtype), ob = dtype_bytes(out_dtype);
   if (!aligned(q, 16) || (q_seq_stride * 2) % 16 != 0) return fail(PA_EINVAL, "%s: q must be 16-byte aligned per sequence", fn);
   if (!aligned(out, 16) || (out_seq_stride * ob) % 16 != 0) return fail(PA_EINVAL, "%s: out must be 16-byte aligned per sequence", fn);
@@ -1111,9 +1125,58 @@ extern "C" pa_status pa_decode_attention(void* out, pa_dtype out_dtype, int64_t 
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (nt) {
+    // the step's cache write goes first on the same stream; it checks its own
+    // arguments before it launches anything, so a refusal leaves no work queued
+    s = pa_reshape_and_cache(nt->k, nt->v, PA_BF16, num_seqs, num_kv_heads, head_size, nt->k_stride, nt->v_stride,
+                             const_cast<void*>(key_cache), const_cast<void*>(value_cache), cache_dtype, num_blocks,
+                             block_size, block_stride, nt->slots, nullptr, 0, k_scale, v_scale, stream);
+    if (s != PA_OK) return s;
+  }
   const int G = num_q_heads / num_kv_heads;
   const bool ok = cache_dtype == PA_BF16 ? launch_d<Ty::BF16>(head_size, G, a, p, st)
                                          : launch_d<Ty::FP8>(head_size, G, a, p, st);
   if (!ok) return fail(PA_EUNSUPPORTED, "%s: no kernel for this shape", fn);
   return after_launch(fn);
+}
+
+}  // namespace
+}  // namespace pa
+
+extern "C" pa_status pa_decode_attention(void* out, pa_dtype out_dtype, int64_t out_seq_stride, const void* q,
+                                         pa_dtype q_dtype, int64_t q_seq_stride, const void* key_cache,
+                                         const void* value_cache, pa_dtype cache_dtype, int64_t num_blocks,
+                                         int32_t block_size, int64_t block_stride, const int32_t* block_tables,
+                                         int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_size,
+                                         float softmax_scale, const float* k_scale, const float* v_scale,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  pa::clear_error();
+  return pa::decode_common("pa_decode_attention", out, out_dtype, out_seq_stride, q, q_dtype, q_seq_stride, key_cache,
+                           value_cache, cache_dtype, num_blocks, block_size, block_stride, block_tables,
+                           max_blocks_per_seq, context_lens, num_seqs, num_q_heads, num_kv_heads, head_size,
+                           softmax_scale, k_scale, v_scale, workspace, workspace_bytes, nullptr, stream);
+}
+
+// Write then attend, as the engine's decode step orders them: the new token
+// enters the cache first, so the attention over context_lens (which count it)
+// reads it back from its slot.
+extern "C" pa_status pa_decode_step(const void* new_k, const void* new_v, pa_dtype new_dtype, int64_t new_k_stride,
+                                    int64_t new_v_stride, const int64_t* new_slots, void* out, pa_dtype out_dtype,
+                                    int64_t out_seq_stride, const void* q, pa_dtype q_dtype, int64_t q_seq_stride,
+                                    void* key_cache, void* value_cache, pa_dtype cache_dtype, int64_t num_blocks,
+                                    int32_t block_size, int64_t block_stride, const int32_t* block_tables,
+                                    int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_size, float softmax_scale,
+                                    const float* k_scale, const float* v_scale, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  pa::clear_error();
+  const char* fn = "pa_decode_step";
+  if (new_dtype != PA_BF16)
+    return pa::fail(PA_EDTYPE, "%s: new-token dtype %s not supported (bf16)", fn, pa::dtype_name(new_dtype));
+  const pa::NewTokens nt{new_k, new_v, new_slots, new_k_stride, new_v_stride};
+  return pa::decode_common(fn, out, out_dtype, out_seq_stride, q, q_dtype, q_seq_stride, key_cache, value_cache,
+                           cache_dtype, num_blocks, block_size, block_stride, block_tables, max_blocks_per_seq,
+                           context_lens, num_seqs, num_q_heads, num_kv_heads, head_size, softmax_scale, k_scale,
+                           v_scale, workspace, workspace_bytes, &nt, stream);
 }

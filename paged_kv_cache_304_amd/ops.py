@@ -182,6 +182,55 @@ def decode_attention(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tensor
     return out
 
 
+def decode_step(new_k: torch.Tensor, new_v: torch.Tensor, new_slots: torch.Tensor,
+                out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tensor,
+                value_cache: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+                softmax_scale: float, k_scale: Optional[torch.Tensor] = None,
+                v_scale: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
+    """One decode step: write each sequence's new token K/V [B, H_KV, D] (bf16)
+    into its slot, then single-token decode attention; writes and returns ``out``."""
+    _on_gpu(new_k, new_v, new_slots, out, q, key_cache, value_cache, block_tables, context_lens,
+            k_scale, v_scale, workspace)
+    B, HQ, D = q.shape
+    NB, BS, HKV, D2 = key_cache.shape
+    if new_k.shape != (B, HKV, D) or new_v.shape != (B, HKV, D):
+        raise ValueError("new_k / new_v must be [B, H_KV, D]")
+    if new_k.stride(2) != 1 or new_k.stride(1) != D or new_v.stride(2) != 1 or new_v.stride(1) != D:
+        raise ValueError("new_k / new_v rows must be contiguous [H_KV, D]")
+    if new_slots.dtype != torch.int64 or new_slots.numel() != B or not new_slots.is_contiguous():
+        raise ValueError("new_slots must be contiguous int64 [B]")
+    if D2 != D or out.shape != q.shape:
+        raise ValueError("q, out and cache head sizes differ")
+    if q.stride(2) != 1 or q.stride(1) != D or out.stride(2) != 1 or out.stride(1) != D:
+        raise ValueError("q and out must be [B, H_Q, D] with contiguous [H_Q, D]")
+    if key_cache.stride(3) != 1 or key_cache.stride(2) != D or key_cache.stride(1) != HKV * D:
+        raise ValueError("cache inner [BS, H_KV, D] must be contiguous")
+    if value_cache.shape != key_cache.shape or value_cache.stride() != key_cache.stride() or \
+            value_cache.dtype != key_cache.dtype:
+        raise ValueError("value_cache must match key_cache")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or \
+            block_tables.shape[0] != B or not block_tables.is_contiguous():
+        raise ValueError("block_tables must be contiguous int32 [B, W]")
+    if context_lens.dtype != torch.int32 or context_lens.numel() != B or \
+            not context_lens.is_contiguous():
+        raise ValueError("context_lens must be contiguous int32 [B]")
+    W = block_tables.shape[1]
+    need = decode_attention_workspace_size(max(B, 1), HQ, HKV, D, W, BS)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if new_v.dtype != new_k.dtype:
+        raise ValueError("new_k and new_v dtypes differ")
+    check(lib.pa_decode_step(
+        new_k.data_ptr(), new_v.data_ptr(), _code(new_k, "new_k"), new_k.stride(0), new_v.stride(0),
+        new_slots.data_ptr(), out.data_ptr(), _code(out, "out"), out.stride(0), q.data_ptr(),
+        _code(q, "q"), q.stride(0), key_cache.data_ptr(), value_cache.data_ptr(),
+        _code(key_cache, "key_cache"), NB, BS, key_cache.stride(0), block_tables.data_ptr(), W,
+        context_lens.data_ptr(), B, HQ, HKV, D, float(softmax_scale), _ptr(k_scale), _ptr(v_scale),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
 def prefill_attention(out: torch.Tensor, q: torch.Tensor, cu_seqlens_q: torch.Tensor,
                       key_cache: torch.Tensor, value_cache: torch.Tensor,
                       block_tables: torch.Tensor, context_lens: torch.Tensor, softmax_scale: float,

@@ -143,6 +143,39 @@ def test_decode_attention_zero_seqs_is_noop(L):
     assert attn(L, B=0, q=None, out=None) == L.PA_OK
 
 
+def step(L, **over):
+    a = dict(nk=1 << 27, nv=1 << 28, ndt=L.PA_BF16, nks=1024, nvs=1024, slots=1 << 29)
+    a.update({k: v for k, v in over.items() if k in a})
+    b = dict(out=1 << 20, odt=L.PA_BF16, os=2048, q=1 << 21, qdt=L.PA_BF16, qs=2048, kc=1 << 22,
+             vc=1 << 23, cdt=L.PA_BF16, NB=16, BS=16, bstride=16 * 8 * 128, bt=1 << 24, W=4,
+             cl=1 << 25, B=2, HQ=16, HKV=8, D=128, scale=0.088, ks=None, vs=None, ws=1 << 26,
+             wsb=1 << 30)
+    b.update({k: v for k, v in over.items() if k in b})
+    return L.lib.pa_decode_step(a["nk"], a["nv"], a["ndt"], a["nks"], a["nvs"], a["slots"],
+                                b["out"], b["odt"], b["os"], b["q"], b["qdt"], b["qs"], b["kc"],
+                                b["vc"], b["cdt"], b["NB"], b["BS"], b["bstride"], b["bt"], b["W"],
+                                b["cl"], b["B"], b["HQ"], b["HKV"], b["D"], b["scale"], b["ks"],
+                                b["vs"], b["ws"], b["wsb"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(ndt=2), "PA_EDTYPE"),               # f32 new tokens
+    (dict(nks=100), "PA_EINVAL"),             # stride below H_KV * D
+    (dict(nv=None), "PA_EINVAL"),
+    (dict(slots=None), "PA_EINVAL"),
+    (dict(cdt=3, ks=1 << 30, vs=None), "PA_EINVAL"),   # one scale only
+    (dict(HQ=12), "PA_EINVAL"),               # the attention's own checks come first too
+    (dict(wsb=16), "PA_EWORKSPACE"),
+])
+def test_decode_step_rejects_before_enqueueing(L, over, code):
+    assert step(L, **over) == getattr(L, code)
+    assert L.last_error()
+
+
+def test_decode_step_zero_seqs_is_noop(L):
+    assert step(L, B=0, q=None, out=None, nk=None, nv=None, slots=None) == L.PA_OK
+
+
 def test_workspace_size_is_pure_and_validates(L):
     f = L.lib.pa_decode_attention_workspace_size
     n = f(64, 16, 8, 128, 256, 16)
