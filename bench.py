@@ -41,7 +41,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="decode_b64",
                    choices=["decode_b64", "prefill_fp8", "decode_fp8_b256", "mla_concat_swa",
-                            "mla_fused", "prefill_chunks"])
+                            "mla_fused", "prefill_chunks", "engine_decode_b64"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--profile-steps", type=int, default=0,
                    help="only run this many untimed steps (for rocprofv3 runs)")
@@ -467,6 +467,170 @@ def cpu_baseline_prefill(torch, q, kc, vc, w, oracle):
                       f"{flops / 1e9:.1f} GFLOP) in {dt:.1f} s"}
 
 
+def engine_prefill_rounds(plan, lens, chunk=16):
+    """Give every sequence its first lens[b] positions in rounds of `chunk` tokens
+    per sequence, all sequences per round (a chunked prefill): each sequence's
+    blocks then interleave with the others' instead of lying side by side."""
+    left = lens.astype(np.int64).copy()
+    while left.any():
+        seqs = np.nonzero(left)[0].astype(np.int32)
+        num = np.minimum(left[seqs], chunk).astype(np.int32)
+        plan(seqs, num)
+        left[seqs] -= num
+
+
+def engine_width(args, w) -> int:
+    """Table width that holds every context after all the steps this run takes."""
+    loops = args.warmup + 2 * args.steps
+    return -(-(int(w.context_lens.max()) + loops) // w.block_size)
+
+
+def run_engine_decode(args, torch, pkv, workloads):
+    """The batch-64 decode workload driven the way an engine drives it: each step
+    the native block manager plans one new token per sequence (slots, tables,
+    lengths), one host-to-device copy uploads that metadata, and pa_decode_step
+    writes and attends. Contexts grow by one token per step; planning of step
+    k+1 overlaps the GPU work of step k (two pinned staging blobs)."""
+    import dataclasses
+    w = workloads.qwen3_decode_b64()
+    B, HQ, HKV, D, BS, NB = (w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_size,
+                             w.block_size, w.num_blocks)
+    W = engine_width(args, w)
+    bm = pkv.BlockManager(NB, BS, B, W, B, 16 * B)
+    lens = w.context_lens.astype(np.int64) - 1          # positions cached before the first step
+    engine_prefill_rounds(lambda s, n: bm.plan_host(s, n), lens)
+    stager = pkv.StepStager(bm)
+    dev = "cuda"
+    kc = workloads.device_normal((NB, BS, HKV, D), torch.bfloat16, dev, w.seed)
+    vc = workloads.device_normal((NB, BS, HKV, D), torch.bfloat16, dev, w.seed + 1)
+    q = workloads.device_normal((B, HQ, D), torch.bfloat16, dev, w.seed + 2)
+    nk = workloads.device_normal((B, HKV, D), torch.bfloat16, dev, w.seed + 3)
+    nv = workloads.device_normal((B, HKV, D), torch.bfloat16, dev, w.seed + 4)
+    out = torch.empty_like(q)
+    ws = torch.zeros(pkv.decode_attention_workspace_size(B, HQ, HKV, D, W, BS), dtype=torch.uint8,
+                     device=dev)
+    seqs = np.arange(B, dtype=np.int32)
+    ones = np.ones(B, dtype=np.int32)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        d = stager.step(seqs, ones)
+        pkv.decode_step(nk, nv, d.slot_mapping, out, q, kc, vc, d.block_tables, d.context_lens,
+                        w.softmax_scale, workspace=ws)
+        lens[:] += 1
+        return d
+
+    def kv_bytes():
+        return int(2 * lens.sum() * HKV * D * 2)
+
+    if args.profile_steps:
+        copy_calibration(torch, pkv)
+        for _ in range(args.profile_steps):
+            step()
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_steps": args.profile_steps, "workload": "engine_decode_b64"}))
+        return
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # (1) K whole steps (plan + upload + write + attention) between two synchronisations
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    kv = 0
+    h0 = time.perf_counter()
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+        kv += kv_bytes()
+    t1.record(stream)
+    h1 = time.perf_counter()
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    host_us_per_step = (h1 - h0) / args.steps * 1e6
+    # (2) the parts: host planning, the upload copy, decode attention on the uploaded metadata
+    blob = stager.host[0]
+    plan_s = 0.0
+    tu, ta = Timer(torch, stream), Timer(torch, stream)
+    attn_bytes = 0
+    for _ in range(args.steps):
+        torch.cuda.synchronize()
+        s0 = time.perf_counter()
+        rows, toks, _ = bm.plan_into(blob.data_ptr(), blob.numel(), seqs, ones)
+        plan_s += time.perf_counter() - s0
+        lens[:] += 1
+        tu.start()
+        pkv._lib.check(pkv._lib.lib.pa_bm_upload(bm._h, blob.data_ptr(), stager.dev.data_ptr(), rows,
+                                                 stream.cuda_stream))
+        tu.stop()
+        lay = bm.layout
+        d = stager.dev
+        bt = d[lay.block_tables:lay.block_tables + 4 * B * W].view(torch.int32).view(B, W)
+        cl = d[lay.context_lens:lay.context_lens + 4 * B].view(torch.int32)
+        ta.start()
+        pkv.decode_attention(out, q, kc, vc, bt, cl, w.softmax_scale, workspace=ws)
+        ta.stop()
+        attn_bytes += decode_bytes(dataclasses.replace(w, context_lens=lens.astype(np.int32)))[1]
+    torch.cuda.synchronize()
+    attn_ms, up_ms = ta.mean_ms(), tu.mean_ms()
+    attn_bytes //= args.steps
+    achieved = attn_bytes / (attn_ms * 1e-3) / 1e9
+    up_bytes = int(bm.layout.block_tables + 4 * B * W)
+    value = kv / args.steps / (ms_per_step * 1e-3) / 1e9
+    res = {
+        "metric": "paged decode attn KV-read GB/s & % HBM peak; cache-write GB/s (1 MI355X)",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) K/V/q of Qwen3-0.6B shapes)",
+        "config": {"workload": "engine_decode_b64", "num_seqs": B, "num_q_heads": HQ,
+                   "num_kv_heads": HKV, "head_size": D, "block_size": BS, "num_blocks": NB,
+                   "context_lens": f"{int(w.context_lens.min())}..{int(w.context_lens.max())} "
+                                   "at the first step, +1 per step",
+                   "allocation": "native block manager, 16-token chunked prefill rounds"},
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
+        "tokens_per_s": round(B / (ms_per_step * 1e-3), 1),
+        "host": {"plan_us": round(plan_s / args.steps * 1e6, 2),
+                 "enqueue_us_per_step": round(host_us_per_step, 2),
+                 "upload_us": round(up_ms * 1e3, 2), "upload_bytes": up_bytes},
+        "attention": {"ms": round(attn_ms, 5), "bytes": attn_bytes, "GBps": round(achieved, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        res["cpu_baseline"] = cpu_baseline_engine(torch, w, W, oracle, kc, vc, q, nk, nv, lens)
+    print(json.dumps(res))
+
+
+def cpu_baseline_engine(torch, w, W, oracle, kc, vc, q, nk, nv, lens):
+    """The oracle on one engine step: its block pool brought to the same state
+    (untimed), then -- timed -- planning the step, the new-token write and fp64
+    attention."""
+    from oracle.block_pool import BlockPool
+    B, BS = w.num_seqs, w.block_size
+    pool = BlockPool(w.num_blocks, BS, W)
+    engine_prefill_rounds(lambda s, n: pool.step(s, n), w.context_lens.astype(np.int64) - 1)
+    grown = lens - (w.context_lens.astype(np.int64) - 1)   # steps the GPU side has taken
+    for _ in range(int(grown[0])):
+        pool.step(range(B), [1] * B)
+    kch = kc.view(torch.int16).cpu().numpy().view(np.uint16)
+    vch = vc.view(torch.int16).cpu().numpy().view(np.uint16)
+    qh = q.view(torch.int16).cpu().numpy().view(np.uint16)
+    nkh = nk.view(torch.int16).cpu().numpy().view(np.uint16)
+    nvh = nv.view(torch.int16).cpu().numpy().view(np.uint16)
+    t0 = time.perf_counter()
+    sm, bt, cl, _ = pool.step_arrays(range(B), [1] * B, W)
+    t1 = time.perf_counter()
+    oracle.reshape_and_cache(nkh, nvh, oracle.BF16, kch, vch, oracle.BF16, sm)
+    oracle.decode_attention(qh, oracle.BF16, kch, vch, oracle.BF16, bt, cl, w.softmax_scale)
+    dt = time.perf_counter() - t0
+    kv = int(2 * cl.astype(np.int64).sum() * w.num_kv_heads * w.head_size * 2)
+    return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": cpu_cores(), "kind": "oracle",
+            "sample": f"one engine step ({B} sequences, {int(cl.sum())} tokens): oracle block-pool "
+                      f"planning ({(t1 - t0) * 1e6:.0f} us) + write + fp64 attention, {dt:.2f} s, "
+                      "KV-read bytes / time"}
+
+
 def run_decode_fp8(args, torch, pkv, workloads):
     w = workloads.mixed_decode_fp8()
     return run_decode(args, torch, pkv, workloads, w,
@@ -533,6 +697,8 @@ def main():
         run_prefill_chunks(args, torch, pkv, workloads)
     elif args.workload == "mla_fused":
         run_mla_fused(args, torch, pkv, workloads)
+    elif args.workload == "engine_decode_b64":
+        run_engine_decode(args, torch, pkv, workloads)
     else:
         run_mla(args, torch, pkv, workloads)
 

@@ -14,11 +14,16 @@
  * and the prefill side of the same cache:
  *   pa_prefill_attention      packed chunks of query tokens per sequence,
  *                             causal, against the same paged K/V
+ * and, on the host, the bookkeeping that feeds them:
+ *   pa_bm_*                   block manager: allocation in block_size units,
+ *                             per-step slot_mapping / block_tables /
+ *                             context_lens / cu_seqlens_q, one H2D upload
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller. The library
  *     never allocates, frees or retains device memory and holds no state
- *     between calls except the thread-local error text.
+ *     between calls except the thread-local error text and the host-memory
+ *     block managers that the caller creates and destroys (pa_bm_*).
  *   - Strides and sizes are in ELEMENTS of the tensor they describe.
  *   - `stream` is a hipStream_t (NULL = the legacy default stream). Every call
  *     only enqueues work: it returns after the launch, never synchronises,
@@ -51,7 +56,8 @@ enum {
   PA_EDTYPE = 2,       /* unsupported dtype or dtype combination */
   PA_EUNSUPPORTED = 3, /* valid but not implemented (e.g. head_size) */
   PA_EHIP = 4,         /* the HIP runtime reported an error at launch */
-  PA_EWORKSPACE = 5    /* workspace missing, too small or misaligned */
+  PA_EWORKSPACE = 5,   /* workspace missing, too small or misaligned */
+  PA_ENOSPACE = 6      /* block manager: not enough free blocks */
 };
 
 /* Element types. bf16 and fp32 are IEEE-style; fp8 is OCP e4m3fn (bias 7,
@@ -349,6 +355,122 @@ pa_status pa_prefill_attention(void* out, pa_dtype out_dtype, int64_t out_token_
  * Errors: PA_EINVAL, PA_EHIP.
  */
 pa_status pa_hbm_copy(void* dst, const void* src, size_t bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Block manager (host side).
+ *
+ * Defined by: "PagedAttention principle" page, paged attention principle
+ * section -- memory is handed out in blocks of block_size token slots, so a
+ * request of n tokens holds ceil(n / block_size) blocks and wastes less than
+ * one; a sequence's blocks need not be adjacent, a table keeps their order;
+ * the host knows every request's blocks and copies the table to the device
+ * before the launch; and the design must stay usable under graph capture
+ * (fixed shapes, no data-dependent host branching in the captured work).
+ * The slot of a position is the "Triton paged KV cache write" page's: slot =
+ * block * block_size + offset (section 2.6).
+ *
+ * Sequences are ids 0..max_seqs-1. A sequence's length is the number of
+ * token positions it has been given; it holds exactly ceil(length /
+ * block_size) blocks, listed in position order in its table. A step grows a
+ * set of sequences by some tokens each (a prefill chunk, or one token per
+ * sequence in decode) and produces that step's metadata: the slot of every
+ * new token, the block table, context length (the new length) and packed
+ * query offsets of every listed sequence, in one host blob laid out by
+ * pa_bm_layout_of; pa_bm_upload copies the blob to the device in one copy,
+ * after which the device pointers base + offset are the kernels' arguments.
+ *
+ * Allocation order (deterministic): free blocks form a stack that starts as
+ * 0, 1, ..., num_blocks-1 from the top; a step takes new blocks from the top,
+ * sequence by sequence in the order listed, positions in increasing order;
+ * pa_bm_release pushes a sequence's blocks back so that its first block is
+ * on top. A manager is not thread-safe; it lives in host memory only.
+ * ------------------------------------------------------------------------ */
+typedef struct pa_block_manager pa_block_manager;
+
+/* Byte offsets of the step blob's arrays (each 256-byte aligned):
+ *   context_lens  int32 [max_step_seqs]
+ *   cu_seqlens_q  int32 [max_step_seqs + 1]
+ *   slot_mapping  int64 [max_step_tokens]
+ *   block_tables  int32 [max_step_seqs, max_blocks_per_seq]  (last)
+ * bytes = the whole blob. */
+typedef struct {
+  int64_t context_lens;
+  int64_t cu_seqlens_q;
+  int64_t slot_mapping;
+  int64_t block_tables;
+  int64_t bytes;
+} pa_bm_layout;
+
+/*
+ * pa_bm_create -- a manager of num_blocks blocks of block_size slots for up
+ * to max_seqs sequences of at most max_blocks_per_seq blocks each; a step
+ * lists at most max_step_seqs sequences and adds at most max_step_tokens
+ * tokens. All sizes > 0; num_blocks and max_blocks_per_seq * block_size fit
+ * int32. *out receives the manager (NULL on error).
+ * Errors: PA_EINVAL.
+ */
+pa_status pa_bm_create(int64_t num_blocks, int32_t block_size, int32_t max_seqs,
+                       int32_t max_blocks_per_seq, int32_t max_step_seqs,
+                       int64_t max_step_tokens, pa_block_manager** out);
+
+/* Frees the manager's host memory (NULL is a no-op). */
+void pa_bm_destroy(pa_block_manager* bm);
+
+/* The step blob's layout. Errors: PA_EINVAL (NULL argument). */
+pa_status pa_bm_layout_of(const pa_block_manager* bm, pa_bm_layout* out);
+
+/* Free blocks now; -1 for a NULL manager. */
+int64_t pa_bm_free_blocks(const pa_block_manager* bm);
+
+/* Length of sequence `seq`; -1 for a bad id or NULL manager. */
+int64_t pa_bm_seq_len(const pa_block_manager* bm, int32_t seq);
+
+/* Copies sequence `seq`'s block table (position order) into blocks[0..);
+ * returns the number of blocks, or -1 for a bad id, a NULL pointer or a
+ * capacity below that number. */
+int32_t pa_bm_seq_table(const pa_block_manager* bm, int32_t seq, int32_t* blocks,
+                        int32_t capacity);
+
+/* Returns every block of sequence `seq` to the free stack; its length
+ * becomes 0. Releasing an empty sequence is a no-op.
+ * Errors: PA_EINVAL (bad id, NULL manager). */
+pa_status pa_bm_release(pa_block_manager* bm, int32_t seq);
+
+/*
+ * pa_bm_plan_step -- grow sequence seqs[i] by num_new[i] tokens (i <
+ * num_seqs) and write the step blob into host_meta:
+ *   context_lens[i]  = the new length (the chunk of sequence i is its last
+ *                      num_new[i] positions);
+ *   cu_seqlens_q[i]  = num_new[0] + ... + num_new[i-1] (i <= num_seqs);
+ *   slot_mapping[cu_seqlens_q[i] + j] = slot of position old_len_i + j;
+ *   block_tables[i, k] = the sequence's k-th block, -1 past its last block.
+ * Rows num_seqs..pad_seqs-1 are filled as empty sequences (length 0,
+ * cu_seqlens_q = the total, table all -1) and slot_mapping entries
+ * total..pad_tokens-1 with -1, so a caller can launch every step with the
+ * fixed sizes (pad_seqs, pad_tokens) -- the padding is a no-op for the
+ * kernels. *num_tokens receives the total of num_new (may be NULL).
+ * Either the whole step is applied or, on any error, nothing changes.
+ * Arguments: seqs distinct ids; num_new[i] >= 0; num_seqs <= pad_seqs <=
+ *   max_step_seqs; total <= pad_tokens <= max_step_tokens; no sequence may
+ *   exceed max_blocks_per_seq blocks; host_meta >= layout bytes, 8-byte
+ *   aligned (pinned memory if it is to be uploaded asynchronously).
+ * Errors: PA_EINVAL, PA_ENOSPACE (fewer free blocks than the step needs).
+ */
+pa_status pa_bm_plan_step(pa_block_manager* bm, const int32_t* seqs, const int32_t* num_new,
+                          int32_t num_seqs, int32_t pad_seqs, int64_t pad_tokens,
+                          void* host_meta, int64_t host_meta_bytes, int64_t* num_tokens);
+
+/*
+ * pa_bm_upload -- one asynchronous host-to-device copy of the step blob's
+ * used part (everything before block_tables, then pad_seqs table rows) from
+ * host_meta to device_meta (a device buffer of layout bytes, 256-byte
+ * aligned) on `stream`. With pinned host memory and a fixed pad_seqs the copy
+ * can be captured into a HIP graph; the host must not rewrite host_meta
+ * until the copy has executed.
+ * Errors: PA_EINVAL, PA_EHIP.
+ */
+pa_status pa_bm_upload(const pa_block_manager* bm, const void* host_meta, void* device_meta,
+                       int32_t pad_seqs, void* stream);
 
 #ifdef __cplusplus
 }

@@ -4,10 +4,11 @@ The compute runs in ``libpagedkv.so`` (hand-written HIP, see ``csrc/``); this
 package only marshals torch tensors into the C entry points declared in
 ``include/pagedkv.h``. PyTorch provides device memory and the current HIP
 stream, nothing else. Importing the package fails loudly when the library has
-not been built (``python -m paged_kv_cache_304_amd.build``): there is no
+not been built (``python paged_kv_cache_304_amd/build.py``): there is no
 fallback implementation.
 """
 from ._lib import LIB_PATH, PagedKVError, abi_version, lib  # noqa: F401
+from .blocks import BlockManager, DeviceStep, StepStager  # noqa: F401
 from .ops import (  # noqa: F401
     concat_and_cache_mla_k,
     concat_and_cast_mla_k,

@@ -69,3 +69,23 @@ def assert_attention_close(gpu: np.ndarray, ref: np.ndarray, what: str = "",
         i = np.unravel_index(np.argmax(err - bound), err.shape)
         raise AssertionError(f"{what}: {bad.sum()} of {err.size} outside tolerance; worst at {i}: "
                              f"gpu={gpu[i]!r} oracle={ref[i]!r} err={err[i]:.3e}")
+
+
+def abs_values(cache_bits):
+    return cache_bits & np.uint16(0x7FFF)   # |x| of bf16 (NaN stays NaN)
+
+
+def check_close(got, ref, ref_abs, what, out_bf16):
+    """Prefill bound: the decode bound plus 2^-9 * sum_j p_j |v_j| / l for the bf16
+    probabilities of the P.V product (ref_abs = the oracle run on |V|)."""
+    assert got.shape == ref.shape
+    assert np.all(np.isfinite(got)), f"{what}: non-finite GPU output"
+    tol = 2e-3 + 2e-3 * np.abs(ref) + 2.0 ** -9 * ref_abs * 1.001
+    if out_bf16:
+        tol = tol + bf16_half_ulp(ref)
+    err = np.abs(got - ref)
+    bad = err > tol
+    if bad.any():
+        i = np.unravel_index(np.argmax(err - tol), err.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())} of {err.size} outside the bound; worst at {i}: "
+                             f"gpu {got[i]!r} oracle {ref[i]!r} tol {tol[i]!r}")

@@ -38,7 +38,7 @@ def test_abi_version_matches_header(L):
 
 def test_status_and_dtype_codes_match_header(L):
     text = open(HEADER).read()
-    for name in ("PA_OK", "PA_EINVAL", "PA_EDTYPE", "PA_EUNSUPPORTED", "PA_EHIP", "PA_EWORKSPACE",
+    for name in ("PA_OK", "PA_EINVAL", "PA_EDTYPE", "PA_EUNSUPPORTED", "PA_EHIP", "PA_EWORKSPACE", "PA_ENOSPACE",
                  "PA_BF16", "PA_F32", "PA_FP8_E4M3FN"):
         m = re.search(rf"\b{name}\s*=\s*(\d+)", text)
         assert m and int(m.group(1)) == getattr(L, name), name

@@ -20,7 +20,7 @@ import torch
 
 import oracle
 import workloads
-from parity_util import bf16_half_ulp, say, to_dev, to_host
+from parity_util import abs_values, check_close, say, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -72,24 +72,6 @@ def gpu_prefill(q, kc, vc, bt, ctx, cu, scale, out_dt=BF16):
                         torch.from_numpy(bt).cuda(), torch.from_numpy(ctx).cuda(), scale)
     torch.cuda.synchronize()
     return out
-
-
-def abs_values(cache_bits):
-    return cache_bits & np.uint16(0x7FFF)   # |x| of bf16 (NaN stays NaN)
-
-
-def check_close(got, ref, ref_abs, what, out_bf16):
-    assert got.shape == ref.shape
-    assert np.all(np.isfinite(got)), f"{what}: non-finite GPU output"
-    tol = 2e-3 + 2e-3 * np.abs(ref) + 2.0 ** -9 * ref_abs * 1.001
-    if out_bf16:
-        tol = tol + bf16_half_ulp(ref)
-    err = np.abs(got - ref)
-    bad = err > tol
-    if bad.any():
-        i = np.unravel_index(np.argmax(err - tol), err.shape)
-        raise AssertionError(f"{what}: {int(bad.sum())} of {err.size} outside the bound; worst at {i}: "
-                             f"gpu {got[i]!r} oracle {ref[i]!r} tol {tol[i]!r}")
 
 
 def run_and_check(name, q, kc, vc, bt, ctx, cu, scale):
