@@ -69,6 +69,9 @@ def _load():
     lib.orc_prefill_attention.argtypes = [P, P, I32, I64, P, I32, P, P, I32, I64, I32, I64, P, I32,
                                           P, I32, I32, I32, F64, P, P]
     lib.orc_prefill_attention.restype = None
+    lib.orc_mla_decode.argtypes = [P, P, I64, P, I64, P, P, P, I64, I32, I64, P, I32, P, I32, I32,
+                                   I32, I32, I32, I32, F64]
+    lib.orc_mla_decode.restype = None
     _lib = lib
     return lib
 
@@ -236,4 +239,36 @@ def prefill_attention(q, q_dtype: int, cu_seqlens_q, key_cache, value_cache, cac
                               _ptr(key_cache), _ptr(value_cache), cache_dtype, NB, BS,
                               block_stride, _ptr(bt), bt.shape[1], _ptr(cl), HQ, HKV, D,
                               float(softmax_scale), _ptr(ks), _ptr(vs))
+    return out
+
+
+def mla_decode(q_nope, q_rope, w_uk, w_uv, latent_cache, block_tables, context_lens,
+               softmax_scale: float) -> np.ndarray:
+    """fp64 MLA decode over a latent paged cache with K and V materialised from the
+    latent as the page defines them (R13).
+
+    bf16 bit arrays: ``q_nope`` [B, H, qk], ``q_rope`` [B, H, r] (or None for no
+    RoPE part), ``w_uk`` [d_c, H*qk], ``w_uv`` [d_c, H*dv], ``latent_cache``
+    [NB, BS, d_c + r]; ``block_tables`` int32 [B, W]; ``context_lens`` int32 [B].
+    Returns [B, H, dv] fp64."""
+    lib = _load()
+    B, H, QK = q_nope.shape
+    NB, BS, ROW = latent_cache.shape
+    R = 0 if q_rope is None else q_rope.shape[2]
+    DC = ROW - R
+    assert w_uk.shape == (DC, H * QK) and w_uv.shape[0] == DC and w_uv.shape[1] % H == 0
+    DV = w_uv.shape[1] // H
+    for a in (q_nope, w_uk, w_uv, latent_cache) + (() if q_rope is None else (q_rope,)):
+        assert a.dtype == np.uint16
+    qn = np.ascontiguousarray(q_nope)
+    qr = np.zeros((B, H, 1), dtype=np.uint16) if q_rope is None else np.ascontiguousarray(q_rope)
+    wk, wv = np.ascontiguousarray(w_uk), np.ascontiguousarray(w_uv)
+    lc = np.ascontiguousarray(latent_cache)
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+    assert bt.shape[0] == B and cl.shape[0] == B
+    out = np.zeros((B, H, DV), dtype=np.float64)
+    lib.orc_mla_decode(out.ctypes.data, _ptr(qn), H * QK, _ptr(qr), H * max(R, 1), _ptr(wk), _ptr(wv),
+                       _ptr(lc), NB, BS, BS * ROW, _ptr(bt), bt.shape[1], _ptr(cl), B, H, QK, R, DC, DV,
+                       float(softmax_scale))
     return out

@@ -2,8 +2,9 @@
  * CPU oracle for the paged KV cache hot path.
  *
  * TEST INFRASTRUCTURE ONLY. This file states, as plainly as possible, what the
- * cache write, the MLA-style K concat, single-token paged decode attention and
- * chunked-prefill (variable-length, causal) paged attention compute, so that the GPU kernels can be checked against it. Only the test
+ * cache write, the MLA-style K concat, single-token paged decode attention,
+ * chunked-prefill (variable-length, causal) paged attention and MLA decode over
+ * a latent paged cache compute, so that the GPU kernels can be checked against it. Only the test
  * suite, the smoke check and the benchmark's CPU-baseline leg may load it; the
  * product library never links or calls it, and it shares no source, header,
  * table or helper with the HIP path.
@@ -24,6 +25,10 @@
  *    variable-length flash path of prefill.
  *  - "PagedAttention principle" page, autoregressive dataflow section: prefill
  *    computes causal attention over the prompt while caching its K/V.
+ *  - "PagedAttention principle" page, MLA paragraphs of the GQA/MLA shapes
+ *    section: MLA caches the latent c_kv = x W_DKV ([d_c] per token) instead of
+ *    K and V, which are recovered as c_kv W_UK and c_kv W_UV ([H_Q * d_h],
+ *    reshaped per head); the q.k dimension carries a RoPE part that v lacks.
  *  - SGLang cache_ops.py (Triton): concat_and_cast_mha_k (per-head k_nope with
  *    one shared k_rope, cast at the store) and reshape_and_cache_flash (source
  *    token strides, optional second-stage SWA slot remap, optional division by
@@ -60,6 +65,16 @@
  *      through block_tables[b] (the same clamping, dequantisation, GQA mapping
  *      and table-entry rule as R7). A query with p < 0 (n_b > ctx_b) has no
  *      key and gives zeros. n_b = 1 is exactly R7's decode step.
+ *  R13 MLA over a latent cache: per token the cache holds one row, the latent
+ *      c (latent_dim values) followed by a RoPE key part k_r (rope_dim values,
+ *      possibly none) shared by every head. Head h's key and value are the
+ *      page's up-projections k_h = (c W_UK)[h*qk_dim ..], v_h = (c W_UV)[h*v_dim
+ *      ..] with W_UK [latent_dim, H*qk_dim], W_UV [latent_dim, H*v_dim]; the
+ *      query of head h is q_nope[h] (qk_dim) and q_rope[h] (rope_dim), and the
+ *      score is scale * (q_nope[h].k_h + q_rope[h].k_r) -- the page says only
+ *      that the q.k dimension carries a RoPE part that v lacks; the decoupled,
+ *      shared RoPE key is the form the MLA-style concat of a shared k_rope
+ *      produces. Context clamping and the table-entry rule are R7's.
  *
  * Build: gcc -O2 -std=c11 -fopenmp -ffp-contract=off -fPIC -shared
  * (no fast-math: IEEE single division and round-to-nearest are required).
@@ -352,6 +367,89 @@ void orc_decode_attention(double* out, const void* q, int q_dt, int64_t q_seq_st
       for (int d = 0; d < head_size; ++d) o[d] /= l;
       free(s);
     }
+}
+
+/* MLA decode attention over a latent paged cache (R13), with K and V written
+ * out as the page defines them: for each cached position the latent row c is
+ * multiplied by W_UK and W_UV (k_raw = c W_UK, v_raw = c W_UV, then split per
+ * head), and each head runs R7's two-pass softmax attention with the RoPE term
+ * added to its scores. All inputs are bf16 bit patterns; out is fp64
+ * [num_seqs, num_heads, v_dim], unrounded. latent_cache is [num_blocks,
+ * block_size, latent_dim + rope_dim] with block stride block_stride. */
+void orc_mla_decode(double* out, const uint16_t* q_nope, int64_t q_nope_stride, const uint16_t* q_rope,
+                    int64_t q_rope_stride, const uint16_t* w_uk, const uint16_t* w_uv,
+                    const uint16_t* latent_cache, int64_t num_blocks, int block_size, int64_t block_stride,
+                    const int32_t* block_tables, int W, const int32_t* context_lens, int num_seqs,
+                    int num_heads, int qk_dim, int rope_dim, int latent_dim, int v_dim,
+                    double softmax_scale) {
+  const int row_len = latent_dim + rope_dim;
+  const int64_t kw = (int64_t)num_heads * qk_dim, vw = (int64_t)num_heads * v_dim;
+  for (int b = 0; b < num_seqs; ++b) {
+    int64_t ctx = context_lens[b];
+    if (ctx < 0) ctx = 0;
+    if (ctx > (int64_t)W * block_size) ctx = (int64_t)W * block_size;
+    for (int64_t i = 0; i < vw; ++i) out[(int64_t)b * vw + i] = 0.0;
+    if (ctx == 0) continue;
+    /* the up-projected keys and values of every position (k_raw, v_raw) */
+    double* K = (double*)malloc(sizeof(double) * (size_t)(ctx * kw));
+    double* V = (double*)malloc(sizeof(double) * (size_t)(ctx * vw));
+    int64_t* row = (int64_t*)malloc(sizeof(int64_t) * (size_t)ctx);
+#pragma omp parallel for schedule(dynamic)
+    for (int64_t p = 0; p < ctx; ++p) {
+      int32_t phys = block_tables[(int64_t)b * W + p / block_size];
+      if (phys < 0 || phys >= num_blocks) {
+        row[p] = -1;
+        continue;
+      }
+      row[p] = (int64_t)phys * block_stride + (p % block_size) * (int64_t)row_len;
+      for (int64_t j = 0; j < kw; ++j) {
+        double acc = 0.0;
+        for (int c = 0; c < latent_dim; ++c)
+          acc += orc_load_f64(latent_cache, row[p] + c, ORC_BF16) * orc_load_f64(w_uk, (int64_t)c * kw + j, ORC_BF16);
+        K[p * kw + j] = acc;
+      }
+      for (int64_t j = 0; j < vw; ++j) {
+        double acc = 0.0;
+        for (int c = 0; c < latent_dim; ++c)
+          acc += orc_load_f64(latent_cache, row[p] + c, ORC_BF16) * orc_load_f64(w_uv, (int64_t)c * vw + j, ORC_BF16);
+        V[p * vw + j] = acc;
+      }
+    }
+#pragma omp parallel for schedule(dynamic)
+    for (int h = 0; h < num_heads; ++h) {
+      double* o = out + (int64_t)b * vw + (int64_t)h * v_dim;
+      const int64_t qn = (int64_t)b * q_nope_stride + (int64_t)h * qk_dim;
+      const int64_t qr = (int64_t)b * q_rope_stride + (int64_t)h * rope_dim;
+      double* s = (double*)malloc(sizeof(double) * (size_t)ctx);
+      double m = -INFINITY;
+      for (int64_t p = 0; p < ctx; ++p) {
+        if (row[p] < 0) {
+          s[p] = -INFINITY;
+          continue;
+        }
+        double dot = 0.0;
+        for (int j = 0; j < qk_dim; ++j) dot += orc_load_f64(q_nope, qn + j, ORC_BF16) * K[p * kw + (int64_t)h * qk_dim + j];
+        for (int r = 0; r < rope_dim; ++r)
+          dot += orc_load_f64(q_rope, qr + r, ORC_BF16) * orc_load_f64(latent_cache, row[p] + latent_dim + r, ORC_BF16);
+        s[p] = softmax_scale * dot;
+        if (s[p] > m) m = s[p];
+      }
+      if (m != -INFINITY) {
+        double l = 0.0;
+        for (int64_t p = 0; p < ctx; ++p) {
+          if (s[p] == -INFINITY) continue;
+          double w = exp(s[p] - m);
+          l += w;
+          for (int j = 0; j < v_dim; ++j) o[j] += w * V[p * vw + (int64_t)h * v_dim + j];
+        }
+        for (int j = 0; j < v_dim; ++j) o[j] /= l;
+      }
+      free(s);
+    }
+    free(K);
+    free(V);
+    free(row);
+  }
 }
 
 /* Chunked-prefill paged attention (R10): for sequence b with n_b queries and
