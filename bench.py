@@ -41,7 +41,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="decode_b64",
                    choices=["decode_b64", "prefill_fp8", "decode_fp8_b256", "mla_concat_swa",
-                            "mla_fused", "prefill_chunks", "engine_decode_b64"])
+                            "mla_fused", "prefill_chunks", "engine_decode_b64",
+                            "mla_decode_b64"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--profile-steps", type=int, default=0,
                    help="only run this many untimed steps (for rocprofv3 runs)")
@@ -631,6 +632,133 @@ def cpu_baseline_engine(torch, w, W, oracle, kc, vc, q, nk, nv, lens):
                       "KV-read bytes / time"}
 
 
+def mla_bytes(w) -> dict:
+    """Algorithmic HBM bytes of one MLA decode call: the latent rows read once,
+    the weights and queries read once, the absorbed query written and read
+    back per 256-position piece, the pieces' partial outputs written and read
+    once, the output written."""
+    ctx = w["context_lens"].astype(np.int64)
+    B, H, QK, R, DC, DV = (w["num_seqs"], w["num_heads"], w["qk_nope_dim"], w["rope_dim"],
+                           w["kv_lora_rank"], w["v_dim"])
+    row = DC + R
+    pieces = int(np.sum(-(-ctx // 256)))
+    latent = int(ctx.sum() * row * 2)
+    tables = int(np.sum(-(-ctx // w["block_size"])) * 4 + 4 * B)
+    weights = DC * H * (QK + DV) * 2
+    q = B * H * (QK + R) * 2
+    qt = B * H * row * 2 * 2
+    partial = pieces * H * (DC + 2) * 4
+    out = B * H * DV * 2
+    split = latent + tables + pieces * H * row * 2 * 2 + partial
+    return {"latent": latent, "split": split,
+            "call": latent + tables + weights + q + 2 * qt + 2 * partial + out + pieces * H * row * 4}
+
+
+def run_mla_decode(args, torch, pkv, workloads):
+    """MLA decode step over a latent paged cache (synthetic DeepSeek-V2-Lite shapes):
+    the batch's new latent rows written with concat_and_cache_mla_k (one 'head'),
+    then pa_mla_decode_attention."""
+    w = workloads.mla_decode_b64()
+    B, H, QK, R, DC, DV = (w["num_seqs"], w["num_heads"], w["qk_nope_dim"], w["rope_dim"],
+                           w["kv_lora_rank"], w["v_dim"])
+    BS, NB, s = w["block_size"], w["num_blocks"], w["seed"]
+    cache = workloads.device_normal((NB, BS, DC + R), torch.bfloat16, "cuda", s)
+    q_nope = workloads.device_normal((B, H, QK), torch.bfloat16, "cuda", s + 1)
+    q_rope = workloads.device_normal((B, H, R), torch.bfloat16, "cuda", s + 2)
+    w_uk = workloads.device_normal((DC, H * QK), torch.bfloat16, "cuda", s + 3, std=w["w_std"])
+    w_uv = workloads.device_normal((DC, H * DV), torch.bfloat16, "cuda", s + 4, std=w["w_std"])
+    new_c = workloads.device_normal((B, 1, DC), torch.bfloat16, "cuda", s + 5)
+    new_r = workloads.device_normal((B, 1, R), torch.bfloat16, "cuda", s + 6)
+    slots = torch.from_numpy(w["new_token_slots"]).cuda()
+    bt = torch.from_numpy(w["block_tables"]).cuda()
+    cl = torch.from_numpy(w["context_lens"]).cuda()
+    out = torch.empty((B, H, DV), dtype=torch.bfloat16, device="cuda")
+    ws = torch.zeros(pkv.mla_decode_workspace_size(B, H, QK, R, DC, DV, bt.shape[1], BS), dtype=torch.uint8,
+                     device="cuda")
+    cache4 = cache.view(NB, BS, 1, DC + R)
+    stream = torch.cuda.current_stream()
+
+    def write():
+        pkv.concat_and_cache_mla_k(new_c, new_r, cache4, slots)
+
+    def attend():
+        pkv.mla_decode_attention(out, q_nope, q_rope, w_uk, w_uv, cache, bt, cl, w["softmax_scale"],
+                                 workspace=ws)
+
+    if args.profile_steps:
+        copy_calibration(torch, pkv)
+        for _ in range(args.profile_steps):
+            write()
+            attend()
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_steps": args.profile_steps, "workload": w["name"]}))
+        return
+    for _ in range(args.warmup):
+        write()
+        attend()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        write()
+        attend()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    ta = Timer(torch, stream)
+    for _ in range(args.steps):
+        ta.start()
+        attend()
+        ta.stop()
+    torch.cuda.synchronize()
+    attn_ms = ta.mean_ms()
+    nb = mla_bytes(w)
+    value = nb["latent"] / (ms * 1e-3) / 1e9
+    achieved = nb["call"] / (attn_ms * 1e-3) / 1e9
+    ctx = w["context_lens"]
+    res = {
+        "metric": "paged decode attn KV-read GB/s & % HBM peak; cache-write GB/s (1 MI355X)",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) latent rows and queries, N(0,1/512) weights)",
+        "config": {"workload": w["name"], "num_seqs": B, "num_heads": H, "qk_nope_dim": QK,
+                   "rope_dim": R, "kv_lora_rank": DC, "v_dim": DV, "block_size": BS,
+                   "num_blocks": NB, "context_lens": f"{int(ctx.min())}..{int(ctx.max())} "
+                                                     f"(sum {int(ctx.sum())})",
+                   "latent_read_bytes_per_step": nb["latent"]},
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
+        "tokens_per_s": round(B / (ms * 1e-3), 1),
+        "attention": {"ms": round(attn_ms, 5), "bytes": nb["call"], "GBps": round(achieved, 2),
+                      "note": "the whole call (absorb + split + merge) on HIP events"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic_from_profiles("mla_decode", w["name"])},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        res["cpu_baseline"] = cpu_baseline_mla(torch, w, oracle, cache, q_nope, q_rope, w_uk, w_uv)
+    print(json.dumps(res))
+
+
+def cpu_baseline_mla(torch, w, oracle, cache, q_nope, q_rope, w_uk, w_uv):
+    """The oracle (K and V written out from the latent, fp64) on four of the
+    batch's sequences; latent-read bytes of those sequences / time."""
+    h16 = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)  # noqa: E731
+    ch, qn, qr, wk, wv = h16(cache), h16(q_nope), h16(q_rope), h16(w_uk), h16(w_uv)
+    pick = np.arange(4)
+    ctx = w["context_lens"][pick]
+    t0 = time.perf_counter()
+    oracle.mla_decode(qn[pick], qr[pick], wk, wv, ch, w["block_tables"][pick], ctx, w["softmax_scale"])
+    dt = time.perf_counter() - t0
+    row = w["kv_lora_rank"] + w["rope_dim"]
+    nbytes = int(ctx.astype(np.int64).sum()) * row * 2
+    return {"value": round(nbytes / dt / 1e9, 5), "unit": "GB/s", "cores": cpu_cores(), "kind": "oracle",
+            "sample": f"sequences 0..3 of the batch ({int(ctx.sum())} cached tokens): fp64 MLA decode with "
+                      f"K/V up-projected per position, {dt:.2f} s, latent-read bytes / time"}
+
+
 def run_decode_fp8(args, torch, pkv, workloads):
     w = workloads.mixed_decode_fp8()
     return run_decode(args, torch, pkv, workloads, w,
@@ -699,6 +827,8 @@ def main():
         run_mla_fused(args, torch, pkv, workloads)
     elif args.workload == "engine_decode_b64":
         run_engine_decode(args, torch, pkv, workloads)
+    elif args.workload == "mla_decode_b64":
+        run_mla_decode(args, torch, pkv, workloads)
     else:
         run_mla(args, torch, pkv, workloads)
 

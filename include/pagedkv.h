@@ -14,6 +14,10 @@
  * and the prefill side of the same cache:
  *   pa_prefill_attention      packed chunks of query tokens per sequence,
  *                             causal, against the same paged K/V
+ * and MLA's latent cache:
+ *   pa_mla_decode_attention   decode over a paged cache of latent rows, with
+ *                             W_UK absorbed into the query and W_UV applied
+ *                             after the softmax
  * and, on the host, the bookkeeping that feeds them:
  *   pa_bm_*                   block manager: allocation in block_size units,
  *                             per-step slot_mapping / block_tables /
@@ -355,6 +359,71 @@ pa_status pa_prefill_attention(void* out, pa_dtype out_dtype, int64_t out_token_
  * Errors: PA_EINVAL, PA_EHIP.
  */
 pa_status pa_hbm_copy(void* dst, const void* src, size_t bytes, void* stream);
+
+/*
+ * pa_mla_decode_workspace_size -- bytes of device workspace
+ * pa_mla_decode_attention needs for these sizes (256-byte aligned); 0 with
+ * pa_last_error() set if the shape is unsupported. Pure function.
+ */
+size_t pa_mla_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t qk_nope_dim,
+                                    int32_t rope_dim, int32_t kv_lora_rank, int32_t v_dim,
+                                    int32_t max_blocks_per_seq, int32_t block_size);
+
+/*
+ * pa_mla_decode_attention -- single-token decode attention of MLA over a
+ * paged cache of latent rows.
+ *
+ * Defined by: "PagedAttention principle" page, MLA paragraphs of the GQA/MLA
+ * shapes section: per token MLA caches the latent c = x W_DKV (kv_lora_rank
+ * values) instead of K and V; head h's key and value are (c W_UK) and (c W_UV)
+ * split per head; the q.k dimension also carries a RoPE part that v lacks.
+ * Each cached row here is c followed by rope_dim values of a RoPE key shared
+ * by all heads (the row pa_concat_and_cache_mla_k writes with num_heads = 1,
+ * nope_dim = kv_lora_rank). For sequence b and head h, over positions p <
+ * context_lens[b] read through block_tables (clamping and table-entry rule as
+ * pa_decode_attention):
+ *   s_p = softmax_scale * (q_nope[b,h] . (c_p W_UK)[h] + q_rope[b,h] . k_r,p)
+ *   out[b,h,:] = sum_p softmax(s)_p (c_p W_UV)[h]
+ * computed with the products re-associated: W_UK is applied to the query
+ * once, the softmax runs over the latent rows, and W_UV is applied to the
+ * weighted latent sum, so each cached row is read once and never expanded.
+ * Internally the absorbed query and the probabilities are carried as bf16
+ * hi + lo pairs on the matrix cores (about 16 bits beyond bf16), everything
+ * else in fp32.
+ *
+ * Arguments
+ *   out      [num_seqs, num_heads, v_dim], sequence stride out_seq_stride;
+ *            out_dtype PA_BF16 or PA_F32.
+ *   q_nope   [num_seqs, num_heads, qk_nope_dim], sequence stride
+ *            q_nope_seq_stride; q_rope [num_seqs, num_heads, rope_dim],
+ *            sequence stride q_rope_seq_stride (unused when rope_dim = 0);
+ *            q_dtype PA_BF16.
+ *   w_uk     [kv_lora_rank, num_heads * qk_nope_dim] row-major (c W_UK gives
+ *            the keys of all heads, head-major); w_uv [kv_lora_rank,
+ *            num_heads * v_dim] likewise; w_dtype PA_BF16; 16-byte aligned.
+ *   latent_cache [num_blocks, block_size, kv_lora_rank + rope_dim], block
+ *            stride block_stride (elements); cache_dtype PA_BF16.
+ *   block_tables, max_blocks_per_seq, context_lens, num_seqs: as
+ *            pa_decode_attention.
+ *   workspace  >= pa_mla_decode_workspace_size(...) bytes, 256-byte aligned;
+ *            contents are scratch.
+ * Supported: num_heads 16 (one tensor-parallel shard of a larger model's
+ *   heads per call), kv_lora_rank 512, rope_dim 0 or 64, qk_nope_dim a
+ *   multiple of 8 up to 256, v_dim = 8 * a divisor of 256.
+ * Errors: PA_EINVAL, PA_EDTYPE, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_EHIP.
+ * num_seqs == 0 is a valid no-op.
+ */
+pa_status pa_mla_decode_attention(void* out, pa_dtype out_dtype, int64_t out_seq_stride,
+                                  const void* q_nope, int64_t q_nope_seq_stride,
+                                  const void* q_rope, int64_t q_rope_seq_stride, pa_dtype q_dtype,
+                                  const void* w_uk, const void* w_uv, pa_dtype w_dtype,
+                                  const void* latent_cache, pa_dtype cache_dtype,
+                                  int64_t num_blocks, int32_t block_size, int64_t block_stride,
+                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, int32_t num_seqs,
+                                  int32_t num_heads, int32_t qk_nope_dim, int32_t rope_dim,
+                                  int32_t kv_lora_rank, int32_t v_dim, float softmax_scale,
+                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Block manager (host side).

@@ -16,6 +16,8 @@ from .ops import (  # noqa: F401
     decode_attention_workspace_size,
     decode_step,
     hbm_copy,
+    mla_decode_attention,
+    mla_decode_workspace_size,
     prefill_attention,
     reshape_and_cache,
 )

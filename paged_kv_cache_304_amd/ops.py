@@ -277,3 +277,57 @@ def hbm_copy(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:
     if dst.numel() * dst.element_size() < n or not (src.is_contiguous() and dst.is_contiguous()):
         raise ValueError("dst must be contiguous and at least as large as src")
     check(lib.pa_hbm_copy(dst.data_ptr(), src.data_ptr(), n, _stream(stream)))
+
+
+def mla_decode_workspace_size(num_seqs: int, num_heads: int, qk_nope_dim: int, rope_dim: int,
+                              kv_lora_rank: int, v_dim: int, max_blocks_per_seq: int,
+                              block_size: int) -> int:
+    n = int(lib.pa_mla_decode_workspace_size(num_seqs, num_heads, qk_nope_dim, rope_dim, kv_lora_rank,
+                                             v_dim, max_blocks_per_seq, block_size))
+    if n == 0:
+        raise _lib.PagedKVError(_lib.PA_EUNSUPPORTED, _lib.last_error())
+    return n
+
+
+def mla_decode_attention(out: torch.Tensor, q_nope: torch.Tensor, q_rope: Optional[torch.Tensor],
+                         w_uk: torch.Tensor, w_uv: torch.Tensor, latent_cache: torch.Tensor,
+                         block_tables: torch.Tensor, context_lens: torch.Tensor, softmax_scale: float,
+                         workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """MLA decode over a paged latent cache [NB, BS, kv_lora_rank + rope_dim]:
+    q_nope [B, H, qk], q_rope [B, H, r] (or None), w_uk [kv_lora_rank, H*qk],
+    w_uv [kv_lora_rank, H*dv]; writes and returns out [B, H, dv]."""
+    _on_gpu(out, q_nope, q_rope, w_uk, w_uv, latent_cache, block_tables, context_lens, workspace)
+    B, H, QK = q_nope.shape
+    NB, BS, ROW = latent_cache.shape
+    R = 0 if q_rope is None else q_rope.shape[2]
+    DC = ROW - R
+    if w_uk.shape != (DC, H * QK) or w_uv.dim() != 2 or w_uv.shape[0] != DC or w_uv.shape[1] % H:
+        raise ValueError("w_uk must be [kv_lora_rank, H*qk] and w_uv [kv_lora_rank, H*dv]")
+    DV = w_uv.shape[1] // H
+    if not (w_uk.is_contiguous() and w_uv.is_contiguous()):
+        raise ValueError("w_uk and w_uv must be contiguous")
+    if out.shape != (B, H, DV) or out.stride(2) != 1 or out.stride(1) != DV:
+        raise ValueError("out must be [B, H, dv] with contiguous [H, dv] rows")
+    if q_nope.stride(2) != 1 or q_nope.stride(1) != QK:
+        raise ValueError("q_nope rows [H, qk] must be contiguous")
+    if q_rope is not None and (q_rope.shape[:2] != (B, H) or q_rope.stride(2) != 1 or q_rope.stride(1) != R):
+        raise ValueError("q_rope must be [B, H, r] with contiguous [H, r] rows")
+    if latent_cache.stride(2) != 1 or latent_cache.stride(1) != ROW:
+        raise ValueError("latent_cache inner [BS, row] must be contiguous")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or \
+            block_tables.shape[0] != B or not block_tables.is_contiguous():
+        raise ValueError("block_tables must be contiguous int32 [B, W]")
+    if context_lens.dtype != torch.int32 or context_lens.numel() != B or not context_lens.is_contiguous():
+        raise ValueError("context_lens must be contiguous int32 [B]")
+    W = block_tables.shape[1]
+    if workspace is None:
+        workspace = torch.empty(mla_decode_workspace_size(max(B, 1), H, QK, R, DC, DV, W, BS),
+                                dtype=torch.uint8, device=q_nope.device)
+    check(lib.pa_mla_decode_attention(
+        out.data_ptr(), _code(out, "out"), out.stride(0), q_nope.data_ptr(), q_nope.stride(0),
+        _ptr(q_rope), q_rope.stride(0) if q_rope is not None else 0, _code(q_nope, "q_nope"),
+        w_uk.data_ptr(), w_uv.data_ptr(), _code(w_uk, "w_uk"), latent_cache.data_ptr(),
+        _code(latent_cache, "latent_cache"), NB, BS, latent_cache.stride(0), block_tables.data_ptr(), W,
+        context_lens.data_ptr(), B, H, QK, R, DC, DV, float(softmax_scale), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out

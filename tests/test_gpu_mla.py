@@ -1,0 +1,199 @@
+"""GPU parity of MLA decode over a latent paged cache (absorbed weights on the
+GPU) against the oracle, which writes K and V out from the latent as the page
+defines them (reading R13).
+
+Tolerance: the decode bound 2e-3 + 2e-3*|o| (fp32 outputs; bf16 outputs get
+half a bf16 ulp more). The GPU's extra steps stay far inside it: the absorbed
+query and the probabilities enter the matrix cores as bf16 hi + lo pairs (each
+within 2^-17 relative of the fp32 value), every product is exact in fp32 and
+the sums run in fp32 over at most 576 terms per step.
+
+Cases: ragged contexts around the 32-position tile and the 256-position piece,
+with and without a RoPE part, block sizes 1, 16, 48, 64, other qk / v widths,
+empty contexts, bad table entries and clamped lengths, NaN in every slot no
+sequence owns, bit-identical output under block relabelling, the full batch-64
+workload on sampled sequences, and a decode step whose latent rows are first
+written by concat_and_cache_mla_k."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity_util import assert_attention_close, say, to_dev, to_host, widen_out
+
+pytestmark = pytest.mark.gpu
+
+BF16, F32 = oracle.BF16, oracle.F32
+NAN_BF16 = 0x7FC0
+H, DC = 16, 512
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def pkv():
+    import paged_kv_cache_304_amd as m
+    return m
+
+
+def weight_bits(rng, shape):
+    return workloads.normal_bf16_bits(rng, shape, std=1.0 / np.sqrt(DC))
+
+
+def make_case(seed, ctx, R=64, QK=128, DV=128, bs=16, spare=4, width=None):
+    rng = np.random.default_rng(seed)
+    ctx = np.asarray(ctx, dtype=np.int32)
+    nblk = [-(-int(c) // bs) for c in ctx]
+    nb = sum(nblk) + spare
+    W = width or max(max(nblk), 1)
+    bt = workloads.deal_block_tables(rng.permutation(nb).astype(np.int32), ctx, bs, W)
+    cache = workloads.normal_bf16_bits(rng, (nb, bs, DC + R))
+    owned = np.zeros((nb, bs), dtype=bool)
+    for b, c in enumerate(ctx):
+        pos = np.arange(int(c))
+        owned[bt[b, pos // bs], pos % bs] = True
+    cache[~owned] = NAN_BF16
+    return dict(ctx=ctx, bt=bt, cache=cache, R=R, QK=QK, DV=DV,
+                q_nope=workloads.normal_bf16_bits(rng, (len(ctx), H, QK)),
+                q_rope=workloads.normal_bf16_bits(rng, (len(ctx), H, R)) if R else None,
+                w_uk=weight_bits(rng, (DC, H * QK)), w_uv=weight_bits(rng, (DC, H * DV)),
+                scale=float(np.float32(1.0 / np.sqrt(QK + R))))
+
+
+def gpu_mla(c, out_dt=F32, **over):
+    m = pkv()
+    c = dict(c, **over)
+    B = len(c["ctx"])
+    out = torch.full((B, H, c["DV"]), float("nan"), device="cuda",
+                     dtype=torch.float32 if out_dt == F32 else torch.bfloat16)
+    m.mla_decode_attention(out, to_dev(c["q_nope"], BF16),
+                           None if c["q_rope"] is None else to_dev(c["q_rope"], BF16),
+                           to_dev(c["w_uk"], BF16), to_dev(c["w_uv"], BF16), to_dev(c["cache"], BF16),
+                           torch.from_numpy(c["bt"]).cuda(), torch.from_numpy(c["ctx"]).cuda(), c["scale"])
+    torch.cuda.synchronize()
+    return widen_out(out)
+
+
+def oracle_mla(c, **over):
+    c = dict(c, **over)
+    return oracle.mla_decode(c["q_nope"], c["q_rope"], c["w_uk"], c["w_uv"], c["cache"], c["bt"], c["ctx"],
+                             c["scale"])
+
+
+CASES = [
+    # name, ctx, rope, qk, v, block size
+    ("R64 ragged around tiles and pieces", [1, 31, 32, 33, 255, 256, 257, 700, 0], 64, 128, 128, 16),
+    ("no RoPE part", [5, 300, 64], 0, 128, 128, 16),
+    ("bs64 qk64 v64", [100, 513], 64, 64, 64, 64),
+    ("bs1", [17, 300], 64, 128, 128, 1),
+    ("bs48", [250, 49, 97], 64, 128, 128, 48),
+    ("qk256 v256", [90, 260], 64, 256, 256, 16),
+    ("qk32 v32 no RoPE", [40], 0, 32, 32, 16),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_mla_matches_oracle(case):
+    name, ctx, R, QK, DV, bs = case
+    say(f"mla_decode {name} ctx={ctx} R={R} qk={QK} v={DV} bs={bs}")
+    c = make_case(zlib.crc32(name.encode()), ctx, R, QK, DV, bs)
+    ref = oracle_mla(c)
+    for out_dt in (F32, BF16):
+        got = gpu_mla(c, out_dt)
+        assert_attention_close(got, ref, f"{name} out={'f32' if out_dt == F32 else 'bf16'}",
+                               out_bf16=out_dt == BF16)
+
+
+def test_bad_table_entries_and_clamped_lengths():
+    say("mla_decode bad table entries")
+    c = make_case(91, [90, 64, 48], width=6)
+    bt = c["bt"].copy()
+    nb = c["cache"].shape[0]
+    bt[0, 2] = nb + 3
+    bt[1, 0] = -7
+    ctx = np.array([90, 64, 9999], dtype=np.int32)   # sequence 2 clamped to 96 positions
+    bt[2, 3:] = nb + 100
+    ref = oracle_mla(c, bt=bt, ctx=ctx)
+    assert_attention_close(gpu_mla(c, bt=bt, ctx=ctx), ref, "bad entries", out_bf16=False)
+
+
+def test_block_relabelling_is_bit_identical():
+    say("mla_decode block relabelling")
+    c = make_case(33, [300, 1234, 64], spare=20)
+    a = gpu_mla(c)
+    perm = np.random.default_rng(1).permutation(c["cache"].shape[0])
+    cache2 = np.empty_like(c["cache"])
+    cache2[perm] = c["cache"]
+    bt2 = np.where(c["bt"] >= 0, perm[np.maximum(c["bt"], 0)], -1).astype(np.int32)
+    b = gpu_mla(c, cache=cache2, bt=bt2)
+    assert np.array_equal(a, b)
+
+
+def full_size_tensors(w):
+    B, R, DCR = w["num_seqs"], w["rope_dim"], w["kv_lora_rank"] + w["rope_dim"]
+    s = w["seed"]
+    cache = workloads.device_normal((w["num_blocks"], w["block_size"], DCR), torch.bfloat16, "cuda", s)
+    q_nope = workloads.device_normal((B, H, w["qk_nope_dim"]), torch.bfloat16, "cuda", s + 1)
+    q_rope = workloads.device_normal((B, H, R), torch.bfloat16, "cuda", s + 2)
+    w_uk = workloads.device_normal((DC, H * w["qk_nope_dim"]), torch.bfloat16, "cuda", s + 3, std=w["w_std"])
+    w_uv = workloads.device_normal((DC, H * w["v_dim"]), torch.bfloat16, "cuda", s + 4, std=w["w_std"])
+    return cache, q_nope, q_rope, w_uk, w_uv
+
+
+def test_full_size_mla_batch_sampled():
+    """The batch-64 MLA workload in the launch the benchmark times; two
+    sequences (the shortest and the longest) against the oracle."""
+    m = pkv()
+    w = workloads.mla_decode_b64()
+    say(f"mla_decode full size {w['name']}")
+    cache, q_nope, q_rope, w_uk, w_uv = full_size_tensors(w)
+    out = torch.empty((w["num_seqs"], H, w["v_dim"]), dtype=torch.bfloat16, device="cuda")
+    m.mla_decode_attention(out, q_nope, q_rope, w_uk, w_uv, cache, torch.from_numpy(w["block_tables"]).cuda(),
+                           torch.from_numpy(w["context_lens"]).cuda(), w["softmax_scale"])
+    torch.cuda.synchronize()
+    got = widen_out(out)
+    ch = to_host(cache, BF16)
+    args = [to_host(t, BF16) for t in (q_nope, q_rope, w_uk, w_uv)]
+    ctx = w["context_lens"]
+    for b in (int(np.argmin(ctx)), int(np.argmax(ctx))):
+        ref = oracle.mla_decode(args[0][b:b + 1], args[1][b:b + 1], args[2], args[3], ch,
+                                w["block_tables"][b:b + 1], ctx[b:b + 1], w["softmax_scale"])
+        assert_attention_close(got[b:b + 1], ref, f"{w['name']} sequence {b} (ctx {ctx[b]})", out_bf16=True)
+
+
+def test_mla_decode_step_writes_latent_rows_then_attends():
+    """The new token's latent row (c ++ k_rope, one 'head') goes into the cache
+    with concat_and_cache_mla_k, then MLA decode reads it back: the cache
+    bit-exact against the oracle's concat + write, the output against the
+    oracle's MLA decode on that cache."""
+    m = pkv()
+    say("mla decode step")
+    c = make_case(4242, [40, 1, 300, 17])
+    rng = np.random.default_rng(7)
+    B, R, QK = len(c["ctx"]), c["R"], c["QK"]
+    bs = c["cache"].shape[1]
+    new_c = workloads.normal_bf16_bits(rng, (B, 1, DC))
+    new_r = workloads.normal_bf16_bits(rng, (B, 1, R))
+    pos = c["ctx"].astype(np.int64) - 1
+    slots = workloads.slots_for_positions(c["bt"], np.arange(B), pos, bs)
+    cache = c["cache"].copy()
+    for b in range(B):                       # the new positions hold NaN until written
+        cache[slots[b] // bs, slots[b] % bs] = NAN_BF16
+    ocache = cache.copy()
+    k = np.zeros((B, 1, DC + R), dtype=np.float32)
+    oracle.concat_and_cast(k, oracle.F32, new_c, BF16, new_r, BF16)
+    oracle.reshape_and_cache(k, None, oracle.F32, ocache.reshape(-1, bs, 1, DC + R), None, BF16, slots)
+    ref = oracle_mla(c, cache=ocache)
+    dcache = to_dev(cache, BF16)
+    m.concat_and_cache_mla_k(to_dev(new_c, BF16), to_dev(new_r, BF16), dcache.view(-1, bs, 1, DC + R),
+                             torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(dcache, BF16), ocache), "latent cache"
+    got = gpu_mla(c, cache=to_host(dcache, BF16))
+    assert_attention_close(got, ref, "mla step", out_bf16=False)

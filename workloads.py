@@ -253,3 +253,23 @@ def prefill_chunks(num_seqs: int = 16, chunk: int = 512, prefix_hi: int = 3584,
                 context_lens=ctx, block_tables=bt, cu_seqlens_q=cu,
                 softmax_scale=float(np.float32(1.0 / np.sqrt(head_size))),
                 seed=torch_seed(rng))
+
+
+def mla_decode_b64(num_seqs: int = 64, ctx_lo: int = 512, ctx_hi: int = 4096,
+                   num_blocks: int = 32768, width: int = 256, workload_id: int = 7) -> dict:
+    """MLA decode over a latent paged cache, DeepSeek-V2-Lite-shaped (synthetic):
+    16 heads, qk_nope 128, RoPE 64, kv_lora_rank 512, v 128, block_size 16, batch 64
+    with ctx ~ U{512..4096} (the GQA decode workload's length mix). Weights are
+    N(0, 1/512) so that up-projected keys and values have unit scale."""
+    rng = rng_for(workload_id)
+    ctx = rng.integers(ctx_lo, ctx_hi + 1, size=num_seqs).astype(np.int32)
+    bs = 16
+    perm = rng.permutation(num_blocks).astype(np.int32)
+    bt = deal_block_tables(perm, ctx, bs, width)
+    H, QK, R, DC, DV = 16, 128, 64, 512, 128
+    new_slots = slots_for_positions(bt, np.arange(num_seqs), ctx.astype(np.int64) - 1, bs)
+    return dict(name="mla_latent_decode_b64", num_seqs=num_seqs, num_heads=H, qk_nope_dim=QK,
+                rope_dim=R, kv_lora_rank=DC, v_dim=DV, block_size=bs, num_blocks=num_blocks,
+                context_lens=ctx, block_tables=bt, new_token_slots=new_slots,
+                softmax_scale=float(np.float32(1.0 / math.sqrt(QK + R))), w_std=1.0 / math.sqrt(DC),
+                seed=torch_seed(rng))
