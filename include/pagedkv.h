@@ -395,7 +395,7 @@ size_t pa_mla_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t
  *   out      [num_seqs, num_heads, v_dim], sequence stride out_seq_stride;
  *            out_dtype PA_BF16 or PA_F32.
  *   q_nope   [num_seqs, num_heads, qk_nope_dim], sequence stride
- *            q_nope_seq_stride; q_rope [num_seqs, num_heads, rope_dim],
+ *            q_nope_seq_stride, 16-byte aligned per sequence; q_rope [num_seqs, num_heads, rope_dim],
  *            sequence stride q_rope_seq_stride (unused when rope_dim = 0);
  *            q_dtype PA_BF16.
  *   w_uk     [kv_lora_rank, num_heads * qk_nope_dim] row-major (c W_UK gives

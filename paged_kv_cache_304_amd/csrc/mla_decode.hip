@@ -15,16 +15,19 @@
 // rows themselves, and the cache is read once.
 //
 // Three kernels:
-//  * absorb: q~ = scale*log2(e) * [W_UK,h^T q_nope,h ; q_rope,h] in fp32, split
-//    into bf16 hi + lo (x - hi rounded again), so that the matrix-core products
-//    below keep ~16 more bits than a bf16 q~ would.
-//  * split: one workgroup per (sequence, 256-position piece), 4 waves, tiles of
-//    32 positions staged in LDS. Scores S^T = C q~^T on v_mfma_f32_16x16x32_bf16
-//    (hi and lo, the four waves each take a 16-position block and half of the
-//    576 dims, partial sums meet in LDS); online softmax in the log2 domain;
-//    O += P C with P split into hi + lo as well and C's operand from LDS by
-//    transposing reads, each wave owning 128 of the 512 latent dims. Writes
-//    the unnormalised O, its running max and sum per head.
+//  * absorb: q~ = scale*log2(e) * [W_UK,h^T q_nope,h ; q_rope,h], a small
+//    matrix-core GEMM per head accumulated in fp32, then split into bf16
+//    hi + lo (x - hi rounded again), so that the products below keep ~16 more
+//    bits than a bf16 q~ would.
+//  * split: one workgroup per live (sequence, 256-position piece) -- found by
+//    a scan of the sequences' piece counts, so the grid holds no idle runs --,
+//    4 waves, tiles of 32 positions staged in LDS (three workgroups per CU).
+//    Scores S^T = C q~^T on v_mfma_f32_16x16x32_bf16 (hi and lo; each wave
+//    takes a quarter of the 576-dim contraction with its q~ operands held in
+//    registers, and the partial sums meet in LDS); online softmax in the log2
+//    domain; O += P C with P split into hi + lo as well and C's operand from
+//    LDS by transposing reads, each wave owning 128 of the 512 latent dims.
+//    Writes the unnormalised O, its running max and sum per head.
 //  * merge: combines the pieces of a sequence and applies W_UV per head.
 #include <math.h>
 
@@ -52,10 +55,9 @@ struct MlaGeo {
   static constexpr int RS = RB + kPad;           // LDS row stride
   static constexpr int KSTEPS = ROW / 32;        // MFMA steps over the row
   static constexpr int HALF = KSTEPS / 2;        // steps per wave pair
-  static constexpr int CHUNKS = kTile * RB / 16; // 16-byte pieces per tile
-  static constexpr int LOADS = CHUNKS / (64 * kWaves);
-  static_assert(KSTEPS % 2 == 0, "two halves of the contraction");
-  static_assert(CHUNKS % (64 * kWaves) == 0, "loads per thread");
+  static constexpr int LOADS = RB / 128;          // 16-byte loads per thread and tile:
+                                                  // 8 threads per row, 32 rows
+  static_assert(RB % 128 == 0 && kTile * 8 == 64 * kWaves, "row-per-8-threads tile loads");
 };
 
 struct MlaArgs {
@@ -92,57 +94,66 @@ __device__ __forceinline__ void split_hi_lo(float x, uint16_t& hi, uint16_t& lo)
 }
 
 // ---------------------------------------------------------------- absorb
-// grid (16 heads, ceil(B / 8)); thread t owns latent dims t and t + 256 for
-// the 8 sequences of its workgroup.
+// q~^T [512 c x B] = W_UK,h [512 x qk] q_h^T [qk x B] per head on the matrix
+// cores (bf16 x bf16 products are exact in fp32, sums in fp32). grid (16
+// heads, 8 blocks of 64 latent dims, ceil(B / 16)); wave w computes latent
+// dims 64 cb + 16 w .. +15 for 16 sequences. The A operand is 16 bytes of a
+// W_UK row (dims 8 (l/16) .. of row l%16), the B operand 16 bytes of a q row.
 __global__ __launch_bounds__(256) void mla_absorb_kernel(MlaArgs a, int row) {
-  const int h = blockIdx.x, b0 = 8 * blockIdx.y, tid = threadIdx.x;
-  __shared__ float qs[8][256];
-  const int nb = min(8, a.num_seqs - b0);
-  for (int i = tid; i < 8 * a.qk; i += 256) {
-    const int bb = i / a.qk, j = i % a.qk;
-    qs[bb][j] = bb < nb ? load1<Ty::BF16>(a.q_nope, (int64_t)(b0 + bb) * a.qn_seq_stride + (int64_t)h * a.qk + j)
-                        : 0.0f;
+  const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const int c0 = 64 * blockIdx.y + 16 * wave, b0 = 16 * blockIdx.z;
+  const int bq = b0 + li;                         // this lane's sequence in the B operand
+  const bool bq_ok = bq < a.num_seqs;
+  const uint16_t* wr = static_cast<const uint16_t*>(a.w_uk) + (int64_t)(c0 + li) * kHeads * a.qk + (int64_t)h * a.qk;
+  const uint16_t* qr = static_cast<const uint16_t*>(a.q_nope) + (int64_t)(bq_ok ? bq : 0) * a.qn_seq_stride +
+                       (int64_t)h * a.qk;
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  constexpr int kMaxSteps = 256 / 32;             // qk <= 256: every load issued before the products
+  u32x4 wa[kMaxSteps], qb[kMaxSteps];
+#pragma unroll
+  for (int s = 0; s < kMaxSteps; ++s) {
+    const int j = 32 * s + 8 * lg;
+    const int jc = j < a.qk ? j : 0;              // qk is a multiple of 8, not always of 32
+    wa[s] = *reinterpret_cast<const u32x4*>(wr + jc);
+    qb[s] = *reinterpret_cast<const u32x4*>(qr + jc);
   }
-  __syncthreads();
-  float acc[2][8];
 #pragma unroll
-  for (int k = 0; k < 2; ++k)
-#pragma unroll
-    for (int bb = 0; bb < 8; ++bb) acc[k][bb] = 0.0f;
-  const int64_t wrow = (int64_t)kHeads * a.qk;  // W_UK row length
-  for (int j = 0; j < a.qk; j += 8) {
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int c = tid + 256 * k;
-      const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.w_uk) + c * wrow +
-                                                        (int64_t)h * a.qk + j);
-      float wf[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        wf[2 * e] = bf16_lo(w[e]);
-        wf[2 * e + 1] = bf16_hi(w[e]);
-      }
-#pragma unroll
-      for (int bb = 0; bb < 8; ++bb)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[k][bb] = fmaf(wf[e], qs[bb][j + e], acc[k][bb]);
-    }
+  for (int s = 0; s < kMaxSteps; ++s) {
+    const bool in = 32 * s + 8 * lg < a.qk;
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, in ? wa[s] : z),
+                                                  __builtin_bit_cast(bf16x8, (in && bq_ok) ? qb[s] : z), acc, 0,
+                                                  0, 0);
   }
-  for (int bb = 0; bb < nb; ++bb) {
-    const int64_t base = ((int64_t)(b0 + bb) * kHeads + h) * row;
+  // lane l holds latent dims c0 + 4 (l/16) + r of sequence b0 + l%16
+  if (bq_ok) {  // four consecutive dims: one 8-byte store each for hi and lo
+    const int64_t base = ((int64_t)bq * kHeads + h) * row + c0 + 4 * lg;
+    uint16_t hi[4], lo[4];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      uint16_t hi, lo;
-      split_hi_lo(acc[k][bb] * a.scale_log2, hi, lo);
-      a.q_hi[base + tid + 256 * k] = hi;
-      a.q_lo[base + tid + 256 * k] = lo;
+    for (int r = 0; r < 4; ++r) split_hi_lo(acc[r] * a.scale_log2, hi[r], lo[r]);
+    *reinterpret_cast<u32x2*>(a.q_hi + base) = u32x2{hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16)};
+    *reinterpret_cast<u32x2*>(a.q_lo + base) = u32x2{lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16)};
+  }
+  if (blockIdx.y == 0) {  // the RoPE part: scaled and split as it is (16 * dr <= 1024 values)
+    float x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = tid + 256 * u;
+      const int bb = b0 + i / (a.dr > 0 ? a.dr : 1), r = i % (a.dr > 0 ? a.dr : 1);
+      const bool ok = i < 16 * a.dr && bb < a.num_seqs;
+      x[u] = ok ? load1<Ty::BF16>(a.q_rope, (int64_t)bb * a.qr_seq_stride + (int64_t)h * a.dr + r) : 0.0f;
     }
-    if (tid < a.dr) {
-      const float x = load1<Ty::BF16>(a.q_rope, (int64_t)(b0 + bb) * a.qr_seq_stride + (int64_t)h * a.dr + tid);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = tid + 256 * u;
+      const int bb = b0 + i / (a.dr > 0 ? a.dr : 1), r = i % (a.dr > 0 ? a.dr : 1);
+      if (!(i < 16 * a.dr && bb < a.num_seqs)) continue;
       uint16_t hi, lo;
-      split_hi_lo(x * a.scale_log2, hi, lo);
-      a.q_hi[base + kDC + tid] = hi;
-      a.q_lo[base + kDC + tid] = lo;
+      split_hi_lo(x[u] * a.scale_log2, hi, lo);
+      const int64_t base = ((int64_t)bb * kHeads + h) * row + kDC;
+      a.q_hi[base + r] = hi;
+      a.q_lo[base + r] = lo;
     }
   }
 }
@@ -156,81 +167,136 @@ __device__ __forceinline__ float bcast_lane(float x, int src) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(x)));
 }
 
+__device__ __forceinline__ int pieces_of(const MlaArgs& a, int b) { return (clamp_ctx(a, b) + kSplit - 1) / kSplit; }
+
+// Workgroup L serves the L-th live piece in (sequence, piece) order: wave 0
+// scans the sequences' piece counts (each lane a run of sequences) and finds
+// it. Returns false when L is past the last piece.
+__device__ bool find_piece(const MlaArgs& a, int L, int lane, int& b_out, int& s_out) {
+  const int per = (a.num_seqs + 63) / 64;
+  const int lo = min(a.num_seqs, lane * per), hi = min(a.num_seqs, lo + per);
+  int mine = 0;
+  for (int b = lo; b < hi; ++b) mine += pieces_of(a, b);
+  int incl = mine;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, (unsigned)o, 64);
+    if (lane >= o) incl += y;
+  }
+  const uint64_t past = __builtin_amdgcn_ballot_w64(incl <= L);  // lanes wholly before L
+  const int owner = __builtin_popcountll(past);
+  if (owner >= 64) return false;
+  int found_b = -1, found_s = 0;
+  if (lane == owner) {
+    int run = incl - mine;
+    for (int b = lo; b < hi; ++b) {
+      const int n = pieces_of(a, b);
+      if (L < run + n) {
+        found_b = b;
+        found_s = L - run;
+        break;
+      }
+      run += n;
+    }
+  }
+  b_out = __shfl(found_b, owner, 64);
+  s_out = __shfl(found_s, owner, 64);
+  return b_out >= 0;
+}
+
 template <int DR>
-__global__ __launch_bounds__(64 * kWaves) void mla_split_kernel(MlaArgs a) {
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3, 3))) void mla_split_kernel(MlaArgs a) {
   using Gm = MlaGeo<DR>;
-  constexpr int ROW = Gm::ROW, RB = Gm::RB, RS = Gm::RS, HALF = Gm::HALF, LOADS = Gm::LOADS;
+  constexpr int ROW = Gm::ROW, RS = Gm::RS, LOADS = Gm::LOADS;
+  constexpr int KSTEPS = ROW / 32, QMAX = (KSTEPS + kWaves - 1) / kWaves;
   const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, lg = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // XCD-aware order: workgroup L runs item (L mod 8) * per_xcd + L / 8, so the
-  // pieces of one sequence (which share its q~) run on the same XCD.
-  const int total = a.num_seqs * a.splits;
-  const int per_xcd = (int)(((int64_t)gridDim.x + 7) / 8);
-  const int item = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
-  if (item >= total) return;
-  const int b = item / a.splits, sp = item % a.splits;
+  __shared__ __attribute__((aligned(16))) char tile_lds[kTile * RS];
+  __shared__ f32x4 sx[kWaves][2][64];
+  __shared__ int64_t rowoff[kSplit];  // byte offset of each position's row; -1: none
+  __shared__ int which[2];
+
+  if (wave == 0) {
+    int b, s;
+    const bool ok = find_piece(a, (int)blockIdx.x, lane, b, s);
+    if (lane == 0) {
+      which[0] = ok ? b : -1;
+      which[1] = s;
+    }
+  }
+  __syncthreads();
+  const int b = which[0], sp = which[1];
+  if (b < 0) return;  // uniform: past the last live piece
   const int ctx = clamp_ctx(a, b);
   const int p0 = sp * kSplit;
-  if (p0 >= ctx) return;  // uniform: this piece is past the context
   const int p1 = min(ctx, p0 + kSplit);
   const int ntiles = (p1 - p0 + kTile - 1) / kTile;
-
-  __shared__ __attribute__((aligned(16))) char tile_lds[kTile * RS];
-  __shared__ __attribute__((aligned(16))) char qhi_lds[kHeads * RS];
-  __shared__ __attribute__((aligned(16))) char qlo_lds[kHeads * RS];
-  __shared__ f32x4 sx[kWaves][64];
-  __shared__ int tab[kSplit + 1];
-
-  const int bs = a.block_size;
-  const int j0 = p0 / bs, nblk = (p1 - 1) / bs - j0 + 1;
-  for (int i = tid; i < nblk; i += 64 * kWaves) {
-    const int e = a.bt[(int64_t)b * a.W + j0 + i];
-    tab[i] = (e >= 0 && (int64_t)e < a.num_blocks) ? e : -1;
+  const int64_t piece = (int64_t)b * a.splits + sp;
+  if (a.num_blocks == 0) {  // uniform: an empty pool -- no position takes part
+    if (tid < kHeads) {
+      a.ws_m[piece * kHeads + tid] = -INFINITY;
+      a.ws_l[piece * kHeads + tid] = 0.0f;
+    }
+    return;
   }
+
+  // where each position's row lives (the only division by block_size)
+  const int bs = a.block_size;
+  for (int i = tid; i < kSplit; i += 64 * kWaves) {
+    const int pos = p0 + i;
+    int64_t off = -1;
+    if (pos < p1) {
+      const int e = a.bt[(int64_t)b * a.W + pos / bs];
+      if (e >= 0 && (int64_t)e < a.num_blocks) off = ((int64_t)e * a.block_stride + (int64_t)(pos % bs) * ROW) * 2;
+    }
+    rowoff[i] = off;
+  }
+
+  // This wave's share of the score contraction: steps s0 .. s0 + nst - 1 of
+  // KSTEPS (32 dims each); its q~ operands (head li, dims 32 s + 8 lg ..) stay
+  // in registers for the whole piece.
+  const int base_n = KSTEPS / kWaves, rem = KSTEPS % kWaves;
+  const int nst = base_n + (wave < rem ? 1 : 0);
+  const int s0 = wave * base_n + min(wave, rem);
+  bf16x8 qh[QMAX], ql[QMAX];
   {
-    const char* qh = reinterpret_cast<const char*>(a.q_hi + (int64_t)b * kHeads * ROW);
-    const char* ql = reinterpret_cast<const char*>(a.q_lo + (int64_t)b * kHeads * ROW);
-    for (int q = tid; q < kHeads * RB / 16; q += 64 * kWaves) {
-      const int hh = q / (RB / 16), c16 = q % (RB / 16);
-      *reinterpret_cast<u32x4*>(qhi_lds + hh * RS + 16 * c16) = *reinterpret_cast<const u32x4*>(qh + 16 * q);
-      *reinterpret_cast<u32x4*>(qlo_lds + hh * RS + 16 * c16) = *reinterpret_cast<const u32x4*>(ql + 16 * q);
+    const uint16_t* qhb = a.q_hi + ((int64_t)b * kHeads + li) * ROW;
+    const uint16_t* qlb = a.q_lo + ((int64_t)b * kHeads + li) * ROW;
+#pragma unroll
+    for (int i = 0; i < QMAX; ++i) {
+      const int k0 = 32 * (s0 + (i < nst ? i : 0)) + 8 * lg;
+      qh[i] = *reinterpret_cast<const bf16x8*>(qhb + k0);
+      ql[i] = *reinterpret_cast<const bf16x8*>(qlb + k0);
     }
   }
   __syncthreads();
 
-  // Tile loads: thread chunk i covers row (i*256 + tid) / (RB/16), 16 bytes at
-  // column (i*256 + tid) % (RB/16); rows past the piece or with a bad table
-  // entry are zeros (their scores are -inf, and 0 * 0 keeps P V finite).
-  const char* cache = static_cast<const char*>(a.cache);
+  // Tile loads: thread t loads row t / 8 of the tile, 16 bytes at columns
+  // 16 (t % 8) + 128 i -- one row offset per thread and tile, immediate
+  // offsets after it. Every thread loads (a row past the piece or with a bad
+  // table entry reads the pool's first row instead) and such rows are zeroed
+  // when stored to LDS: a load under a divergent branch would make the
+  // compiler wait for it before the other branch writes the register. Their
+  // scores are -inf, and 0 * 0 keeps P V finite.
+  const char* cache = static_cast<const char*>(a.cache) + 16 * (tid & 7);
+  const int lrow = tid >> 3;
+  char* const lds_dst = tile_lds + lrow * RS + 16 * (tid & 7);
   u32x4 pre[LOADS];
+  bool row_ok = false;
   auto load_tile = [&](int t) {
+    const int64_t ro = rowoff[kTile * t + lrow];
+    row_ok = ro >= 0;
+    const char* src = cache + (row_ok ? ro : 0);
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int q = i * 64 * kWaves + tid;
-      const int r = q / (RB / 16), c16 = q % (RB / 16);
-      const int pos = p0 + kTile * t + r;
-      int phys = -1;
-      if (pos < p1) phys = tab[pos / bs - j0];
-      if (phys >= 0) {
-        const char* src = cache + ((int64_t)phys * a.block_stride + (int64_t)(pos % bs) * ROW) * 2 + 16 * c16;
-        pre[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
-      } else {
-        pre[i] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
+    for (int i = 0; i < LOADS; ++i) pre[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + 128 * i));
   };
   auto store_tile = [&]() {
+    const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int q = i * 64 * kWaves + tid;
-      const int r = q / (RB / 16), c16 = q % (RB / 16);
-      *reinterpret_cast<u32x4*>(tile_lds + r * RS + 16 * c16) = pre[i];
-    }
+    for (int i = 0; i < LOADS; ++i) *reinterpret_cast<u32x4*>(lds_dst + 128 * i) = row_ok ? pre[i] : z;
   };
 
-  // Score half of this wave: position block pb, contraction steps hs*HALF ..
-  const int pb = wave & 1, hs = wave >> 1;
   const int dim0 = 128 * wave;  // this wave's 128 latent dims of O
   float m_run = -INFINITY, l_run = 0.0f;
   f32x4 acc[8];
@@ -244,35 +310,38 @@ __global__ __launch_bounds__(64 * kWaves) void mla_split_kernel(MlaArgs a) {
     lds_barrier();
     if (t + 1 < ntiles) load_tile(t + 1);
 
-    // S^T partial: rows = positions 16 pb + 4 lg + r, column = head li
-    f32x4 sp4 = {0.0f, 0.0f, 0.0f, 0.0f};
+    // partial S^T of both 16-position blocks over this wave's contraction
+    // steps: rows = positions 16 pb + 4 lg + r, column = head li
+    f32x4 spb[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
-    for (int s = 0; s < HALF; ++s) {
-      const int k0 = 32 * (hs * HALF + s) + 8 * lg;  // first dim of this lane's 8
-      const bf16x8 cop = *reinterpret_cast<const bf16x8*>(tile_lds + (16 * pb + li) * RS + 2 * k0);
-      const bf16x8 qh = *reinterpret_cast<const bf16x8*>(qhi_lds + li * RS + 2 * k0);
-      const bf16x8 ql = *reinterpret_cast<const bf16x8*>(qlo_lds + li * RS + 2 * k0);
-      sp4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cop, qh, sp4, 0, 0, 0);
-      sp4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cop, ql, sp4, 0, 0, 0);
-    }
-    sx[wave][lane] = sp4;
-    lds_barrier();
-    // full scores of this lane's head li at positions 4 lg + r (block 0) and
-    // 16 + 4 lg + r (block 1); every wave forms them the same way
-    float sc[8];
-    {
-      const f32x4 a0 = sx[0][lane], a1 = sx[1][lane], a2 = sx[2][lane], a3 = sx[3][lane];
+    for (int i = 0; i < QMAX; ++i) {
+      if (i < nst) {
+        const int k0 = 32 * (s0 + i) + 8 * lg;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        sc[r] = a0[r] + a2[r];
-        sc[4 + r] = a1[r] + a3[r];
+        for (int pb = 0; pb < 2; ++pb) {
+          const bf16x8 cop = *reinterpret_cast<const bf16x8*>(tile_lds + (16 * pb + li) * RS + 2 * k0);
+          spb[pb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cop, qh[i], spb[pb], 0, 0, 0);
+          spb[pb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cop, ql[i], spb[pb], 0, 0, 0);
+        }
       }
     }
-    const int base = p0 + kTile * t;
+    sx[wave][0][lane] = spb[0];
+    sx[wave][1][lane] = spb[1];
+    lds_barrier();
+    // full scores of head li at positions 4 lg + r (block 0) and 16 + 4 lg + r
+    // (block 1), summed over the waves in one fixed order
+    float sc[8];
+#pragma unroll
+    for (int pb = 0; pb < 2; ++pb) {
+      f32x4 s4 = sx[0][pb][lane];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) s4 += sx[w][pb][lane];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sc[4 * pb + r] = s4[r];
+    }
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const int pos = base + 16 * (k >> 2) + 4 * lg + (k & 3);
-      const bool ok = pos < p1 && tab[pos / bs - j0] >= 0;
+      const bool ok = rowoff[kTile * t + 16 * (k >> 2) + 4 * lg + (k & 3)] >= 0;  // -1 past p1 too
       sc[k] = ok ? sc[k] : -INFINITY;
     }
     float mx = sc[0];
@@ -331,7 +400,6 @@ __global__ __launch_bounds__(64 * kWaves) void mla_split_kernel(MlaArgs a) {
   // the four lane groups saw different positions under one running max
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
-  const int64_t piece = (int64_t)b * a.splits + sp;
   if (wave == 0 && lane < kHeads) {
     a.ws_m[piece * kHeads + lane] = m_run;
     a.ws_l[piece * kHeads + lane] = l_run;
@@ -344,22 +412,22 @@ __global__ __launch_bounds__(64 * kWaves) void mla_split_kernel(MlaArgs a) {
 }
 
 // ---------------------------------------------------------------- merge
-// grid (16 heads, ceil(B / 8)): the pieces of each of 8 sequences combined
+// grid (16 heads, ceil(B / 4)): the pieces of each of 4 sequences combined
 // into o~ [512] (normalised), then o = o~ W_UV,h.
 __global__ __launch_bounds__(256) void mla_merge_kernel(MlaArgs a) {
-  const int h = blockIdx.x, b0 = 8 * blockIdx.y, tid = threadIdx.x;
+  const int h = blockIdx.x, b0 = 4 * blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  __shared__ float ot[8][kDC];
-  __shared__ float mM[8], mInv[8];
-  __shared__ int nps[8];
-  __shared__ float red[256 * 64];
-  const int nb = min(8, a.num_seqs - b0);
-  // per sequence: pieces, global max and 1 / sum (each wave takes two)
-  for (int bb = wave; bb < 8; bb += 4) {
+  __shared__ float ot[4][kDC];
+  __shared__ float mM[4], mInv[4];
+  __shared__ int nps[4];
+  __shared__ float red[256 * 32];
+  const int nb = min(4, a.num_seqs - b0);
+  {  // wave bb: pieces, global max and 1 / sum of sequence b0 + bb
+    const int bb = wave;
     int n = 0;
     float M = -INFINITY;
     if (bb < nb) {
-      n = (clamp_ctx(a, b0 + bb) + kSplit - 1) / kSplit;
+      n = pieces_of(a, b0 + bb);
       for (int s = lane; s < n; s += 64) M = fmaxf(M, a.ws_m[((int64_t)(b0 + bb) * a.splits + s) * kHeads + h]);
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
@@ -380,20 +448,35 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(MlaArgs a) {
     }
   }
   __syncthreads();
-  for (int bb = 0; bb < 8; ++bb) {
+  {  // thread (bb, c8): o~[bb][8 c8 .. +8] as a weighted sum over the pieces
+    const int bb = wave, c = 8 * lane;
     const int n = nps[bb];
-    const float M = mM[bb], inv = mInv[bb];
+    const float M = mM[bb];
+    float v[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    const int64_t p0 = (int64_t)(b0 + bb) * a.splits;
+    constexpr int kBatch = 4;  // pieces whose loads are in flight together
+    for (int s0 = 0; s0 < n; s0 += kBatch) {
+      f32x4 x[kBatch][2];
+      float w[kBatch];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int c = tid + 256 * k;
-      float v = 0.0f;
-      for (int s = 0; s < n; ++s) {
-        const int64_t piece = (int64_t)(b0 + bb) * a.splits + s;
-        const float w = __builtin_amdgcn_exp2f(a.ws_m[piece * kHeads + h] - M);
-        v = fmaf(w, a.ws_o[(piece * kHeads + h) * kDC + c], v);
+      for (int u = 0; u < kBatch; ++u) {
+        const int s = s0 + u < n ? s0 + u : s0;
+        const float* src = a.ws_o + ((p0 + s) * kHeads + h) * kDC + c;
+        x[u][0] = *reinterpret_cast<const f32x4*>(src);
+        x[u][1] = *reinterpret_cast<const f32x4*>(src + 4);
+        w[u] = s0 + u < n ? __builtin_amdgcn_exp2f(a.ws_m[(p0 + s) * kHeads + h] - M) : 0.0f;
       }
-      ot[bb][c] = v * inv;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[e] = fmaf(w[u], x[u][0][e], v[e]);
+          v[4 + e] = fmaf(w[u], x[u][1][e], v[4 + e]);
+        }
     }
+    const float inv = mInv[bb];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ot[bb][c + e] = v[e] * inv;
   }
   __syncthreads();
   // o = o~ W_UV,h: thread (jg, cg) takes 8 output dims 8 jg.. and a slice of
@@ -401,41 +484,39 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(MlaArgs a) {
   const int jgs = a.dv / 8, cgs = 256 / jgs;
   const int jg = tid % jgs, cg = tid / jgs;
   const int per = kDC / cgs;
-  float acc[8][8];
+  float acc[4][8];
 #pragma unroll
-  for (int bb = 0; bb < 8; ++bb)
+  for (int bb = 0; bb < 4; ++bb)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[bb][e] = 0.0f;
-  if (cg < cgs) {
-    const int64_t wrow = (int64_t)kHeads * a.dv;
-    for (int c = cg * per; c < (cg + 1) * per; ++c) {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.w_uv) + c * wrow +
-                                                        (int64_t)h * a.dv + 8 * jg);
-      float wf[8];
+  const int64_t wrow = (int64_t)kHeads * a.dv;
+  const uint16_t* wbase = static_cast<const uint16_t*>(a.w_uv) + (int64_t)h * a.dv + 8 * jg;
+#pragma unroll 8
+  for (int c = cg * per; c < (cg + 1) * per; ++c) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(wbase + c * wrow);
+    float wf[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        wf[2 * e] = bf16_lo(w[e]);
-        wf[2 * e + 1] = bf16_hi(w[e]);
-      }
-#pragma unroll
-      for (int bb = 0; bb < 8; ++bb) {
-        const float x = ot[bb][c];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[bb][e] = fmaf(x, wf[e], acc[bb][e]);
-      }
+    for (int e = 0; e < 4; ++e) {
+      wf[2 * e] = bf16_lo(w[e]);
+      wf[2 * e + 1] = bf16_hi(w[e]);
     }
-    // red[cg][bb][dv]
 #pragma unroll
-    for (int bb = 0; bb < 8; ++bb)
+    for (int bb = 0; bb < 4; ++bb) {
+      const float x = ot[bb][c];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) red[(cg * 8 + bb) * a.dv + 8 * jg + e] = acc[bb][e];
+      for (int e = 0; e < 8; ++e) acc[bb][e] = fmaf(x, wf[e], acc[bb][e]);
+    }
   }
+#pragma unroll
+  for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[(cg * 4 + bb) * a.dv + 8 * jg + e] = acc[bb][e];
   __syncthreads();
-  for (int i = tid; i < 8 * a.dv; i += 256) {
+  for (int i = tid; i < 4 * a.dv; i += 256) {
     const int bb = i / a.dv, j = i % a.dv;
     if (bb >= nb) continue;
     float v = 0.0f;
-    for (int g = 0; g < cgs; ++g) v += red[(g * 8 + bb) * a.dv + j];
+    for (int g = 0; g < cgs; ++g) v += red[(g * 4 + bb) * a.dv + j];
     const int64_t oi = (int64_t)(b0 + bb) * a.out_seq_stride + (int64_t)h * a.dv + j;
     if (a.out_f32)
       static_cast<float*>(a.out)[oi] = v;
@@ -532,6 +613,8 @@ extern "C" pa_status pa_mla_decode_attention(void* out, pa_dtype out_dtype, int6
   if (!aligned(latent_cache, 16) || (block_stride * 2) % 16 != 0)
     return fail(PA_EINVAL, "%s: latent cache must be 16-byte aligned per block", fn);
   if (!aligned(w_uk, 16) || !aligned(w_uv, 16)) return fail(PA_EINVAL, "%s: weights must be 16-byte aligned", fn);
+  if (!aligned(q_nope, 16) || (q_nope_seq_stride * 2) % 16 != 0)
+    return fail(PA_EINVAL, "%s: q_nope must be 16-byte aligned per sequence", fn);
   const MlaPlan p = mla_plan(num_seqs, rope_dim, max_blocks_per_seq, block_size);
   if (!workspace || workspace_bytes < p.bytes || !aligned(workspace, 256))
     return fail(PA_EWORKSPACE, "%s: workspace needs %zu bytes, 256-byte aligned (got %zu)", fn, p.bytes, workspace_bytes);
@@ -567,15 +650,15 @@ extern "C" pa_status pa_mla_decode_attention(void* out, pa_dtype out_dtype, int6
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const dim3 g2(kHeads, (unsigned)((num_seqs + 7) / 8));
-  mla_absorb_kernel<<<g2, 256, 0, st>>>(a, row);
+  mla_absorb_kernel<<<dim3(kHeads, kDC / 64, (unsigned)((num_seqs + 15) / 16)), 256, 0, st>>>(a, row);
+  // one workgroup per live piece at most: sum over sequences of ceil(ctx / 256)
+  // <= num_seqs * splits; workgroups past the last live piece exit at once
   const int64_t items = (int64_t)num_seqs * p.splits;
   if (items > INT32_MAX / 2) return fail(PA_EINVAL, "%s: too many (sequence, piece) items", fn);
-  const unsigned grid = (unsigned)((items + 7) / 8 * 8);
   if (rope_dim == 64)
-    mla_split_kernel<64><<<grid, 64 * kWaves, 0, st>>>(a);
+    mla_split_kernel<64><<<(unsigned)items, 64 * kWaves, 0, st>>>(a);
   else
-    mla_split_kernel<0><<<grid, 64 * kWaves, 0, st>>>(a);
-  mla_merge_kernel<<<g2, 256, 0, st>>>(a);
+    mla_split_kernel<0><<<(unsigned)items, 64 * kWaves, 0, st>>>(a);
+  mla_merge_kernel<<<dim3(kHeads, (unsigned)((num_seqs + 3) / 4)), 256, 0, st>>>(a);
   return after_launch(fn);
 }
