@@ -221,6 +221,58 @@ def test_prefill_attention_empty_is_noop(L):
     assert prefill(L, B=0, cu=None) == L.PA_OK
 
 
+def mla(L, **over):
+    a = dict(out=1 << 20, odt=L.PA_BF16, os=16 * 128, qn=1 << 21, qns=16 * 128, qr=1 << 22, qrs=16 * 64,
+             qdt=L.PA_BF16, wuk=1 << 23, wuv=1 << 24, wdt=L.PA_BF16, cache=1 << 25, cdt=L.PA_BF16, NB=16,
+             BS=16, bstride=16 * 576, bt=1 << 26, W=4, cl=1 << 27, B=2, H=16, QK=128, R=64, DC=512, DV=128,
+             scale=0.07, ws=1 << 28, wsb=1 << 30)
+    a.update(over)
+    return L.lib.pa_mla_decode_attention(a["out"], a["odt"], a["os"], a["qn"], a["qns"], a["qr"], a["qrs"],
+                                         a["qdt"], a["wuk"], a["wuv"], a["wdt"], a["cache"], a["cdt"], a["NB"],
+                                         a["BS"], a["bstride"], a["bt"], a["W"], a["cl"], a["B"], a["H"],
+                                         a["QK"], a["R"], a["DC"], a["DV"], a["scale"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(H=8), "PA_EUNSUPPORTED"),
+    (dict(DC=256), "PA_EUNSUPPORTED"),
+    (dict(R=32), "PA_EUNSUPPORTED"),
+    (dict(QK=12), "PA_EUNSUPPORTED"),
+    (dict(QK=264), "PA_EUNSUPPORTED"),
+    (dict(DV=24), "PA_EUNSUPPORTED"),          # 24 / 8 = 3 does not divide 256
+    (dict(B=-1), "PA_EINVAL"),
+    (dict(W=0), "PA_EINVAL"),
+    (dict(odt=3), "PA_EDTYPE"),
+    (dict(qdt=2), "PA_EDTYPE"),
+    (dict(wdt=2), "PA_EDTYPE"),
+    (dict(cdt=3), "PA_EDTYPE"),
+    (dict(scale=float("nan")), "PA_EINVAL"),
+    (dict(bstride=16 * 576 - 8), "PA_EINVAL"),
+    (dict(os=100), "PA_EINVAL"),
+    (dict(qns=100), "PA_EINVAL"),
+    (dict(qrs=10), "PA_EINVAL"),
+    (dict(qr=None), "PA_EINVAL"),
+    (dict(cache=None), "PA_EINVAL"),
+    (dict(qn=(1 << 21) + 2), "PA_EINVAL"),     # misaligned q_nope
+    (dict(wuk=(1 << 23) + 4), "PA_EINVAL"),    # misaligned weights
+    (dict(wsb=16), "PA_EWORKSPACE"),
+])
+def test_mla_decode_rejects(L, over, code):
+    assert mla(L, **over) == getattr(L, code)
+    assert L.last_error()
+
+
+def test_mla_decode_empty_and_workspace_size(L):
+    assert mla(L, B=0, qn=None, out=None) == L.PA_OK
+    # no RoPE part: q_rope may be NULL (the call then stops at the too-small workspace)
+    assert mla(L, R=0, qr=None, bstride=16 * 512, wsb=16) == L.PA_EWORKSPACE
+    f = L.lib.pa_mla_decode_workspace_size
+    n = f(64, 16, 128, 64, 512, 128, 256, 16)
+    assert n > 0 and n % 256 == 0 and n == f(64, 16, 128, 64, 512, 128, 256, 16)
+    assert n > f(32, 16, 128, 64, 512, 128, 256, 16)
+    assert f(64, 8, 128, 64, 512, 128, 256, 16) == 0 and L.last_error()
+
+
 def test_hbm_copy_rejects(L):
     assert L.lib.pa_hbm_copy(None, 1 << 20, 64, None) == L.PA_EINVAL
     assert L.lib.pa_hbm_copy(1 << 20, (1 << 20) + 16, 64, None) == L.PA_EINVAL  # overlap
