@@ -272,11 +272,19 @@ pa_status pa_decode_attention(void* out, pa_dtype out_dtype, int64_t out_seq_str
  *       k_scale, v_scale, stream);
  *   pa_decode_attention(out, ..., context_lens, ..., workspace, ...);
  * where context_lens[b] already counts the new token (position
- * context_lens[b] - 1). Both kernels go on `stream`, write first; every
- * argument is checked before either is enqueued, so an error leaves no work
- * queued. (Reading the new rows from new_k/new_v inside the attention kernel
- * instead of from the cache was measured slower on gfx950: it costs the
- * persistent kernel registers in its inner loop.)
+ * context_lens[b] - 1). Every argument is checked before anything is
+ * enqueued, so an error leaves no work queued. For the persistent kernel's
+ * shapes (block_size a multiple of 16, head_size <= 128) the call launches
+ * two kernels: the attention over the cached positions, which leaves out
+ * position ctx-1 when new_slots[b] is that position's slot, and the merge
+ * pass, which takes the new token in from new_k / new_v as the cache write
+ * encodes it and then writes its row into new_slots[b]. The caches end up
+ * bit-identical to the two separate calls; the output differs from theirs
+ * only in the order of fp32 sums. Other shapes enqueue the cache write, then
+ * the attention.
+ * Precondition (no check is possible on the host): new_slots[b], when it is
+ * written, is not the slot of any other position that some sequence's
+ * context reads in this call.
  *
  * Arguments
  *   new_k, new_v  [num_seqs, num_kv_heads, head_size], sequence strides

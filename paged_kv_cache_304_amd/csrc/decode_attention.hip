@@ -104,7 +104,17 @@ struct DecArgs {
   int32_t slots;           // persistent kernel: workgroups per KV-head group
   int32_t out_f32;
   float scale_log2;        // softmax_scale * log2(e)
+  // decode step (persistent kernel): the new tokens, bf16 [B, H_KV, D] rows,
+  // folded into the attention instead of being read back from the cache
+  const uint16_t* new_k;   // null: plain attention
+  const uint16_t* new_v;
+  const int64_t* new_slots;
+  int64_t new_k_stride, new_v_stride;
 };
+
+// Persistent kernel: flag in a sequence's chunk count (workspace) that the
+// decode step's new token is its last position and is left to the merge pass.
+constexpr int kFoldBit = 1 << 30;
 
 __device__ __forceinline__ int clamp_ctx(const DecArgs& a, int b) {
   int ctx = a.ctx_lens[b];
@@ -112,9 +122,99 @@ __device__ __forceinline__ int clamp_ctx(const DecArgs& a, int b) {
   return ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
 }
 
+// Decode step: position ctx-1 of sequence b is the new token when the token's
+// slot is that position's slot (the normal case). The attention then covers
+// positions 0 .. ctx-2 from the cache and takes the last one from the new row
+// as the cache write encodes it; otherwise every position comes from the cache.
+__device__ __forceinline__ bool new_token_is_last(const DecArgs& a, int b, int ctx) {
+  if (ctx < 1) return false;
+  const int64_t pool = a.num_blocks * (int64_t)a.block_size;
+  const int64_t s = resolve_token_slot<false>(a.new_slots, nullptr, 0, pool, b);
+  if (s < 0) return false;
+  const int p = ctx - 1;
+  const int e = a.bt[(int64_t)b * a.W + p / a.block_size];
+  return e >= 0 && (int64_t)e < a.num_blocks && s == (int64_t)e * a.block_size + p % a.block_size;
+}
+
 // ------------------------------------------------------------ small helpers
 
 template <int NW> struct Dw { uint32_t w[NW]; };
+
+// Eight elements of a new token's row as the cache write stores them (a bit
+// copy for a bf16 cache without scales, else fp32 / scale rounded once to the
+// cache type) and as the attention reads them back: the code and the raw
+// decoded values (scales are applied by the attention, as for cached rows).
+template <Ty C> struct NewCode;
+template <> struct NewCode<Ty::BF16> { using T = u32x4; };
+template <> struct NewCode<Ty::FP8> { using T = u32x2; };
+
+template <Ty C>
+__device__ __forceinline__ void new_token_chunk(const u32x4& raw, bool scaled, float s, double rcp,
+                                                typename NewCode<C>::T& code, float (&val)[8]) {
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bf16_lo(raw[i]);
+    f[2 * i + 1] = bf16_hi(raw[i]);
+  }
+  if constexpr (C == Ty::BF16) {
+    if (!scaled) {
+      code = raw;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) val[i] = f[i];
+      return;
+    }
+    div_by_scale<8>(f, s, rcp);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      code[i] = f32x2_to_bf16x2(f[2 * i], f[2 * i + 1]);
+      val[2 * i] = bf16_lo(code[i]);
+      val[2 * i + 1] = bf16_hi(code[i]);
+    }
+  } else {
+    if (scaled) div_by_scale<8>(f, s, rcp);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      code[i] = f32x4_to_fp8x4(f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3]);
+      const f32x2 lo = fp8x2_lo(code[i]), hi = fp8x2_hi(code[i]);
+      val[4 * i] = lo[0];
+      val[4 * i + 1] = lo[1];
+      val[4 * i + 2] = hi[0];
+      val[4 * i + 3] = hi[1];
+    }
+  }
+}
+
+// One element of a new token's row as the attention reads it back from the
+// cache (the raw decoded value; see new_token_chunk).
+template <Ty C>
+__device__ __forceinline__ float new_token_value(float x, bool scaled, float s, double rcp) {
+  if (C == Ty::BF16 && !scaled) return x;
+  float f[1] = {x};
+  if (scaled) div_by_scale<1>(f, s, rcp);
+  if constexpr (C == Ty::BF16)
+    return bf16_lo(f32_to_bf16(f[0]));
+  else
+    return fp8x2_lo(f32_to_fp8(f[0]))[0];
+}
+
+// Writes chunk `e0 .. e0+7` of head g of the new token of sequence b into its
+// cache slot s (K and V).
+template <Ty C>
+__device__ __forceinline__ void write_new_chunk(const DecArgs& a, int b, int g, int D, int e0, int64_t s,
+                                                const u32x4& kraw, const u32x4& vraw, bool scaled, float ks,
+                                                double rk, float vs, double rv) {
+  (void)b;
+  constexpr int CB = TyInfo<C>::kBytes;
+  const int64_t blk = s / a.block_size, off = s - blk * a.block_size;
+  const int64_t at = (blk * a.block_stride + off * (int64_t)a.HKV * D + (int64_t)g * D + e0) * CB;
+  typename NewCode<C>::T code;
+  float val[8];
+  new_token_chunk<C>(kraw, scaled, ks, rk, code, val);
+  *reinterpret_cast<typename NewCode<C>::T*>(static_cast<char*>(const_cast<void*>(a.kc)) + at) = code;
+  new_token_chunk<C>(vraw, scaled, vs, rv, code, val);
+  *reinterpret_cast<typename NewCode<C>::T*>(static_cast<char*>(const_cast<void*>(a.vc)) + at) = code;
+}
 
 // NW dwords; non-temporal when NT (data read once per call, full lines per
 // instruction), cached otherwise (a line read in parts by successive loads).
@@ -237,7 +337,7 @@ __device__ __forceinline__ void store_split(const DecArgs& a, int b, int h, int 
 // would need an agent-scope release/acquire per workgroup, i.e. an L2
 // write-back on its XCD for every piece; the kernel boundary gives that
 // ordering for free.)
-template <int D>
+template <Ty C, int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecArgs a) {
   constexpr int PER = D / 64;
   constexpr int kFirst = 4;   // outputs loaded before the piece count is known
@@ -250,6 +350,30 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecArgs a) {
 
   const int ctx_raw = a.ctx_lens[b];
   const int n_raw = a.ws_n ? a.ws_n[b] : 0;
+  // Decode step: the new token's elements of this head (q, k, v) and, for the
+  // row write, this lane's 8-element chunk are loaded up front, alongside the
+  // chunks, whether or not they are needed.
+  const bool step = a.new_k != nullptr;
+  const int G = a.HQ / a.HKV, g = h / G;
+  float q_t[PER], k_t[PER], v_t[PER];
+  u32x4 kw8 = {0u, 0u, 0u, 0u}, vw8 = {0u, 0u, 0u, 0u};
+  int64_t slot_raw = -1;
+  if (step) {
+    const uint16_t* nk = a.new_k + (int64_t)b * a.new_k_stride + (int64_t)g * D;
+    const uint16_t* nv = a.new_v + (int64_t)b * a.new_v_stride + (int64_t)g * D;
+    const uint16_t* qh = static_cast<const uint16_t*>(a.q) + (int64_t)b * a.q_seq_stride + (int64_t)h * D;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      q_t[i] = load1<Ty::BF16>(qh, lane + 64 * i);
+      k_t[i] = load1<Ty::BF16>(nk, lane + 64 * i);
+      v_t[i] = load1<Ty::BF16>(nv, lane + 64 * i);
+    }
+    if (lane < D / 8) {
+      kw8 = *reinterpret_cast<const u32x4*>(nk + 8 * lane);
+      vw8 = *reinterpret_cast<const u32x4*>(nv + 8 * lane);
+    }
+    slot_raw = a.new_slots[b];
+  }
   const int cap0 = min(64, a.max_splits);
   const float m0 = lane < cap0 ? a.ws_m[base + lane] : -INFINITY;
   const float l0 = lane < cap0 ? a.ws_l[base + lane] : 0.0f;
@@ -264,22 +388,43 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecArgs a) {
 
   const int cap = a.W * a.block_size;
   const int ctx = ctx_raw < 0 ? 0 : (ctx_raw > cap ? cap : ctx_raw);
+  // Decode step: the persistent kernel left every chunk here, without the
+  // new token when it is the last position; it joins the softmax below as
+  // one more position, its row as the cache write encodes it.
+  const int64_t pool = a.num_blocks * (int64_t)a.block_size;
+  const int64_t slot_new = slot_raw >= 0 && slot_raw < pool ? slot_raw : -1;
+  const bool fold = step && ctx >= 1 && (n_raw & kFoldBit) != 0;  // decided by the persistent kernel
   int n;
   if (a.ws_n) {
-    n = ctx == 0 ? 0 : n_raw;  // count written by the persistent kernel (not for empty sequences)
+    n = ctx == 0 ? 0 : (n_raw & (kFoldBit - 1));  // written by the persistent kernel (not for empty sequences)
   } else {
     const int nblk = (ctx + a.block_size - 1) / a.block_size;
     n = (nblk + a.split_blocks - 1) / a.split_blocks;
     if (n <= 1) return;  // written by the split pass (zeros included)
   }
-  if (n == 1) return;
+  if (n == 1 && !step) return;
+
+  const bool scaled = a.k_scale != nullptr;
+  const float ks = scaled ? *a.k_scale : 1.0f, vs = scaled ? *a.v_scale : 1.0f;
+  const double rk = scaled ? 1.0 / (double)ks : 1.0, rv = scaled ? 1.0 / (double)vs : 1.0;
+  float s_new = -INFINITY;  // the new token's score (log2 domain) and value
+  float v_new[PER];
+  if (fold) {
+    float dot = 0.0f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      dot = fmaf(q_t[i], new_token_value<C>(k_t[i], scaled, ks, rk), dot);
+      v_new[i] = new_token_value<C>(v_t[i], scaled, vs, rv) * vs;
+    }
+    s_new = wave_sum(dot) * (a.scale_log2 * ks);
+  }
 
   float o[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) o[i] = 0.0f;
   float M = lane < n ? m0 : -INFINITY;
   for (int s = 64 + lane; s < n; s += 64) M = fmaxf(M, a.ws_m[base + s]);
-  M = wave_max(M);
+  M = fmaxf(wave_max(M), s_new);
   if (M != -INFINITY) {
     float den = 0.0f;
     for (int c = 0; c < n; c += 64) {
@@ -318,11 +463,22 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecArgs a) {
         }
       }
     }
-    const float inv = 1.0f / wave_sum(den);
+    float dsum = wave_sum(den);
+    if (fold) {
+      const float wt = __builtin_amdgcn_exp2f(s_new - M);
+      dsum += wt;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) o[i] = fmaf(wt, v_new[i], o[i]);
+    }
+    const float inv = 1.0f / dsum;
 #pragma unroll
     for (int i = 0; i < PER; ++i) o[i] *= inv;
   }
-  // n == 0 (empty sequence) or no attended position: zeros
+  // n == 0 (empty sequence) or no attended position: zeros. A decode step
+  // writes the new token's row into its slot here, one wave per KV head,
+  // after every read of this launch's attention.
+  if (step && h % G == 0 && slot_new >= 0 && lane < D / 8)
+    write_new_chunk<C>(a, b, g, D, 8 * lane, slot_new, kw8, vw8, scaled, ks, rk, vs, rv);
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int64_t at = (int64_t)b * a.out_seq_stride + (int64_t)h * D + lane + 64 * i;
@@ -660,7 +816,7 @@ constexpr int persistent_waves_per_eu(int D, int G) {
   return D == 64 ? (G <= 2 ? 5 : (G == 4 ? 4 : 3)) : (G <= 2 ? 4 : (G == 4 ? 3 : 2));
 }
 
-template <Ty C, int D, int G>
+template <Ty C, int D, int G, bool kFused>
 __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(persistent_waves_per_eu(D, G), 8)))
 void decode_persistent_kernel(DecArgs a) {
   using T = Tile<C, D>;
@@ -681,6 +837,7 @@ void decode_persistent_kernel(DecArgs a) {
   __shared__ __attribute__((aligned(16))) char k_lds[kMaxWaves * T::KB];
   __shared__ __attribute__((aligned(16))) char q_lds[kMaxWaves * 2 * QB];
   __shared__ int seg_b[kSegMax], seg_t0[kSegMax], seg_t1[kSegMax], seg_ctx[kSegMax], seg_k[kSegMax], seg_n[kSegMax];
+  __shared__ int seg_x[kSegMax];  // decode step: the new token is this sequence's last position
   __shared__ int64_t wave_tiles[kMaxWaves];
   __shared__ int seg_count;
 
@@ -756,7 +913,16 @@ void decode_persistent_kernel(DecArgs a) {
           seg_b[i] = b;
           seg_t0[i] = (int)(lo - S);
           seg_t1[i] = (int)(hi - S);
-          seg_ctx[i] = ctx;
+          // the positions this segment attends end at ctx -- or at ctx - 1 in
+          // a decode step whose new token is the last position: the merge
+          // pass takes that one in from the new row (its cache slot is written
+          // after this launch)
+          int sc = ctx;
+          if constexpr (kFused) {
+            if (hi == S + nt && new_token_is_last(a, b, ctx)) sc = ctx - 1;
+          }
+          seg_ctx[i] = sc;
+          seg_x[i] = sc < ctx ? 1 : 0;
           seg_k[i] = (int)(lo / RT - S / RT);
           seg_n[i] = (int)((S + nt - 1) / RT - S / RT + 1);
         }
@@ -889,10 +1055,14 @@ void decode_persistent_kernel(DecArgs a) {
             float o[EPL];
 #pragma unroll
             for (int k = 0; k < EPL; ++k) o[k] = acc[j][k] * inv;
-            store_split<D, EPL>(a, b, g * G + j, chunk, nch, EPL * li, o, li == j, m_run, lj[j]);
+            // a decode step always leaves its chunks to the merge pass (it adds the new token)
+            store_split<D, EPL>(a, b, g * G + j, chunk, kFused && nch == 1 ? 2 : nch, EPL * li, o, li == j, m_run,
+                                lj[j]);
           }
         }
-        if (chunk == 0 && g == 0 && lane == 0) a.ws_n[b] = nch;
+        // the chunk count, and (decode step) whether the merge pass takes in
+        // the new token, written once per sequence by its last chunk's group 0
+        if (chunk == nch - 1 && g == 0 && lane == 0) a.ws_n[b] = nch | (kFused && seg_x[i] ? kFoldBit : 0);
         bt_cur = bt_nxt;
       }
     }
@@ -960,13 +1130,14 @@ int device_cus() {
 
 // Resident workgroups per compute unit of the persistent kernel at this
 // workgroup size (a property of the kernel binary, cached).
-template <Ty C, int D, int G>
+template <Ty C, int D, int G, bool kFused>
 int persistent_occupancy(int waves_per_wg) {
   static std::atomic<int> cache[kMaxWaves + 1];
   const int c = cache[waves_per_wg].load(std::memory_order_relaxed);
   if (c > 0) return c;
   int nb = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_persistent_kernel<C, D, G>, 64 * waves_per_wg, 0) != hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_persistent_kernel<C, D, G, kFused>, 64 * waves_per_wg, 0) !=
+      hipSuccess)
     return 0;
   cache[waves_per_wg].store(nb, std::memory_order_relaxed);
   return nb;
@@ -976,12 +1147,19 @@ template <Ty C, int D, int G>
 bool launch_split(DecArgs& a, const Plan& p, hipStream_t st) {
   if (p.persistent) {
     if constexpr (D <= 128) {
-      const int cus = device_cus(), occ = persistent_occupancy<C, D, G>(p.waves_per_wg);
+      const bool fused = a.new_k != nullptr;
+      const int cus = device_cus();
+      const int occ = fused ? persistent_occupancy<C, D, G, true>(p.waves_per_wg)
+                            : persistent_occupancy<C, D, G, false>(p.waves_per_wg);
       if (cus <= 0 || occ <= 0) return false;
       const int64_t resident = (int64_t)cus * occ;
       a.slots = (int)(resident / p.kv_groups > 1 ? resident / p.kv_groups : 1);
-      decode_persistent_kernel<C, D, G><<<(unsigned)(a.slots * p.kv_groups), 64 * p.waves_per_wg, 0, st>>>(a);
-      decode_merge_kernel<D><<<(unsigned)(((int64_t)a.num_seqs * a.HQ + 3) / 4), 256, 0, st>>>(a);
+      const unsigned grid = (unsigned)(a.slots * p.kv_groups);
+      if (fused)
+        decode_persistent_kernel<C, D, G, true><<<grid, 64 * p.waves_per_wg, 0, st>>>(a);
+      else
+        decode_persistent_kernel<C, D, G, false><<<grid, 64 * p.waves_per_wg, 0, st>>>(a);
+      decode_merge_kernel<C, D><<<(unsigned)(((int64_t)a.num_seqs * a.HQ + 3) / 4), 256, 0, st>>>(a);
       return true;
     }
     return false;
@@ -991,7 +1169,7 @@ bool launch_split(DecArgs& a, const Plan& p, hipStream_t st) {
   dim3 grid(p.kv_groups, p.max_splits, a.num_seqs);
   decode_split_valu_kernel<C, D, G><<<grid, 64 * p.waves_per_wg, 0, st>>>(a);
   if (p.max_splits > 1)
-    decode_merge_kernel<D><<<(unsigned)(((int64_t)a.num_seqs * a.HQ + 3) / 4), 256, 0, st>>>(a);
+    decode_merge_kernel<C, D><<<(unsigned)(((int64_t)a.num_seqs * a.HQ + 3) / 4), 256, 0, st>>>(a);
   return true;
 }
 
@@ -1085,6 +1263,8 @@ pa_status decode_common(const char* fn, void* out, pa_dtype out_dtype, int64_t o
   if (!out || !q || !key_cache || !value_cache || !block_tables || !context_lens)
     return fail(PA_EINVAL, "%s: null pointer argument", fn);
   if (nt && (!nt->k || !nt->v || !nt->slots)) return fail(PA_EINVAL, "%s: null new-token pointer", fn);
+  if (nt && (!aligned(nt->k, 16) || !aligned(nt->v, 16) || (nt->k_stride * 2) % 16 != 0 || (nt->v_stride * 2) % 16 != 0))
+    return fail(PA_EINVAL, "%s: new-token rows must be 16-byte aligned", fn);
   const int cb = dtype_bytes(cache_dtype), ob = dtype_bytes(out_dtype);
   if (!aligned(q, 16) || (q_seq_stride * 2) % 16 != 0) return fail(PA_EINVAL, "%s: q must be 16-byte aligned per sequence", fn);
   if (!aligned(out, 16) || (out_seq_stride * ob) % 16 != 0) return fail(PA_EINVAL, "%s: out must be 16-byte aligned per sequence", fn);
@@ -1125,9 +1305,20 @@ pa_status decode_common(const char* fn, void* out, pa_dtype out_dtype, int64_t o
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  if (nt) {
-    // the step's cache write goes first on the same stream; it checks its own
-    // arguments before it launches anything, so a refusal leaves no work queued
+  a.new_k = nullptr;
+  a.new_v = nullptr;
+  a.new_slots = nullptr;
+  a.new_k_stride = a.new_v_stride = 0;
+  if (nt && p.persistent) {
+    // the persistent kernel takes the new tokens in itself and writes them
+    a.new_k = static_cast<const uint16_t*>(nt->k);
+    a.new_v = static_cast<const uint16_t*>(nt->v);
+    a.new_slots = nt->slots;
+    a.new_k_stride = nt->k_stride;
+    a.new_v_stride = nt->v_stride;
+  } else if (nt) {
+    // other shapes: the cache write first, on the same stream; it checks its
+    // own arguments before it launches anything, so a refusal queues nothing
     s = pa_reshape_and_cache(nt->k, nt->v, PA_BF16, num_seqs, num_kv_heads, head_size, nt->k_stride, nt->v_stride,
                              const_cast<void*>(key_cache), const_cast<void*>(value_cache), cache_dtype, num_blocks,
                              block_size, block_stride, nt->slots, nullptr, 0, k_scale, v_scale, stream);

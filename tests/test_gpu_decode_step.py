@@ -137,8 +137,11 @@ def test_step_matches_write_then_attention(case):
 
 
 def test_full_b64_step_equals_separate_calls():
-    """The batch-64 Qwen3-0.6B step: the fused call leaves caches and output
-    bit-identical to reshape_and_cache followed by decode_attention on the GPU."""
+    """The batch-64 Qwen3-0.6B step: the one-call step leaves the caches
+    bit-identical to reshape_and_cache followed by decode_attention on the GPU,
+    and its output within the attention tolerance of theirs (the step takes the
+    new token into the softmax after the cached positions, a different order of
+    the same fp32 sums)."""
     m = pkv()
     w = workloads.qwen3_decode_b64()
     B, HQ, HKV, D, BS, NB = (w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_size,
@@ -161,7 +164,8 @@ def test_full_b64_step_equals_separate_calls():
     torch.cuda.synchronize()
     assert torch.equal(kc.view(torch.int16), kc2.view(torch.int16))
     assert torch.equal(vc.view(torch.int16), vc2.view(torch.int16))
-    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+    assert_attention_close(widen_out(out1), widen_out(out2).astype(np.float64), "step vs separate calls",
+                           out_bf16=True)
 
 
 def test_step_in_a_hip_graph_replays_exactly():
