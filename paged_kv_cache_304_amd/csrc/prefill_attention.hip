@@ -90,6 +90,7 @@ __device__ __forceinline__ void barrier_no_vmem_wait() {
 }
 
 constexpr int kTab = 2048;  // block-table entries staged in LDS at a time
+constexpr int kBins = 64;   // length classes of the dispatch order
 
 struct PfArgs {
   void* out;
@@ -113,6 +114,7 @@ struct PfArgs {
   int32_t HKV;
   int32_t out_f32;
   int64_t tiles_ub;        // query tiles per KV head, upper bound (grid = HKV * tiles_ub, rounded up to 8)
+  int32_t bin_w;           // key tiles per length class of the dispatch order
   float scale_log2;
 };
 
@@ -170,6 +172,8 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
     int tab[kTab];              // validated table entries of blocks tab_base ..
     int64_t wave_tiles[kWaves];
     int found[2];               // sequence, tile index within it
+    int bins[kBins];            // query tiles per length class
+    int64_t pick[2];            // the class holding this workgroup's tile, its rank inside
   };
   static_assert(sizeof(Smem::kv) <= 65536, "LDS-DMA targets stay below 64 KB");
   __shared__ __attribute__((aligned(16))) Smem sm;
@@ -178,9 +182,13 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
   auto& found = sm.found;
   auto& tab = sm.tab;
 
-  // ---- which (sequence, query tile) this workgroup serves: tiles are counted
-  // per sequence in order (a thread-run scan over cu_seqlens), each sequence's
-  // tiles taken last-first so that the longest causal ranges start first.
+  // ---- which (sequence, query tile) this workgroup serves. Dispatch order:
+  // sequences in descending length classes (class = key tiles of the
+  // sequence's longest query tile / bin_w), by index within a class; each
+  // sequence's query tiles together and last-first. The workgroups dispatched
+  // first -- those resident from the start -- take the longest work, and the
+  // tiles of one (KV head, sequence) stay consecutive, which keeps them on
+  // one XCD. Tiles are found by thread-run scans over cu_seqlens.
   const int nthr = 64 * kWaves;
   const int per = (a.num_seqs + nthr - 1) / nthr;
   const int b_lo = min(a.num_seqs, tid * per), b_hi = min(a.num_seqs, b_lo + per);
@@ -190,8 +198,41 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
     hi = hi < lo ? lo : (hi > a.num_tokens ? (int)a.num_tokens : hi);
     return hi - lo;
   };
+  const int cap_all = a.W * a.block_size;
+  auto seq_class = [&](int b) -> int {
+    int L = a.ctx_lens[b];
+    L = L < 0 ? 0 : (L > cap_all ? cap_all : L);
+    return min(kBins - 1, ((L + kKeys - 1) / kKeys) / a.bin_w);
+  };
+  if (tid < kBins) sm.bins[tid] = 0;
+  __syncthreads();
+  for (int b = b_lo; b < b_hi; ++b) {
+    const int nt = (seq_rows(b) + QT - 1) / QT;
+    if (nt > 0) atomicAdd(&sm.bins[seq_class(b)], nt);
+  }
+  __syncthreads();
+  if (wave == 0) {  // classes in descending order: lane c holds class kBins-1-c
+    const int64_t cnt = sm.bins[kBins - 1 - lane];
+    int64_t inc = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int64_t y = __shfl_up(inc, (unsigned)o, 64);
+      if (lane >= o) inc += y;
+    }
+    const uint64_t below = __builtin_amdgcn_ballot_w64(inc <= t);  // classes wholly before t
+    const int sel = __builtin_popcountll(below);
+    if (lane == (sel < 64 ? sel : 0)) {
+      sm.pick[0] = sel < 64 ? kBins - 1 - sel : -1;
+      sm.pick[1] = t - (inc - cnt);
+    }
+  }
+  __syncthreads();
+  const int cls = (int)sm.pick[0];
+  const int64_t t_in = sm.pick[1];  // rank of this workgroup's tile inside class cls
   int64_t mine = 0;
-  for (int b = b_lo; b < b_hi; ++b) mine += (seq_rows(b) + QT - 1) / QT;
+  if (cls >= 0)
+    for (int b = b_lo; b < b_hi; ++b)
+      if (seq_class(b) == cls) mine += (seq_rows(b) + QT - 1) / QT;
   int64_t incl = mine;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -203,14 +244,15 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
   __syncthreads();
   int64_t before = 0;
   for (int w = 0; w < wave; ++w) before += wave_tiles[w];
-  {
+  if (cls >= 0) {
     int64_t S = before + incl - mine;
-    if (t >= S && t < S + mine) {
+    if (t_in >= S && t_in < S + mine) {
       for (int b = b_lo; b < b_hi; ++b) {
+        if (seq_class(b) != cls) continue;
         const int nt = (seq_rows(b) + QT - 1) / QT;
-        if (t < S + nt) {
+        if (t_in < S + nt) {
           found[0] = b;
-          found[1] = nt - 1 - (int)(t - S);
+          found[1] = nt - 1 - (int)(t_in - S);
           break;
         }
         S += nt;
@@ -649,6 +691,11 @@ extern "C" pa_status pa_prefill_attention(void* out, pa_dtype out_dtype, int64_t
   // query tiles: at most ceil(T / QT) + num_seqs (one partial tile per sequence)
   const int64_t qt = kRows / G;
   a.tiles_ub = (num_tokens + qt - 1) / qt + num_seqs;
+  {  // length classes: the key tiles of the longest possible query tile over kBins classes
+    const int64_t kt_max = ((int64_t)max_blocks_per_seq * block_size + kKeys - 1) / kKeys;
+    a.bin_w = (int)((kt_max + kBins - 1) / kBins);
+    if (a.bin_w < 1) a.bin_w = 1;
+  }
   if (a.tiles_ub * num_kv_heads + 7 > 0x7FFFFFFF) return fail(PA_EINVAL, "%s: too many query tiles", fn);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const bool ok = head_size == 64 ? launch_g<64>(G, a, st) : launch_g<128>(G, a, st);
