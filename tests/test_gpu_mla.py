@@ -197,3 +197,42 @@ def test_mla_decode_step_writes_latent_rows_then_attends():
     assert np.array_equal(to_host(dcache, BF16), ocache), "latent cache"
     got = gpu_mla(c, cache=to_host(dcache, BF16))
     assert_attention_close(got, ref, "mla step", out_bf16=False)
+
+
+def test_mla_in_a_hip_graph_replays_exactly():
+    """Captured once (workspace supplied), replayed four times with new queries
+    and eager work in between; every replay equals an eager call."""
+    m = pkv()
+    say("mla_decode graph capture")
+    c = make_case(515, [300, 1, 700, 64])
+    B = len(c["ctx"])
+    qn, qr = to_dev(c["q_nope"], BF16), to_dev(c["q_rope"], BF16)
+    wk, wv, cache = to_dev(c["w_uk"], BF16), to_dev(c["w_uv"], BF16), to_dev(c["cache"], BF16)
+    bt, cl = torch.from_numpy(c["bt"]).cuda(), torch.from_numpy(c["ctx"]).cuda()
+    ws = torch.empty(m.mla_decode_workspace_size(B, H, c["QK"], c["R"], DC, c["DV"], c["bt"].shape[1],
+                                                 c["cache"].shape[1]), dtype=torch.uint8, device="cuda")
+    out = torch.zeros((B, H, c["DV"]), dtype=torch.float32, device="cuda")
+    eager = torch.zeros_like(out)
+    call = lambda o: m.mla_decode_attention(o, qn, qr, wk, wv, cache, bt, cl, c["scale"], workspace=ws)  # noqa: E731
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(out)
+    rng = np.random.default_rng(2)
+    for i in range(4):
+        qn.copy_(to_dev(workloads.normal_bf16_bits(rng, c["q_nope"].shape), BF16))
+        qr.copy_(to_dev(workloads.normal_bf16_bits(rng, c["q_rope"].shape), BF16))
+        out.zero_()
+        junk = torch.randn(1 << 18, device="cuda").sum()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        call(eager)
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i}"
+        del junk

@@ -165,3 +165,35 @@ def test_full_size_prefill_batch():
         ref_abs = oracle.prefill_attention(sub[0], BF16, sub[1], kh, abs_values(vh), BF16, sub[2],
                                            sub[3], w["softmax_scale"])
         check_close(got_all[rows], ref, ref_abs, f"{w['name']} sequence {b}", True)
+
+
+def test_prefill_in_a_hip_graph_replays_exactly():
+    """Captured once, replayed four times with new queries and eager work in
+    between; every replay equals an eager call on the same inputs."""
+    m = pkv()
+    say("prefill_attention graph capture")
+    q, kc, vc, bt, ctx, cu = make_case(606, [300, 77, 1000], [64, 77, 129], 16, 8, 128, 16)
+    dq, dk, dv = to_dev(q, BF16), to_dev(kc, BF16), to_dev(vc, BF16)
+    dcu, dbt, dctx = torch.from_numpy(cu).cuda(), torch.from_numpy(bt).cuda(), torch.from_numpy(ctx).cuda()
+    out = torch.zeros(dq.shape, dtype=torch.bfloat16, device="cuda")
+    eager = torch.zeros_like(out)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        m.prefill_attention(out, dq, dcu, dk, dv, dbt, dctx, 0.088)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        m.prefill_attention(out, dq, dcu, dk, dv, dbt, dctx, 0.088)
+    rng = np.random.default_rng(1)
+    for i in range(4):
+        dq.copy_(to_dev(workloads.normal_bf16_bits(rng, q.shape), BF16))
+        out.zero_()
+        junk = torch.randn(1 << 18, device="cuda").sum()  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        m.prefill_attention(eager, dq, dcu, dk, dv, dbt, dctx, 0.088)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {i}"
+        del junk
