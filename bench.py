@@ -38,14 +38,16 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    # the first ~10 ms of work after start-up run up to 15% slower (the
+    # memory path warms up), so the default warm-up covers well past that
+    p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--workload", default="decode_b64",
                    choices=["decode_b64", "prefill_fp8", "decode_fp8_b256", "mla_concat_swa",
                             "mla_fused", "prefill_chunks", "engine_decode_b64",
                             "mla_decode_b64"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--profile-steps", type=int, default=0,
-                   help="only run this many untimed steps (for rocprofv3 runs)")
+                   help="only run --warmup then this many untimed steps (for rocprofv3 runs)")
     return p.parse_args()
 
 
@@ -167,8 +169,11 @@ def run_decode(args, torch, pkv, workloads, w, metric_name):
     stream = torch.cuda.current_stream()
     if args.profile_steps:
         copy_calibration(torch, pkv)
-        for _ in range(args.profile_steps):
+        for _ in range(args.warmup + args.profile_steps):
             decode_step(pkv, t, w)
+        # the launches roofline.achieved times: attention calls back to back
+        for _ in range(args.profile_steps):
+            decode_attn(pkv, t, w)
         torch.cuda.synchronize()
         print(json.dumps({"profile_steps": args.profile_steps, "workload": w.name}))
         return
@@ -184,15 +189,17 @@ def run_decode(args, torch, pkv, workloads, w, metric_name):
     t1.record(stream)
     torch.cuda.synchronize()
     ms_per_step = t0.elapsed_time(t1) / args.steps
-    # (2) per-call durations on the launch stream (attention = split pass + merge pass)
+    # (2) per-launch durations on the launch stream: K attention calls (split
+    # pass + merge pass) back to back between two events, then K new-token writes
     ta, tw = Timer(torch, stream), Timer(torch, stream)
+    ta.start()
     for _ in range(args.steps):
-        tw.start()
-        decode_write(pkv, t, w)
-        tw.stop()
-        ta.start()
         decode_attn(pkv, t, w)
-        ta.stop()
+    ta.stop()
+    tw.start()
+    for _ in range(args.steps):
+        decode_write(pkv, t, w)
+    tw.stop()
     torch.cuda.synchronize()
     # (3) cold: the 256 MB Infinity Cache flushed before every attention call
     flush_src = torch.empty(MALL_FLUSH_BYTES // 2, dtype=torch.uint8, device="cuda")
@@ -215,7 +222,7 @@ def run_decode(args, torch, pkv, workloads, w, metric_name):
     del flush_src, flush_dst
 
     kv, attn_bytes, write_bytes = decode_bytes(w)
-    attn_ms, write_ms, cold_ms = ta.mean_ms(), tw.mean_ms(), tc.mean_ms()
+    attn_ms, write_ms, cold_ms = ta.mean_ms() / args.steps, tw.mean_ms() / args.steps, tc.mean_ms()
     achieved = attn_bytes / (attn_ms * 1e-3) / 1e9
     value = kv / (ms_per_step * 1e-3) / 1e9
     res = {
@@ -404,7 +411,7 @@ def run_prefill_chunks(args, torch, pkv, workloads):
     stream = torch.cuda.current_stream()
     if args.profile_steps:
         copy_calibration(torch, pkv)
-        for _ in range(args.profile_steps):
+        for _ in range(args.warmup + args.profile_steps):
             step()
         torch.cuda.synchronize()
         print(json.dumps({"profile_steps": args.profile_steps, "workload": w["name"]}))
@@ -482,7 +489,7 @@ def engine_prefill_rounds(plan, lens, chunk=16):
 
 def engine_width(args, w) -> int:
     """Table width that holds every context after all the steps this run takes."""
-    loops = args.warmup + 2 * args.steps
+    loops = args.warmup + max(2 * args.steps, args.profile_steps)
     return -(-(int(w.context_lens.max()) + loops) // w.block_size)
 
 
@@ -526,7 +533,7 @@ def run_engine_decode(args, torch, pkv, workloads):
 
     if args.profile_steps:
         copy_calibration(torch, pkv)
-        for _ in range(args.profile_steps):
+        for _ in range(args.warmup + args.profile_steps):
             step()
         torch.cuda.synchronize()
         print(json.dumps({"profile_steps": args.profile_steps, "workload": "engine_decode_b64"}))
@@ -687,7 +694,7 @@ def run_mla_decode(args, torch, pkv, workloads):
 
     if args.profile_steps:
         copy_calibration(torch, pkv)
-        for _ in range(args.profile_steps):
+        for _ in range(args.warmup + args.profile_steps):
             write()
             attend()
         torch.cuda.synchronize()
@@ -769,7 +776,7 @@ def generic(args, torch, pkv, step, nbytes, kernel, name, dtype, units, unit_nam
     stream = torch.cuda.current_stream()
     if args.profile_steps:
         copy_calibration(torch, pkv)
-        for _ in range(args.profile_steps):
+        for _ in range(args.warmup + args.profile_steps):
             step()
         torch.cuda.synchronize()
         print(json.dumps({"profile_steps": args.profile_steps, "workload": name}))

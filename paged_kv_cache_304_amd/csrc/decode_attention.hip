@@ -70,6 +70,9 @@ namespace {
 #ifndef PA_DECODE_PRIO
 #define PA_DECODE_PRIO 1
 #endif
+#ifndef PA_DECODE_FP8_WAVES
+#define PA_DECODE_FP8_WAVES 4
+#endif
 constexpr int kMaxWaves = PA_DECODE_MAX_WAVES;        // KV heads (waves) per workgroup
 constexpr int kTargetWgs = PA_DECODE_TARGET_WGS;      // split workgroups aimed for if every sequence used all W blocks
 constexpr int kMinSplitTokens = PA_DECODE_MIN_SPLIT;  // positions per split, lower bound
@@ -809,6 +812,17 @@ constexpr int kSegMax = kRangeMaxTiles;  // each segment holds >= 1 tile of the 
 
 __device__ __forceinline__ int tiles_of(int ctx) { return (ctx + 15) >> 4; }
 
+// KV heads (waves) per workgroup of the persistent kernel. An fp8 wave reads
+// 128-byte pieces of each 1 KB cache row (eight heads of 128 dims); with four
+// heads per workgroup a workgroup reads half of every row, which the memory
+// system serves faster than four workgroups each reading a quarter
+// (153.6 vs 161.2 us on the batch-256 fp8 workload), while bf16 rows are
+// fastest in two-wave workgroups (96.4 vs 98.2 us at batch 64).
+template <Ty C> constexpr int persistent_max_waves() { return C == Ty::FP8 ? PA_DECODE_FP8_WAVES : PA_DECODE_MAX_WAVES; }
+constexpr int kWavesCap = 8;
+static_assert(PA_DECODE_FP8_WAVES >= 1 && PA_DECODE_FP8_WAVES <= kWavesCap && PA_DECODE_MAX_WAVES <= kWavesCap,
+              "waves per workgroup");
+
 // Waves per SIMD the persistent kernel is compiled for (its register budget):
 // the natural allocation of each shape, except that MFMA accumulator registers
 // must not push the D = 128, G <= 2 shapes past 128 registers.
@@ -817,7 +831,8 @@ constexpr int persistent_waves_per_eu(int D, int G) {
 }
 
 template <Ty C, int D, int G, bool kFused>
-__global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(persistent_waves_per_eu(D, G), 8)))
+__global__ __launch_bounds__(64 * persistent_max_waves<C>())
+__attribute__((amdgpu_waves_per_eu(persistent_waves_per_eu(D, G), 8)))
 void decode_persistent_kernel(DecArgs a) {
   using T = Tile<C, D>;
   constexpr int KS = T::KS;
@@ -834,11 +849,12 @@ void decode_persistent_kernel(DecArgs a) {
   const int g = gr * a.waves_per_wg + wave;
   const bool active = g < a.HKV;
 
-  __shared__ __attribute__((aligned(16))) char k_lds[kMaxWaves * T::KB];
-  __shared__ __attribute__((aligned(16))) char q_lds[kMaxWaves * 2 * QB];
+  constexpr int kW = persistent_max_waves<C>();
+  __shared__ __attribute__((aligned(16))) char k_lds[kW * T::KB];
+  __shared__ __attribute__((aligned(16))) char q_lds[kW * 2 * QB];
   __shared__ int seg_b[kSegMax], seg_t0[kSegMax], seg_t1[kSegMax], seg_ctx[kSegMax], seg_k[kSegMax], seg_n[kSegMax];
   __shared__ int seg_x[kSegMax];  // decode step: the new token is this sequence's last position
-  __shared__ int64_t wave_tiles[kMaxWaves];
+  __shared__ int64_t wave_tiles[kW];
   __shared__ int seg_count;
 
   // Tile counts of all sequences and their prefix sums: thread i owns a
@@ -1132,7 +1148,7 @@ int device_cus() {
 // workgroup size (a property of the kernel binary, cached).
 template <Ty C, int D, int G, bool kFused>
 int persistent_occupancy(int waves_per_wg) {
-  static std::atomic<int> cache[kMaxWaves + 1];
+  static std::atomic<int> cache[kWavesCap + 1];
   const int c = cache[waves_per_wg].load(std::memory_order_relaxed);
   if (c > 0) return c;
   int nb = 0;
@@ -1148,17 +1164,21 @@ bool launch_split(DecArgs& a, const Plan& p, hipStream_t st) {
   if (p.persistent) {
     if constexpr (D <= 128) {
       const bool fused = a.new_k != nullptr;
+      // this kernel's own workgroup width (the plan's is the vector path's)
+      constexpr int wmax = persistent_max_waves<C>();
+      a.waves_per_wg = a.HKV < wmax ? a.HKV : wmax;
+      a.kv_groups = (a.HKV + a.waves_per_wg - 1) / a.waves_per_wg;
       const int cus = device_cus();
-      const int occ = fused ? persistent_occupancy<C, D, G, true>(p.waves_per_wg)
-                            : persistent_occupancy<C, D, G, false>(p.waves_per_wg);
+      const int occ = fused ? persistent_occupancy<C, D, G, true>(a.waves_per_wg)
+                            : persistent_occupancy<C, D, G, false>(a.waves_per_wg);
       if (cus <= 0 || occ <= 0) return false;
       const int64_t resident = (int64_t)cus * occ;
-      a.slots = (int)(resident / p.kv_groups > 1 ? resident / p.kv_groups : 1);
-      const unsigned grid = (unsigned)(a.slots * p.kv_groups);
+      a.slots = (int)(resident / a.kv_groups > 1 ? resident / a.kv_groups : 1);
+      const unsigned grid = (unsigned)(a.slots * a.kv_groups);
       if (fused)
-        decode_persistent_kernel<C, D, G, true><<<grid, 64 * p.waves_per_wg, 0, st>>>(a);
+        decode_persistent_kernel<C, D, G, true><<<grid, 64 * a.waves_per_wg, 0, st>>>(a);
       else
-        decode_persistent_kernel<C, D, G, false><<<grid, 64 * p.waves_per_wg, 0, st>>>(a);
+        decode_persistent_kernel<C, D, G, false><<<grid, 64 * a.waves_per_wg, 0, st>>>(a);
       decode_merge_kernel<C, D><<<(unsigned)(((int64_t)a.num_seqs * a.HQ + 3) / 4), 256, 0, st>>>(a);
       return true;
     }
