@@ -304,21 +304,27 @@ def traffic_from_profiles(kernel: str, workload: str):
 def run_prefill_fp8(args, torch, pkv, workloads):
     w = workloads.prefill_write_fp8()
     T, H, D, BS, NB = w["num_tokens"], w["num_heads"], w["head_size"], w["block_size"], w["num_blocks"]
-    key = workloads.device_normal((T, H, D), torch.bfloat16, "cuda", w["seed"], std=w["std"])
-    val = workloads.device_normal((T, H, D), torch.bfloat16, "cuda", w["seed"] + 1, std=w["std"])
-    kc = torch.empty((NB, BS, H, D), dtype=torch.float8_e4m3fn, device="cuda")
-    vc = torch.empty_like(kc)
     slots = torch.from_numpy(w["slot_mapping"]).cuda()
     ks = torch.tensor([w["k_scale"]], device="cuda")
     vs = torch.tensor([w["v_scale"]], device="cuda")
+    # four independent source/cache sets (191 MB each): calls that rotate over
+    # them find none of their data in the 256 MB Infinity Cache
+    sets = []
+    for i in range(4):
+        key = workloads.device_normal((T, H, D), torch.bfloat16, "cuda", w["seed"], std=w["std"])
+        val = workloads.device_normal((T, H, D), torch.bfloat16, "cuda", w["seed"] + 1, std=w["std"])
+        kc = torch.empty((NB, BS, H, D), dtype=torch.float8_e4m3fn, device="cuda")
+        sets.append((key, val, kc, torch.empty_like(kc)))
 
-    def step():
+    def call(i):
+        key, val, kc, vc = sets[i % len(sets)]
         pkv.reshape_and_cache(key, val, kc, vc, slots, k_scale=ks, v_scale=vs)
 
     kept = int((w["slot_mapping"] >= 0).sum())
     nbytes = 8 * T + kept * 2 * H * D * (2 + 1)
-    return generic(args, torch, pkv, step, nbytes, "reshape_and_cache",
-                   "bulk_prefill_write_32768_bf16_to_fp8", "fp8_e4m3fn", T, "tokens_per_s")
+    return generic(args, torch, pkv, lambda: call(0), nbytes, "reshape_and_cache",
+                   "bulk_prefill_write_32768_bf16_to_fp8", "fp8_e4m3fn", T, "tokens_per_s",
+                   rotating=call)
 
 
 def run_mla(args, torch, pkv, workloads):
@@ -772,12 +778,15 @@ def run_decode_fp8(args, torch, pkv, workloads):
                       "paged decode attn KV-read GB/s & % HBM peak; cache-write GB/s (1 MI355X)")
 
 
-def generic(args, torch, pkv, step, nbytes, kernel, name, dtype, units, unit_name):
+def generic(args, torch, pkv, step, nbytes, kernel, name, dtype, units, unit_name, rotating=None):
+    """K back-to-back steps (warm). Cold: with `rotating(i)` (call i on one of
+    several buffer sets that together exceed the Infinity Cache), K such calls back
+    to back; otherwise each call timed alone after a 512 MiB copy."""
     stream = torch.cuda.current_stream()
     if args.profile_steps:
         copy_calibration(torch, pkv)
-        for _ in range(args.warmup + args.profile_steps):
-            step()
+        for i in range(args.warmup + args.profile_steps):
+            rotating(i) if rotating is not None else step()  # the launches the roofline times
         torch.cuda.synchronize()
         print(json.dumps({"profile_steps": args.profile_steps, "workload": name}))
         return
@@ -793,6 +802,30 @@ def generic(args, torch, pkv, step, nbytes, kernel, name, dtype, units, unit_nam
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
     gbps = nbytes / (ms * 1e-3) / 1e9
+    # cold: the 256 MB Infinity Cache flushed before every call (a working set
+    # below its size is otherwise partly served from it); the roofline uses this
+    tc = Timer(torch, stream)
+    if rotating is not None:
+        for i in range(8):
+            rotating(i)
+        tc.start()
+        for i in range(args.steps):
+            rotating(i)
+        tc.stop()
+        torch.cuda.synchronize()
+        cold_ms = tc.mean_ms() / args.steps
+    else:
+        flush_src = torch.empty(MALL_FLUSH_BYTES // 2, dtype=torch.uint8, device="cuda")
+        flush_dst = torch.empty_like(flush_src)
+        for _ in range(max(3, args.steps // 5)):
+            pkv.hbm_copy(flush_dst, flush_src)
+            tc.start()
+            step()
+            tc.stop()
+        torch.cuda.synchronize()
+        del flush_src, flush_dst
+        cold_ms = tc.mean_ms()
+    cold = nbytes / (cold_ms * 1e-3) / 1e9
     print(json.dumps({
         "metric": "paged decode attn KV-read GB/s & % HBM peak; cache-write GB/s (1 MI355X)",
         "value": round(gbps, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -801,8 +834,9 @@ def generic(args, torch, pkv, step, nbytes, kernel, name, dtype, units, unit_nam
         "config": {"workload": name, "bytes_per_step": nbytes},
         "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         unit_name: round(units / (ms * 1e-3), 1),
-        "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "cold": {"ms": round(cold_ms, 5), "GBps": round(cold, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(cold, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(cold / HBM_PEAK_GBPS, 4),
                      "traffic": traffic_from_profiles(kernel, name)},
     }))
 
