@@ -75,6 +75,12 @@ CASES = [
     ("G4 D256 fp8 bs32", [40, 129, 1000], 8, 2, 256, 32, FP8, 40),
     ("G1 D128 bf16 16 kv heads", [70, 3], 16, 16, 128, 16, BF16, 8),
     ("G1 D128 bf16 12 kv heads (idle waves)", [300, 40, 129], 12, 12, 128, 16, BF16, 20),
+    # fp8 caches run four KV heads per workgroup, bf16 two: head counts that leave
+    # idle waves in the last workgroup, or a workgroup of three waves
+    ("G2 D128 fp8 6 kv heads (idle waves)", [300, 40, 129, 1], 12, 6, 128, 16, FP8, 20),
+    ("G2 D128 fp8 3 kv heads (3-wave workgroup)", [500, 17, 64], 6, 3, 128, 16, FP8, 32),
+    ("G1 D64 fp8 5 kv heads", [222, 1000, 2], 5, 5, 64, 16, FP8, 64),
+    ("G1 D64 bf16 3 kv heads (idle wave)", [150, 31, 600], 3, 3, 64, 16, BF16, 40),
     ("G2 D128 fp8 bs32", [31, 32, 33, 700], 16, 8, 128, 32, FP8, 24),
     ("G2 D128 bf16 one seq long", [4096], 16, 8, 128, 16, BF16, 256),
     ("G2 D128 bf16 many short", list(range(1, 65)), 16, 8, 128, 16, BF16, 4),
