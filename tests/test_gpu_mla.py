@@ -95,6 +95,9 @@ CASES = [
     ("bs48", [250, 49, 97], 64, 128, 128, 48),
     ("qk256 v256", [90, 260], 64, 256, 256, 16),
     ("qk32 v32 no RoPE", [40], 0, 32, 32, 16),
+    # narrow values: each merge thread's slice of W_UV is 2 (v8) or 4 (v16) latent rows
+    ("qk16 v8", [70, 3, 300], 64, 16, 8, 16),
+    ("qk24 v16", [129, 1], 0, 24, 16, 16),
 ]
 
 
