@@ -67,6 +67,22 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 #define PA_PREFILL_BUFS 4
 #endif
 constexpr int kWaves = PA_PREFILL_WAVES;
+#ifndef PA_PREFILL_PRIO_QK
+#define PA_PREFILL_PRIO_QK 0
+#endif
+#ifndef PA_PREFILL_PRIO_SM
+#define PA_PREFILL_PRIO_SM 1
+#endif
+#ifndef PA_PREFILL_PRIO_PV
+#define PA_PREFILL_PRIO_PV 0
+#endif
+// Issue priority of a wave in each phase of a key tile: the S product, the
+// softmax, the P.V product.
+constexpr int kPrioQK = PA_PREFILL_PRIO_QK, kPrioSM = PA_PREFILL_PRIO_SM, kPrioPV = PA_PREFILL_PRIO_PV;
+template <int P> __device__ __forceinline__ void set_prio() {
+  static_assert(P >= 0 && P <= 3, "priority 0..3");
+  __builtin_amdgcn_s_setprio(P);
+}
 constexpr int kRowsPerWave = 32;              // two 16-row MFMA blocks
 constexpr int kRows = kWaves * kRowsPerWave;  // (token, head) rows per workgroup
 constexpr int kKeys = PA_PREFILL_KEYS;        // positions per key tile
@@ -426,6 +442,7 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
       for (int kb = 0; kb < kKB; ++kb) kb_ok[kb] = (okbits >> kb) & 1;
     }
     // S^T: sc[rb][kb] holds keys 16kb + 4lg + r of row (rb, li)
+    set_prio<kPrioQK>();
     f32x4 sc[2][kKB];
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb) {
@@ -438,6 +455,7 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
         sc[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[1][s], sc[1][kb], 0, 0, 0);
       }
     }
+    set_prio<kPrioSM>();
     constexpr int kSt = kKeys / 32;  // 32-key steps of P.V
     bf16x8 pop[2][kSt];  // A operands of P.V: [rb][32-key step]
 #pragma unroll
@@ -494,6 +512,7 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
           for (int r = 0; r < 4; ++r) acc[rb][cb][r] *= al[r];
       }
     }
+    set_prio<kPrioPV>();
     // O += P V, V's operand by transposing reads (lane m of a 16-lane group
     // reads row kbase + m/4, columns 16cb + 4(m%4) .. +3, kbase = 32st + 4g,
     // then + 16); the two reads are the operand's low and high halves.
