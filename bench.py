@@ -10,7 +10,8 @@ Prints ONE JSON line. ``value`` is the step's KV-read throughput: the K/V bytes
 attention must read (2 * sum(ctx) * H_KV * d_h * 2 B) divided by the measured
 time per step (write + attention). ``roofline`` is for the dominant kernel
 (decode attention) against MI355X's 8 TB/s; ``cpu_baseline`` is the CPU oracle
-timed on this host on the same step.
+timed on this host on the same step; ``bulk_cache_write`` is the 32,768-token
+bf16 -> fp8 cache write measured in the same run with a cold Infinity Cache.
 
 Other workloads (parity-test configurations, for measurement only):
 ``--workload prefill_fp8 | decode_fp8_b256 | mla_concat_swa``.
@@ -274,15 +275,19 @@ def run_decode(args, torch, pkv, workloads, w, metric_name):
         "attention": {"ms": round(attn_ms, 5), "bytes": attn_bytes,
                       "GBps": round(achieved, 2), "cold_ms": round(cold_ms, 5),
                       "cold_GBps": round(attn_bytes / (cold_ms * 1e-3) / 1e9, 2)},
-        "cache_write": {"ms": round(write_ms, 5), "bytes": write_bytes,
-                        "GBps": round(write_bytes / (write_ms * 1e-3) / 1e9, 2),
-                        "tokens": w.num_seqs},
+        "new_token_write": {"ms": round(write_ms, 5), "bytes": write_bytes,
+                            "GBps": round(write_bytes / (write_ms * 1e-3) / 1e9, 2),
+                            "tokens": w.num_seqs},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic_from_profiles("decode_attention", w.name)},
         "hbm_copy_GBps": round(copy_gbps, 1),
         "frac_of_copy": round(achieved / copy_gbps, 4),
     }
+    if args.workload == "decode_b64":
+        # the cache-write target is quoted on the bulk write (a 64-token write is
+        # launch-latency bound), so the default line carries it too
+        res["bulk_cache_write"] = measure_bulk_write(args, torch, pkv, workloads)
     if not args.no_cpu_baseline:
         import oracle
         res["cpu_baseline"] = cpu_baseline_decode(torch, t, w, oracle)
@@ -326,14 +331,16 @@ def traffic_from_profiles(kernel: str, workload: str):
 # other workloads (measurement of the parity-test configurations)
 # --------------------------------------------------------------------------- #
 
-def run_prefill_fp8(args, torch, pkv, workloads):
+def bulk_write_setup(torch, pkv, workloads):
+    """The bulk bf16 -> fp8 write (32,768 tokens, 5% skipped) on four independent
+    source/cache sets (191 MB each): calls that rotate over them find none of
+    their data in the 256 MB Infinity Cache. Returns (call(i), algorithmic bytes,
+    tokens)."""
     w = workloads.prefill_write_fp8()
     T, H, D, BS, NB = w["num_tokens"], w["num_heads"], w["head_size"], w["block_size"], w["num_blocks"]
     slots = torch.from_numpy(w["slot_mapping"]).cuda()
     ks = torch.tensor([w["k_scale"]], device="cuda")
     vs = torch.tensor([w["v_scale"]], device="cuda")
-    # four independent source/cache sets (191 MB each): calls that rotate over
-    # them find none of their data in the 256 MB Infinity Cache
     sets = []
     for i in range(4):
         key = workloads.device_normal((T, H, D), torch.bfloat16, "cuda", w["seed"], std=w["std"])
@@ -346,10 +353,36 @@ def run_prefill_fp8(args, torch, pkv, workloads):
         pkv.reshape_and_cache(key, val, kc, vc, slots, k_scale=ks, v_scale=vs)
 
     kept = int((w["slot_mapping"] >= 0).sum())
-    nbytes = 8 * T + kept * 2 * H * D * (2 + 1)
-    return generic(args, torch, pkv, lambda: call(0), nbytes, "reshape_and_cache",
-                   "bulk_prefill_write_32768_bf16_to_fp8", "fp8_e4m3fn", T, "tokens_per_s",
-                   rotating=call)
+    return call, 8 * T + kept * 2 * H * D * (2 + 1), T
+
+
+BULK_WRITE_NAME = "bulk_prefill_write_32768_bf16_to_fp8"
+
+
+def run_prefill_fp8(args, torch, pkv, workloads):
+    call, nbytes, T = bulk_write_setup(torch, pkv, workloads)
+    return generic(args, torch, pkv, lambda: call(0), nbytes, "reshape_and_cache", BULK_WRITE_NAME,
+                   "fp8_e4m3fn", T, "tokens_per_s", rotating=call)
+
+
+def measure_bulk_write(args, torch, pkv, workloads):
+    """The cache-write target's workload measured beside the decode step: K calls
+    back to back rotating over the four sets (cold Infinity Cache)."""
+    call, nbytes, T = bulk_write_setup(torch, pkv, workloads)
+    stream = torch.cuda.current_stream()
+    for i in range(max(8, args.warmup)):
+        call(i)
+    tm = Timer(torch, stream)
+    tm.start()
+    for i in range(args.steps):
+        call(i)
+    tm.stop()
+    torch.cuda.synchronize()
+    ms = tm.mean_ms() / args.steps
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": BULK_WRITE_NAME, "ms": round(ms, 5), "bytes": nbytes, "GBps": round(gbps, 2),
+            "frac": round(gbps / HBM_PEAK_GBPS, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
+            "traffic": traffic_from_profiles("reshape_and_cache", BULK_WRITE_NAME)}
 
 
 def run_mla(args, torch, pkv, workloads):
