@@ -579,9 +579,9 @@ def run_engine_decode(args, torch, pkv, workloads):
     stream = torch.cuda.current_stream()
 
     def step():
-        d = stager.step(seqs, ones)
+        d = stager.step(seqs, ones, stream=stream)
         pkv.decode_step(nk, nv, d.slot_mapping, out, q, kc, vc, d.block_tables, d.context_lens,
-                        w.softmax_scale, workspace=ws)
+                        w.softmax_scale, workspace=ws, stream=stream)
         lens[:] += 1
         return d
 

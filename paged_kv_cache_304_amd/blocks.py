@@ -138,7 +138,13 @@ class StepStager:
         self.devs = [torch.empty(n, dtype=torch.uint8, device=device) for _ in range(depth)]
         self.dev = self.devs[0]
         self.copy_stream = torch.cuda.Stream(device=device) if overlap else None
-        self.consumed = [None] * depth      # recorded after the kernels that read pair i
+        # per pair: an event recorded after the kernels that read it, and one after
+        # its upload (created once and re-recorded: a wait or sync binds to the
+        # latest record, which is all a step needs)
+        self.consumed = [torch.cuda.Event() for _ in range(depth)]
+        self.recorded = [False] * depth
+        self.uploaded = [torch.cuda.Event() for _ in range(depth)]
+        self._views = {}                    # (pair, rows, tokens) -> device views
         self.k = 0
 
     def step(self, seqs, num_new, pad_seqs=None, pad_tokens=None, stream=None) -> DeviceStep:
@@ -146,29 +152,32 @@ class StepStager:
         st = stream or torch.cuda.current_stream()
         depth = len(self.host)
         if self.k > 0:                      # everything enqueued so far read the previous pair
-            ev = torch.cuda.Event()
-            ev.record(st)
-            self.consumed[(self.k - 1) % depth] = ev
+            j = (self.k - 1) % depth
+            self.consumed[j].record(st)
+            self.recorded[j] = True
         i = self.k % depth
         self.k += 1
-        if self.consumed[i] is not None:
+        if self.recorded[i]:
             self.consumed[i].synchronize()  # its last kernels (and so its upload) are done
         h, d = self.host[i], self.devs[i]
         rows, toks, real = self.bm.plan_into(h.data_ptr(), h.numel(), seqs, num_new, pad_seqs, pad_tokens)
         cs = self.copy_stream or st
         check(lib.pa_bm_upload(self.bm._h, h.data_ptr(), d.data_ptr(), rows, cs.cuda_stream))
         if self.copy_stream is not None:
-            up = torch.cuda.Event()
+            up = self.uploaded[i]
             up.record(cs)
             st.wait_event(up)
-        lay, W = self.bm.layout, self.bm.width
         self.dev = d
+        v = self._views.get((i, rows, toks))
+        if v is None:
+            lay, W = self.bm.layout, self.bm.width
 
-        def view(off, count, dt, itemsize):
-            return d[off:off + count * itemsize].view(dt)
-        return DeviceStep(
-            slot_mapping=view(lay.slot_mapping, toks, torch.int64, 8),
-            block_tables=view(lay.block_tables, rows * W, torch.int32, 4).view(rows, W),
-            context_lens=view(lay.context_lens, rows, torch.int32, 4),
-            cu_seqlens_q=view(lay.cu_seqlens_q, rows + 1, torch.int32, 4),
-            num_seqs=rows, num_tokens=toks, real_tokens=real)
+            def view(off, count, dt, itemsize):
+                return d[off:off + count * itemsize].view(dt)
+            v = (view(lay.slot_mapping, toks, torch.int64, 8),
+                 view(lay.block_tables, rows * W, torch.int32, 4).view(rows, W),
+                 view(lay.context_lens, rows, torch.int32, 4),
+                 view(lay.cu_seqlens_q, rows + 1, torch.int32, 4))
+            self._views[(i, rows, toks)] = v
+        return DeviceStep(slot_mapping=v[0], block_tables=v[1], context_lens=v[2], cu_seqlens_q=v[3],
+                          num_seqs=rows, num_tokens=toks, real_tokens=real)
