@@ -144,16 +144,6 @@ def decode_bytes(w):
 CPU_BASELINE_MIN_S = 10.0  # each CPU baseline repeats its sample for at least this long
 
 
-def oracle_threads() -> int:
-    """Threads the (OpenMP) oracle runs with: OMP_NUM_THREADS if set, else the
-    cores this process may use."""
-    try:
-        n = int(os.environ.get("OMP_NUM_THREADS", "").split(",")[0])
-    except ValueError:
-        n = 0
-    return n if n > 0 else cpu_cores()
-
-
 def repeat_for(fn, min_s=CPU_BASELINE_MIN_S):
     """Run fn until at least min_s seconds have passed; (runs, seconds)."""
     n, t0 = 0, time.perf_counter()
@@ -182,12 +172,19 @@ def cpu_baseline_decode(torch, t, w, oracle):
                                  k_scale=w.k_scale, v_scale=w.v_scale)
         oracle.decode_attention(q, oracle.BF16, kc, vc, cdt, w.block_tables, w.context_lens,
                                 w.softmax_scale, w.k_scale, w.v_scale)
+    threads = oracle.max_threads()
     n, dt = repeat_for(step)
-    return {"value": round(n * kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": oracle_threads(),
-            "kind": "oracle",
-            "sample": f"the whole step ({w.num_seqs} sequences, {int(w.context_lens.sum())} cached "
-                      f"tokens): oracle write of the new tokens + fp64 attention, {n} steps in "
-                      f"{dt:.1f} s, KV-read bytes / time"}
+    oracle.set_num_threads(1)  # the same sample on one thread
+    try:
+        n1, dt1 = repeat_for(step)
+    finally:
+        oracle.set_num_threads(threads)
+    sample = (f"the whole step ({w.num_seqs} sequences, {int(w.context_lens.sum())} cached tokens): "
+              "oracle write of the new tokens + fp64 attention, KV-read bytes / time")
+    return {"value": round(n * kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "sample": f"{sample}; {n} steps in {dt:.1f} s",
+            "single_thread": {"value": round(n1 * kv_bytes / dt1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                              "sample": f"{n1} steps in {dt1:.1f} s"}}
 
 
 def run_decode(args, torch, pkv, workloads, w, metric_name):
@@ -526,7 +523,7 @@ def cpu_baseline_prefill(torch, q, kc, vc, w, oracle):
         qh, oracle.BF16, w["cu_seqlens_q"], kh, vh, oracle.BF16, w["block_tables"], w["context_lens"],
         w["softmax_scale"]))
     flops = prefill_flops(w)
-    return {"value": round(n * flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle_threads(),
+    return {"value": round(n * flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.max_threads(),
             "kind": "oracle",
             "sample": f"the whole call ({w['num_tokens']} query rows x {w['num_q_heads']} heads, "
                       f"{flops / 1e9:.1f} GFLOP), {n} calls in {dt:.1f} s"}
@@ -693,7 +690,7 @@ def cpu_baseline_engine(torch, w, W, oracle, kc, vc, q, nk, nv, lens):
     n, dt = repeat_for(attend)
     per_step = plan_s + dt / n
     kv = int(2 * cl.astype(np.int64).sum() * w.num_kv_heads * w.head_size * 2)
-    return {"value": round(kv / per_step / 1e9, 4), "unit": "GB/s", "cores": oracle_threads(),
+    return {"value": round(kv / per_step / 1e9, 4), "unit": "GB/s", "cores": oracle.max_threads(),
             "kind": "oracle",
             "sample": f"one engine step ({B} sequences, {int(cl.sum())} tokens): oracle block-pool "
                       f"planning ({plan_s * 1e6:.0f} us, once) + write + fp64 attention ({n} times in "
@@ -821,7 +818,7 @@ def cpu_baseline_mla(torch, w, oracle, cache, q_nope, q_rope, w_uk, w_uv):
                                                  w["softmax_scale"]))
     row = w["kv_lora_rank"] + w["rope_dim"]
     nbytes = int(ctx.astype(np.int64).sum()) * row * 2
-    return {"value": round(n * nbytes / dt / 1e9, 5), "unit": "GB/s", "cores": oracle_threads(),
+    return {"value": round(n * nbytes / dt / 1e9, 5), "unit": "GB/s", "cores": oracle.max_threads(),
             "kind": "oracle",
             "sample": f"sequences 0..3 of the batch ({int(ctx.sum())} cached tokens): fp64 MLA decode with "
                       f"K/V up-projected per position, {n} runs in {dt:.1f} s, latent-read bytes / time"}

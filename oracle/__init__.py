@@ -47,6 +47,10 @@ def _load():
         build()
     lib = ctypes.CDLL(_LIB_PATH)
     P, I64, I32, F64 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double
+    lib.orc_max_threads.argtypes = []
+    lib.orc_max_threads.restype = I32
+    lib.orc_set_num_threads.argtypes = [I32]
+    lib.orc_set_num_threads.restype = None
     lib.orc_e4m3fn_to_f64.argtypes = [ctypes.c_uint8]
     lib.orc_e4m3fn_to_f64.restype = F64
     lib.orc_f32_to_bf16.argtypes = [ctypes.c_float]
@@ -74,6 +78,16 @@ def _load():
     lib.orc_mla_decode.restype = None
     _lib = lib
     return lib
+
+
+def max_threads() -> int:
+    """Threads the oracle's parallel loops run with."""
+    return int(_load().orc_max_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads for the oracle's parallel loops from now on (timing only)."""
+    _load().orc_set_num_threads(int(n))
 
 
 def _ptr(a):

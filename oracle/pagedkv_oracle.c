@@ -80,9 +80,14 @@
  * (no fast-math: IEEE single division and round-to-nearest are required).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+
+/* Threads of the OpenMP loops below (for timing the oracle; no effect on results). */
+int orc_max_threads(void) { return omp_get_max_threads(); }
+void orc_set_num_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
 
 /* dtype codes of this file (independent of the product library's) */
 enum { ORC_BF16 = 0, ORC_F32 = 2, ORC_FP8_E4M3FN = 3 };
