@@ -43,7 +43,7 @@ def parse():
     # memory path warms up), so the default warm-up covers well past that
     p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--workload", default="decode_b64",
-                   choices=["decode_b64", "prefill_fp8", "decode_fp8_b256", "mla_concat_swa",
+                   choices=["decode_b64", "decode_b64_tp2", "prefill_fp8", "decode_fp8_b256", "mla_concat_swa",
                             "mla_fused", "prefill_chunks", "engine_decode_b64",
                             "mla_decode_b64"])
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -824,6 +824,16 @@ def cpu_baseline_mla(torch, w, oracle, cache, q_nope, q_rope, w_uk, w_uv):
                       f"K/V up-projected per position, {n} runs in {dt:.1f} s, latent-read bytes / time"}
 
 
+def run_decode_tp2(args, torch, pkv, workloads):
+    """The batch-64 decode step at one GPU's share under 2-way tensor parallelism:
+    4 KV heads and their 8 q heads per GPU, same contexts and block tables."""
+    import dataclasses
+    w = workloads.qwen3_decode_b64(num_q_heads=8, num_kv_heads=4)
+    w = dataclasses.replace(w, name="qwen3_0.6b_decode_b64_bf16_tp2_shard")
+    return run_decode(args, torch, pkv, workloads, w,
+                      "paged decode attn KV-read GB/s & % HBM peak; cache-write GB/s (1 MI355X)")
+
+
 def run_decode_fp8(args, torch, pkv, workloads):
     w = workloads.mixed_decode_fp8()
     return run_decode(args, torch, pkv, workloads, w,
@@ -910,6 +920,8 @@ def main():
     metric = "paged decode attn KV-read GB/s & % HBM peak; cache-write GB/s (1 MI355X)"
     if args.workload == "decode_b64":
         run_decode(args, torch, pkv, workloads, workloads.qwen3_decode_b64(), metric)
+    elif args.workload == "decode_b64_tp2":
+        run_decode_tp2(args, torch, pkv, workloads)
     elif args.workload == "decode_fp8_b256":
         run_decode_fp8(args, torch, pkv, workloads)
     elif args.workload == "prefill_fp8":

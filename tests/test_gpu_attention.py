@@ -81,6 +81,8 @@ CASES = [
     ("G2 D128 fp8 3 kv heads (3-wave workgroup)", [500, 17, 64], 6, 3, 128, 16, FP8, 32),
     ("G1 D64 fp8 5 kv heads", [222, 1000, 2], 5, 5, 64, 16, FP8, 64),
     ("G1 D64 bf16 3 kv heads (idle wave)", [150, 31, 600], 3, 3, 64, 16, BF16, 40),
+    # one GPU's share of the batch-64 workload under 2-way tensor parallelism
+    ("G2 D128 bf16 tp2 shard", [1469, 1841, 856, 3464, 17], 8, 4, 128, 16, BF16, 224),
     ("G2 D128 fp8 bs32", [31, 32, 33, 700], 16, 8, 128, 32, FP8, 24),
     ("G2 D128 bf16 one seq long", [4096], 16, 8, 128, 16, BF16, 256),
     ("G2 D128 bf16 many short", list(range(1, 65)), 16, 8, 128, 16, BF16, 4),
