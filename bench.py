@@ -14,7 +14,8 @@ timed on this host on the same step; ``bulk_cache_write`` is the 32,768-token
 bf16 -> fp8 cache write measured in the same run with a cold Infinity Cache.
 
 Other workloads (parity-test configurations, for measurement only):
-``--workload prefill_fp8 | decode_fp8_b256 | mla_concat_swa``.
+``--workload decode_fp8_b256 | decode_b64_tp2 | prefill_fp8 | mla_concat_swa | mla_fused |
+prefill_chunks | engine_decode_b64 | mla_decode_b64``.
 """
 from __future__ import annotations
 
@@ -39,8 +40,8 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
-    # the first ~10 ms of work after start-up run up to 15% slower (the
-    # memory path warms up), so the default warm-up covers well past that
+    # kernels in the first ~10 ms of GPU work after start-up were measured up
+    # to 15% slower, so the default warm-up covers well past that
     p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--workload", default="decode_b64",
                    choices=["decode_b64", "decode_b64_tp2", "prefill_fp8", "decode_fp8_b256", "mla_concat_swa",
@@ -156,7 +157,8 @@ def repeat_for(fn, min_s=CPU_BASELINE_MIN_S):
 
 
 def cpu_baseline_decode(torch, t, w, oracle):
-    """The oracle (all host threads) on the same step: new-token write + attention."""
+    """The oracle on the same step (new-token write + attention), with all host
+    threads and with one."""
     cdt = oracle.FP8_E4M3FN if w.cache_dtype == "fp8" else oracle.BF16
     raw = torch.uint8 if w.cache_dtype == "fp8" else torch.int16
     npv = np.uint8 if w.cache_dtype == "fp8" else np.uint16
