@@ -72,6 +72,9 @@ class Timer:
     def mean_ms(self):
         return float(np.mean([a.elapsed_time(b) for a, b in self.pairs]))
 
+    def percentiles_ms(self, qs=(10, 50, 90)):
+        return [round(float(x), 5) for x in np.percentile([a.elapsed_time(b) for a, b in self.pairs], qs)]
+
 
 def cpu_cores():
     try:
@@ -230,7 +233,7 @@ def run_decode(args, torch, pkv, workloads, w, metric_name):
     flush_src = torch.empty(MALL_FLUSH_BYTES // 2, dtype=torch.uint8, device="cuda")
     flush_dst = torch.empty_like(flush_src)
     tc = Timer(torch, stream)
-    for _ in range(max(3, args.steps // 5)):
+    for _ in range(max(10, args.steps // 2)):
         pkv.hbm_copy(flush_dst, flush_src)
         tc.start()
         decode_attn(pkv, t, w)
@@ -273,7 +276,8 @@ def run_decode(args, torch, pkv, workloads, w, metric_name):
         "tokens_per_s": round(w.num_seqs / (ms_per_step * 1e-3), 1),
         "attention": {"ms": round(attn_ms, 5), "bytes": attn_bytes,
                       "GBps": round(achieved, 2), "cold_ms": round(cold_ms, 5),
-                      "cold_GBps": round(attn_bytes / (cold_ms * 1e-3) / 1e9, 2)},
+                      "cold_GBps": round(attn_bytes / (cold_ms * 1e-3) / 1e9, 2),
+                      "cold_p10_p50_p90_ms": tc.percentiles_ms()},
         "new_token_write": {"ms": round(write_ms, 5), "bytes": write_bytes,
                             "GBps": round(write_bytes / (write_ms * 1e-3) / 1e9, 2),
                             "tokens": w.num_seqs},
