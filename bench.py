@@ -33,6 +33,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0
 MALL_FLUSH_BYTES = 1 << 30   # > 256 MB Infinity Cache
+READ_PROBE_BYTES = 2 << 30   # streaming-read reference size
 COPY_CAL_BYTES = 512 << 20
 
 
@@ -248,6 +249,19 @@ def run_decode(args, torch, pkv, workloads, w, metric_name):
     torch.cuda.synchronize()
     copy_gbps = 2 * flush_src.numel() / (tcopy.mean_ms() * 1e-3) / 1e9
     del flush_src, flush_dst
+    # (5) the streaming-read reference (2 GiB, well past the Infinity Cache)
+    rd = torch.empty(READ_PROBE_BYTES // 4, dtype=torch.int32, device="cuda")
+    sink = torch.empty((pkv.ops.HBM_READ_SINK_UNITS, 4), dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        pkv.hbm_read(rd, sink)
+    tread = Timer(torch, stream)
+    tread.start()
+    for _ in range(10):
+        pkv.hbm_read(rd, sink)
+    tread.stop()
+    torch.cuda.synchronize()
+    read_gbps = READ_PROBE_BYTES / (tread.mean_ms() / 10 * 1e-3) / 1e9
+    del rd, sink
 
     kv, attn_bytes, write_bytes = decode_bytes(w)
     attn_ms, write_ms, cold_ms = ta.mean_ms() / args.steps, tw.mean_ms() / args.steps, tc.mean_ms()
@@ -286,6 +300,8 @@ def run_decode(args, torch, pkv, workloads, w, metric_name):
                      "traffic": traffic_from_profiles("decode_attention", w.name)},
         "hbm_copy_GBps": round(copy_gbps, 1),
         "frac_of_copy": round(achieved / copy_gbps, 4),
+        "hbm_read_GBps": round(read_gbps, 1),
+        "frac_of_read": round(achieved / read_gbps, 4),
     }
     if args.workload == "decode_b64":
         # the cache-write target is quoted on the bulk write (a 64-token write is

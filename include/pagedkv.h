@@ -369,6 +369,19 @@ pa_status pa_prefill_attention(void* out, pa_dtype out_dtype, int64_t out_token_
 pa_status pa_hbm_copy(void* dst, const void* src, size_t bytes, void* stream);
 
 /*
+ * pa_hbm_read -- streaming read of `bytes` bytes at `src` (measurement utility,
+ * not part of the cache path): the read-only bandwidth reference for the decode
+ * kernels, which read far more than they write. `sink` is caller-owned device
+ * memory of PA_HBM_READ_SINK_UNITS 16-byte units; a call with bytes > 0
+ * overwrites all of them with partial XOR folds of src's 16-byte units, whose
+ * XOR is the XOR of every unit of src (so a check proves every byte was read);
+ * bytes == 0 enqueues nothing. bytes must be a multiple of 16; src and sink
+ * 16-byte aligned. Errors: PA_EINVAL, PA_EHIP.
+ */
+#define PA_HBM_READ_SINK_UNITS 2048
+pa_status pa_hbm_read(const void* src, size_t bytes, void* sink, void* stream);
+
+/*
  * pa_mla_decode_workspace_size -- bytes of device workspace
  * pa_mla_decode_attention needs for these sizes (256-byte aligned); 0 with
  * pa_last_error() set if the shape is unsupported. Pure function.

@@ -16,6 +16,7 @@ from .ops import (  # noqa: F401
     decode_attention_workspace_size,
     decode_step,
     hbm_copy,
+    hbm_read,
     mla_decode_attention,
     mla_decode_workspace_size,
     prefill_attention,

@@ -20,7 +20,7 @@ EXPORTS = ("pa_last_error", "pa_abi_version", "pa_reshape_and_cache", "pa_concat
            "pa_concat_and_cache_mla_k",
            "pa_decode_attention_workspace_size", "pa_decode_attention", "pa_decode_step",
            "pa_prefill_attention",
-           "pa_hbm_copy",
+           "pa_hbm_copy", "pa_hbm_read",
            "pa_bm_create", "pa_bm_destroy", "pa_bm_layout_of", "pa_bm_free_blocks", "pa_bm_seq_len",
            "pa_bm_seq_table", "pa_bm_release", "pa_bm_plan_step", "pa_bm_upload",
            "pa_mla_decode_workspace_size", "pa_mla_decode_attention")
@@ -73,6 +73,8 @@ def _load() -> ctypes.CDLL:
     L.pa_prefill_attention.restype = I32
     L.pa_hbm_copy.argtypes = [P, P, SZ, P]
     L.pa_hbm_copy.restype = I32
+    L.pa_hbm_read.argtypes = [P, SZ, P, P]
+    L.pa_hbm_read.restype = I32
     L.pa_mla_decode_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32, I32, I32]
     L.pa_mla_decode_workspace_size.restype = SZ
     L.pa_mla_decode_attention.argtypes = [P, I32, I64, P, I64, P, I64, I32, P, P, I32, P, I32, I64, I32,

@@ -44,6 +44,34 @@ __global__ __launch_bounds__(256) void hbm_copy_kernel(u32x4* __restrict__ dst,
   for (; i < n16; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
+// Grid-stride streaming read, each unit XOR-folded; a workgroup's folds meet
+// through shuffles and LDS and go to its own sink unit (no atomics: thousands
+// of them on one address would serialise).
+__global__ __launch_bounds__(256) void hbm_read_kernel(const u32x4* __restrict__ src, int64_t n16,
+                                                       u32x4* __restrict__ sink) {
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  u32x4 x = {0u, 0u, 0u, 0u};
+  constexpr int U = 4;  // loads in flight per thread (5.97 TB/s; 8: 5.93, 16: 5.77)
+  for (; i + (U - 1) * stride < n16; i += U * stride) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < U; ++u) x ^= v[u];
+  }
+  for (; i < n16; i += stride) x ^= __builtin_nontemporal_load(src + i);
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x[w] ^= (uint32_t)__shfl_xor((int)x[w], o, 64);
+  }
+  __shared__ u32x4 part[4];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
+}
+
 __global__ void tail_copy_kernel(uint8_t* __restrict__ dst, const uint8_t* __restrict__ src, int n) {
   if ((int)threadIdx.x < n) dst[threadIdx.x] = src[threadIdx.x];
 }
@@ -53,6 +81,20 @@ __global__ void tail_copy_kernel(uint8_t* __restrict__ dst, const uint8_t* __res
 extern "C" const char* pa_last_error(void) { return pa::g_error; }
 
 extern "C" int32_t pa_abi_version(void) { return PA_ABI_VERSION; }
+
+extern "C" pa_status pa_hbm_read(const void* src, size_t bytes, void* sink, void* stream) {
+  using namespace pa;
+  clear_error();
+  if (bytes == 0) return PA_OK;
+  if (!src || !sink) return fail(PA_EINVAL, "pa_hbm_read: null pointer");
+  if (!aligned(src, 16) || !aligned(sink, 16)) return fail(PA_EINVAL, "pa_hbm_read: pointers must be 16-byte aligned");
+  if (bytes % 16 != 0) return fail(PA_EINVAL, "pa_hbm_read: bytes must be a multiple of 16");
+  const int64_t n16 = (int64_t)(bytes / 16);
+  // the copy's shape (256 CUs x 8 workgroups); every sink unit gets a fold
+  hbm_read_kernel<<<PA_HBM_READ_SINK_UNITS, 256, 0, reinterpret_cast<hipStream_t>(stream)>>>(
+      reinterpret_cast<const u32x4*>(src), n16, static_cast<u32x4*>(sink));
+  return after_launch("pa_hbm_read");
+}
 
 extern "C" pa_status pa_hbm_copy(void* dst, const void* src, size_t bytes, void* stream) {
   using namespace pa;

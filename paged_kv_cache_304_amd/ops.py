@@ -279,6 +279,25 @@ def hbm_copy(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:
     check(lib.pa_hbm_copy(dst.data_ptr(), src.data_ptr(), n, _stream(stream)))
 
 
+HBM_READ_SINK_UNITS = 2048  # PA_HBM_READ_SINK_UNITS
+
+
+def hbm_read(src: torch.Tensor, sink: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Streaming read of ``src``'s bytes (read-bandwidth reference kernel). Returns
+    ``sink`` (int32 [2048, 4], allocated if not given): partial XOR folds of src's
+    16-byte units, whose XOR over the first axis is the XOR of all of them."""
+    _on_gpu(src, sink)
+    n = src.numel() * src.element_size()
+    if not src.is_contiguous() or n % 16 != 0:
+        raise ValueError("src must be contiguous with a multiple of 16 bytes")
+    if sink is None:
+        sink = torch.empty((HBM_READ_SINK_UNITS, 4), dtype=torch.int32, device=src.device)
+    elif sink.dtype != torch.int32 or sink.numel() != 4 * HBM_READ_SINK_UNITS or not sink.is_contiguous():
+        raise ValueError("sink must be contiguous int32 [2048, 4]")
+    check(lib.pa_hbm_read(src.data_ptr(), n, sink.data_ptr(), _stream(stream)))
+    return sink
+
+
 def mla_decode_workspace_size(num_seqs: int, num_heads: int, qk_nope_dim: int, rope_dim: int,
                               kv_lora_rank: int, v_dim: int, max_blocks_per_seq: int,
                               block_size: int) -> int:

@@ -273,6 +273,14 @@ def test_mla_decode_empty_and_workspace_size(L):
     assert f(64, 8, 128, 64, 512, 128, 256, 16) == 0 and L.last_error()
 
 
+def test_hbm_read_rejects(L):
+    assert L.lib.pa_hbm_read(None, 64, 1 << 20, None) == L.PA_EINVAL
+    assert L.lib.pa_hbm_read(1 << 20, 64, None, None) == L.PA_EINVAL
+    assert L.lib.pa_hbm_read((1 << 20) + 8, 64, 1 << 21, None) == L.PA_EINVAL  # misaligned
+    assert L.lib.pa_hbm_read(1 << 20, 40, 1 << 21, None) == L.PA_EINVAL        # not whole 16-byte units
+    assert L.lib.pa_hbm_read(1 << 20, 0, 1 << 21, None) == L.PA_OK             # empty: nothing enqueued
+
+
 def test_hbm_copy_rejects(L):
     assert L.lib.pa_hbm_copy(None, 1 << 20, 64, None) == L.PA_EINVAL
     assert L.lib.pa_hbm_copy(1 << 20, (1 << 20) + 16, 64, None) == L.PA_EINVAL  # overlap
