@@ -350,6 +350,13 @@ def traffic_from_profiles(kernel: str, workload: str):
 # other workloads (measurement of the parity-test configurations)
 # --------------------------------------------------------------------------- #
 
+def bulk_write_bytes(w) -> int:
+    """Algorithmic bytes of the bulk write: every token's slot, and for each kept
+    token its bf16 K and V rows read and its fp8 K and V rows written."""
+    kept = int((w["slot_mapping"] >= 0).sum())
+    return 8 * w["num_tokens"] + kept * 2 * w["num_heads"] * w["head_size"] * (2 + 1)
+
+
 def bulk_write_setup(torch, pkv, workloads):
     """The bulk bf16 -> fp8 write (32,768 tokens, 5% skipped) on four independent
     source/cache sets (191 MB each): calls that rotate over them find none of
@@ -371,8 +378,7 @@ def bulk_write_setup(torch, pkv, workloads):
         key, val, kc, vc = sets[i % len(sets)]
         pkv.reshape_and_cache(key, val, kc, vc, slots, k_scale=ks, v_scale=vs)
 
-    kept = int((w["slot_mapping"] >= 0).sum())
-    return call, 8 * T + kept * 2 * H * D * (2 + 1), T
+    return call, bulk_write_bytes(w), T
 
 
 BULK_WRITE_NAME = "bulk_prefill_write_32768_bf16_to_fp8"

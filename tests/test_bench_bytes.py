@@ -64,3 +64,14 @@ def walk_prefill_flops(w):
 def test_prefill_flops_match_a_walk_of_the_workload():
     w = workloads.prefill_chunks(num_seqs=3, chunk=40, prefix_hi=90, num_blocks=64)
     assert bench.prefill_flops(w) == walk_prefill_flops(w)
+
+
+def test_bulk_write_bytes_match_a_walk_of_the_workload():
+    w = workloads.prefill_write_fp8(num_tokens=300)
+    nbytes = 0
+    for t in range(w["num_tokens"]):
+        nbytes += 8  # the token's slot
+        if w["slot_mapping"][t] >= 0:
+            for _h in range(w["num_heads"]):
+                nbytes += 2 * w["head_size"] * (2 + 1)  # K and V: bf16 row in, fp8 row out
+    assert bench.bulk_write_bytes(w) == nbytes
