@@ -75,3 +75,20 @@ def test_bulk_write_bytes_match_a_walk_of_the_workload():
             for _h in range(w["num_heads"]):
                 nbytes += 2 * w["head_size"] * (2 + 1)  # K and V: bf16 row in, fp8 row out
     assert bench.bulk_write_bytes(w) == nbytes
+
+
+def test_mla_algorithmic_bytes_match_a_walk_of_the_workload():
+    """Latent rows (latent + RoPE part, bf16) once per cached position, one table
+    entry per block, the lengths, W_UK and W_UV once, q (nope + RoPE) in and the
+    output out once per head; the workspace of the design is not counted."""
+    w = workloads.mla_decode_b64(num_seqs=3, ctx_lo=5, ctx_hi=70, num_blocks=64, width=8)
+    H, QK, R, DC, DV = w["num_heads"], w["qk_nope_dim"], w["rope_dim"], w["kv_lora_rank"], w["v_dim"]
+    nbytes = DC * H * QK * 2 + DC * H * DV * 2  # the two up-projections, bf16
+    for b in range(w["num_seqs"]):
+        blocks = set()
+        for p in range(int(w["context_lens"][b])):
+            nbytes += (DC + R) * 2
+            blocks.add(int(w["block_tables"][b][p // w["block_size"]]))
+        nbytes += 4 * len(blocks) + 4
+        nbytes += H * ((QK + R) * 2 + DV * 2)
+    assert bench.mla_bytes(w)["algorithmic"] == nbytes
