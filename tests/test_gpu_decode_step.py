@@ -117,6 +117,11 @@ CASES = [
     ("G2 D128 bf16 empty sequences", [0, 40, 0, 1, 90], 16, 8, 128, 16, BF16, "table"),
     ("G2 D128 bf16 skipped writes", [10, 40, 70, 33], 16, 8, 128, 16, BF16, "skip"),
     ("G2 D128 fp8 writes elsewhere", [10, 40, 70, 33], 16, 8, 128, 16, FP8, "elsewhere"),
+    # fp8 caches run four KV heads per workgroup: six heads leave two waves idle,
+    # three make a three-wave workgroup
+    ("G2 D128 fp8 6 kv heads (idle waves)", [17, 300, 1, 129], 12, 6, 128, 16, FP8, "table"),
+    ("G2 D128 fp8 3 kv heads", [64, 65, 500], 6, 3, 128, 16, FP8, "table"),
+    ("G1 D128 fp8 bs32 skipped writes", [33, 2, 250], 8, 8, 128, 32, FP8, "skip"),
 ]
 
 
