@@ -257,6 +257,35 @@ pa_status pa_decode_attention(void* out, pa_dtype out_dtype, int64_t out_seq_str
                               void* stream);
 
 /*
+ * pa_decode_attention_noalloc -- pa_decode_attention for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Same arguments and results as
+ * pa_decode_attention without the workspace: the per-split partial results go
+ * to a fixed device array of pa_decode_attention_noalloc_max_workspace()
+ * bytes (64 MiB) inside the library, one copy per GPU, held until the process
+ * ends. The call allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine); its first call on a device looks up that device's copy
+ * of the array (hipGetSymbolAddress).
+ * Every call on one GPU shares that GPU's array, and the array keeps the last
+ * call's contents (the kernels need nothing from it on entry): calls that
+ * overlap in time on one GPU (different streams, or different host threads
+ * without ordering) race and must not be made.
+ * Errors: those of pa_decode_attention; PA_EWORKSPACE when
+ * pa_decode_attention_workspace_size() of these sizes exceeds the array.
+ */
+size_t pa_decode_attention_noalloc_max_workspace(void);
+pa_status pa_decode_attention_noalloc(void* out, pa_dtype out_dtype, int64_t out_seq_stride,
+                                      const void* q, pa_dtype q_dtype, int64_t q_seq_stride,
+                                      const void* key_cache, const void* value_cache,
+                                      pa_dtype cache_dtype, int64_t num_blocks,
+                                      int32_t block_size, int64_t block_stride,
+                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t* context_lens, int32_t num_seqs,
+                                      int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_size, float softmax_scale,
+                                      const float* k_scale, const float* v_scale, void* stream);
+
+/*
  * pa_decode_step -- one decode step in one call: the new tokens' K/V are
  * written into the paged caches and single-token decode attention runs over
  * the contexts that now include them. Launch shapes depend on host arguments

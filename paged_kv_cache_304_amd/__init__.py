@@ -13,6 +13,7 @@ from .ops import (  # noqa: F401
     concat_and_cache_mla_k,
     concat_and_cast_mla_k,
     decode_attention,
+    decode_attention_noalloc,
     decode_attention_workspace_size,
     decode_step,
     hbm_copy,

@@ -19,6 +19,7 @@ STATUS_NAMES = {PA_OK: "PA_OK", PA_EINVAL: "PA_EINVAL", PA_EDTYPE: "PA_EDTYPE",
 EXPORTS = ("pa_last_error", "pa_abi_version", "pa_reshape_and_cache", "pa_concat_and_cast_mla_k",
            "pa_concat_and_cache_mla_k",
            "pa_decode_attention_workspace_size", "pa_decode_attention", "pa_decode_step",
+           "pa_decode_attention_noalloc", "pa_decode_attention_noalloc_max_workspace",
            "pa_prefill_attention",
            "pa_hbm_copy", "pa_hbm_read",
            "pa_bm_create", "pa_bm_destroy", "pa_bm_layout_of", "pa_bm_free_blocks", "pa_bm_seq_len",
@@ -65,6 +66,11 @@ def _load() -> ctypes.CDLL:
     L.pa_decode_attention.argtypes = [P, I32, I64, P, I32, I64, P, P, I32, I64, I32, I64, P, I32, P,
                                       I32, I32, I32, I32, F, P, P, P, SZ, P]
     L.pa_decode_attention.restype = I32
+    L.pa_decode_attention_noalloc.argtypes = [P, I32, I64, P, I32, I64, P, P, I32, I64, I32, I64, P,
+                                              I32, P, I32, I32, I32, I32, F, P, P, P]
+    L.pa_decode_attention_noalloc.restype = I32
+    L.pa_decode_attention_noalloc_max_workspace.argtypes = []
+    L.pa_decode_attention_noalloc_max_workspace.restype = SZ
     L.pa_decode_step.argtypes = [P, P, I32, I64, I64, P, P, I32, I64, P, I32, I64, P, P, I32, I64, I32,
                                  I64, P, I32, P, I32, I32, I32, I32, F, P, P, P, SZ, P]
     L.pa_decode_step.restype = I32

@@ -41,6 +41,7 @@
 #include <math.h>
 
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "pa_device.h"
@@ -1390,4 +1391,72 @@ extern "C" pa_status pa_decode_step(const void* new_k, const void* new_v, pa_dty
                            cache_dtype, num_blocks, block_size, block_stride, block_tables, max_blocks_per_seq,
                            context_lens, num_seqs, num_q_heads, num_kv_heads, head_size, softmax_scale, k_scale,
                            v_scale, workspace, workspace_bytes, &nt, stream);
+}
+
+// ---------------------------------------------------------------------------
+// pa_decode_attention_noalloc: pa_decode_attention with its workspace in a
+// fixed device array instead of a caller buffer, for callers that cannot
+// allocate. The array is a file-scope __device__ object: every GPU the library
+// runs on holds its own copy for the life of the process. Host code never uses
+// the array's name as a device address (on the host that name is only a
+// stand-in): the address is looked up once per device with
+// hipGetSymbolAddress and kept in g_scratch_ptr.
+namespace pa {
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)64 << 20;  // 64 MiB
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch` (looked up on first use per device).
+pa_status scratch_on_current_device(const char* fn, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PA_EHIP, "%s: hipGetDevice failed: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(PA_EUNSUPPORTED, "%s: device index %d >= %d", fn, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(PA_EHIP, "%s: hipGetSymbolAddress of the fixed workspace failed: %s", fn, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return PA_OK;
+}
+
+}  // namespace
+}  // namespace pa
+
+extern "C" size_t pa_decode_attention_noalloc_max_workspace(void) { return pa::kScratchBytes; }
+
+extern "C" pa_status pa_decode_attention_noalloc(void* out, pa_dtype out_dtype, int64_t out_seq_stride, const void* q,
+                                                 pa_dtype q_dtype, int64_t q_seq_stride, const void* key_cache,
+                                                 const void* value_cache, pa_dtype cache_dtype, int64_t num_blocks,
+                                                 int32_t block_size, int64_t block_stride,
+                                                 const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                                 const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                                 int32_t num_kv_heads, int32_t head_size, float softmax_scale,
+                                                 const float* k_scale, const float* v_scale, void* stream) {
+  using namespace pa;
+  clear_error();
+  const char* fn = "pa_decode_attention_noalloc";
+  pa_status s = check_sizes(fn, num_seqs, num_q_heads, num_kv_heads, head_size, max_blocks_per_seq, block_size);
+  if (s != PA_OK) return s;
+  if (num_seqs == 0) return PA_OK;
+  const Plan p = make_plan(num_seqs, num_q_heads, num_kv_heads, head_size, max_blocks_per_seq, block_size);
+  if (p.bytes > kScratchBytes)
+    return fail(PA_EWORKSPACE, "%s: these sizes need %zu bytes of workspace; the fixed workspace holds %zu",
+                fn, p.bytes, kScratchBytes);
+  void* ws = nullptr;
+  s = scratch_on_current_device(fn, &ws);
+  if (s != PA_OK) return s;
+  return decode_common(fn, out, out_dtype, out_seq_stride, q, q_dtype, q_seq_stride, key_cache, value_cache,
+                       cache_dtype, num_blocks, block_size, block_stride, block_tables, max_blocks_per_seq,
+                       context_lens, num_seqs, num_q_heads, num_kv_heads, head_size, softmax_scale, k_scale,
+                       v_scale, ws, kScratchBytes, nullptr, stream);
 }

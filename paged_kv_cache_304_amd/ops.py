@@ -182,6 +182,39 @@ def decode_attention(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tensor
     return out
 
 
+def decode_attention_noalloc(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tensor,
+                             value_cache: torch.Tensor, block_tables: torch.Tensor,
+                             context_lens: torch.Tensor, softmax_scale: float,
+                             k_scale: Optional[torch.Tensor] = None,
+                             v_scale: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """``decode_attention`` with the library's fixed device workspace: neither this
+    function nor the C call allocates. Calls that overlap on one GPU race."""
+    _on_gpu(out, q, key_cache, value_cache, block_tables, context_lens, k_scale, v_scale)
+    B, HQ, D = q.shape
+    NB, BS, HKV, D2 = key_cache.shape
+    if D2 != D or out.shape != q.shape:
+        raise ValueError("q, out and cache head sizes differ")
+    if q.stride(2) != 1 or q.stride(1) != D or out.stride(2) != 1 or out.stride(1) != D:
+        raise ValueError("q and out must be [B, H_Q, D] with contiguous [H_Q, D]")
+    if key_cache.stride(3) != 1 or key_cache.stride(2) != D or key_cache.stride(1) != HKV * D:
+        raise ValueError("cache inner [BS, H_KV, D] must be contiguous")
+    if value_cache.shape != key_cache.shape or value_cache.stride() != key_cache.stride() or \
+            value_cache.dtype != key_cache.dtype:
+        raise ValueError("value_cache must match key_cache")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or \
+            block_tables.shape[0] != B or not block_tables.is_contiguous():
+        raise ValueError("block_tables must be contiguous int32 [B, W]")
+    if context_lens.dtype != torch.int32 or context_lens.numel() != B or \
+            not context_lens.is_contiguous():
+        raise ValueError("context_lens must be contiguous int32 [B]")
+    check(lib.pa_decode_attention_noalloc(
+        out.data_ptr(), _code(out, "out"), out.stride(0), q.data_ptr(), _code(q, "q"), q.stride(0),
+        key_cache.data_ptr(), value_cache.data_ptr(), _code(key_cache, "key_cache"), NB, BS,
+        key_cache.stride(0), block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(),
+        B, HQ, HKV, D, float(softmax_scale), _ptr(k_scale), _ptr(v_scale), _stream(stream)))
+    return out
+
+
 def decode_step(new_k: torch.Tensor, new_v: torch.Tensor, new_slots: torch.Tensor,
                 out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tensor,
                 value_cache: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
