@@ -649,12 +649,13 @@ extern "C" pa_status pa_mla_decode_attention(void* out, pa_dtype out_dtype, int6
   a.out_f32 = out_dtype == PA_F32;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
 
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  mla_absorb_kernel<<<dim3(kHeads, kDC / 64, (unsigned)((num_seqs + 15) / 16)), 256, 0, st>>>(a, row);
   // one workgroup per live piece at most: sum over sequences of ceil(ctx / 256)
-  // <= num_seqs * splits; workgroups past the last live piece exit at once
+  // <= num_seqs * splits; workgroups past the last live piece exit at once.
+  // Checked before the first launch, so a refusal leaves nothing enqueued.
   const int64_t items = (int64_t)num_seqs * p.splits;
   if (items > INT32_MAX / 2) return fail(PA_EINVAL, "%s: too many (sequence, piece) items", fn);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  mla_absorb_kernel<<<dim3(kHeads, kDC / 64, (unsigned)((num_seqs + 15) / 16)), 256, 0, st>>>(a, row);
   if (rope_dim == 64)
     mla_split_kernel<64><<<(unsigned)items, 64 * kWaves, 0, st>>>(a);
   else

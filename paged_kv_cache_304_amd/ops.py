@@ -39,6 +39,14 @@ def _stream(stream=None) -> int:
     return s.cuda_stream
 
 
+def _scratch(nbytes: int, device, stream=None) -> torch.Tensor:
+    """Workspace allocated on the stream the kernels run on: the caching allocator
+    then hands its memory out again only in that stream's order, i.e. after them."""
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    with torch.cuda.stream(s):
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
 def reshape_and_cache(key: torch.Tensor, value: Optional[torch.Tensor], key_cache: torch.Tensor,
                       value_cache: Optional[torch.Tensor], slot_mapping: torch.Tensor,
                       swa_slot_mapping: Optional[torch.Tensor] = None,
@@ -62,8 +70,9 @@ def reshape_and_cache(key: torch.Tensor, value: Optional[torch.Tensor], key_cach
         if value_cache is None or value_cache.shape != key_cache.shape or \
                 value_cache.stride() != key_cache.stride() or value_cache.dtype != key_cache.dtype:
             raise ValueError("value_cache must match key_cache")
-    if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != T:
-        raise ValueError("slot_mapping must be int64 [T]")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != T or \
+            not slot_mapping.is_contiguous():
+        raise ValueError("slot_mapping must be contiguous int64 [T]")
     if swa_slot_mapping is not None and (swa_slot_mapping.dtype != torch.int64
                                          or not swa_slot_mapping.is_contiguous()):
         raise ValueError("swa_slot_mapping must be contiguous int64")
@@ -74,7 +83,7 @@ def reshape_and_cache(key: torch.Tensor, value: Optional[torch.Tensor], key_cach
         key.data_ptr(), _ptr(value), _code(key, "key"), T, H, D, key.stride(0),
         value.stride(0) if value is not None else 0, key_cache.data_ptr(), _ptr(value_cache),
         _code(key_cache, "key_cache"), NB, BS, key_cache.stride(0),
-        slot_mapping.contiguous().data_ptr(), _ptr(swa_slot_mapping),
+        slot_mapping.data_ptr(), _ptr(swa_slot_mapping),
         swa_slot_mapping.numel() if swa_slot_mapping is not None else 0,
         _ptr(k_scale), _ptr(v_scale), _stream(stream)))
 
@@ -172,7 +181,7 @@ def decode_attention(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tensor
     W = block_tables.shape[1]
     need = decode_attention_workspace_size(max(B, 1), HQ, HKV, D, W, BS)
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _scratch(need, q.device, stream)
     check(lib.pa_decode_attention(
         out.data_ptr(), _code(out, "out"), out.stride(0), q.data_ptr(), _code(q, "q"), q.stride(0),
         key_cache.data_ptr(), value_cache.data_ptr(), _code(key_cache, "key_cache"), NB, BS,
@@ -251,7 +260,7 @@ def decode_step(new_k: torch.Tensor, new_v: torch.Tensor, new_slots: torch.Tenso
     W = block_tables.shape[1]
     need = decode_attention_workspace_size(max(B, 1), HQ, HKV, D, W, BS)
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _scratch(need, q.device, stream)
     if new_v.dtype != new_k.dtype:
         raise ValueError("new_k and new_v dtypes differ")
     check(lib.pa_decode_step(
@@ -324,7 +333,8 @@ def hbm_read(src: torch.Tensor, sink: Optional[torch.Tensor] = None, stream=None
     if not src.is_contiguous() or n % 16 != 0:
         raise ValueError("src must be contiguous with a multiple of 16 bytes")
     if sink is None:
-        sink = torch.empty((HBM_READ_SINK_UNITS, 4), dtype=torch.int32, device=src.device)
+        sink = _scratch(16 * HBM_READ_SINK_UNITS, src.device, stream).view(torch.int32).view(
+            HBM_READ_SINK_UNITS, 4)
     elif sink.dtype != torch.int32 or sink.numel() != 4 * HBM_READ_SINK_UNITS or not sink.is_contiguous():
         raise ValueError("sink must be contiguous int32 [2048, 4]")
     check(lib.pa_hbm_read(src.data_ptr(), n, sink.data_ptr(), _stream(stream)))
@@ -373,8 +383,8 @@ def mla_decode_attention(out: torch.Tensor, q_nope: torch.Tensor, q_rope: Option
         raise ValueError("context_lens must be contiguous int32 [B]")
     W = block_tables.shape[1]
     if workspace is None:
-        workspace = torch.empty(mla_decode_workspace_size(max(B, 1), H, QK, R, DC, DV, W, BS),
-                                dtype=torch.uint8, device=q_nope.device)
+        workspace = _scratch(mla_decode_workspace_size(max(B, 1), H, QK, R, DC, DV, W, BS),
+                             q_nope.device, stream)
     check(lib.pa_mla_decode_attention(
         out.data_ptr(), _code(out, "out"), out.stride(0), q_nope.data_ptr(), q_nope.stride(0),
         _ptr(q_rope), q_rope.stride(0) if q_rope is not None else 0, _code(q_nope, "q_nope"),
