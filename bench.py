@@ -77,6 +77,30 @@ class Timer:
         return [round(float(x), 5) for x in np.percentile([a.elapsed_time(b) for a, b in self.pairs], qs)]
 
 
+def gpu_spin_up(torch, pkv, min_ms: float = 200.0):
+    """Untimed streaming reads for at least min_ms of wall time before any warm-up:
+    GPU work in the first ~10 ms after start-up was measured up to 15% slower, and
+    a short --warmup would otherwise leave that inside the timed region."""
+    buf = torch.empty(READ_PROBE_BYTES // 4, dtype=torch.int32, device="cuda")
+    sink = torch.empty((pkv.ops.HBM_READ_SINK_UNITS, 4), dtype=torch.int32, device="cuda")
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < min_ms:
+        for _ in range(8):
+            pkv.hbm_read(buf, sink)
+        torch.cuda.synchronize()
+    del buf, sink
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_cores():
     try:
         return len(os.sched_getaffinity(0))
@@ -93,10 +117,8 @@ def setup_decode(torch, pkv, workloads, w):
                              w.block_size, w.num_blocks)
     dev = "cuda"
     if w.cache_dtype == "fp8":
-        kc = workloads.device_normal((NB, BS, HKV, D), torch.float8_e4m3fn, dev, w.seed,
-                                     std=1.0 / w.k_scale)
-        vc = workloads.device_normal((NB, BS, HKV, D), torch.float8_e4m3fn, dev, w.seed + 1,
-                                     std=1.0 / w.v_scale)
+        kc = workloads.device_fp8((NB, BS, HKV, D), dev, w.seed, w.k_scale)
+        vc = workloads.device_fp8((NB, BS, HKV, D), dev, w.seed + 1, w.v_scale)
     else:
         kc = workloads.device_normal((NB, BS, HKV, D), torch.bfloat16, dev, w.seed)
         vc = workloads.device_normal((NB, BS, HKV, D), torch.bfloat16, dev, w.seed + 1)
@@ -188,7 +210,7 @@ def cpu_baseline_decode(torch, t, w, oracle):
     sample = (f"the whole step ({w.num_seqs} sequences, {int(w.context_lens.sum())} cached tokens): "
               "oracle write of the new tokens + fp64 attention, KV-read bytes / time")
     return {"value": round(n * kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle", "sample": f"{sample}; {n} steps in {dt:.1f} s",
+            "kind": "oracle", "sample": f"{sample}; {n} steps in {dt:.1f} s", "cpu_model": cpu_model(),
             "single_thread": {"value": round(n1 * kv_bytes / dt1 / 1e9, 4), "unit": "GB/s", "cores": 1,
                               "sample": f"{n1} steps in {dt1:.1f} s"}}
 
@@ -206,6 +228,7 @@ def run_decode(args, torch, pkv, workloads, w, metric_name):
         torch.cuda.synchronize()
         print(json.dumps({"profile_steps": args.profile_steps, "workload": w.name}))
         return
+    gpu_spin_up(torch, pkv)
     for _ in range(args.warmup):
         decode_step(pkv, t, w)
     torch.cuda.synchronize()
@@ -297,7 +320,8 @@ def run_decode(args, torch, pkv, workloads, w, metric_name):
                             "tokens": w.num_seqs},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic_from_profiles("decode_attention", w.name)},
+                     "traffic": traffic_from_profiles("decode_attention", w.name),
+                     "dominant_kernel": kernel_trace_from_profiles("decode_attention", w.name, attn_bytes)},
         "hbm_copy_GBps": round(copy_gbps, 1),
         "frac_of_copy": round(achieved / copy_gbps, 4),
         "hbm_read_GBps": round(read_gbps, 1),
@@ -307,10 +331,73 @@ def run_decode(args, torch, pkv, workloads, w, metric_name):
         # the cache-write target is quoted on the bulk write (a 64-token write is
         # launch-latency bound), so the default line carries it too
         res["bulk_cache_write"] = measure_bulk_write(args, torch, pkv, workloads)
+        # the other reported configurations, timed in the same process: the
+        # batch-256 fp8 decode and the MLA K assembly + SWA write (fused and not)
+        res["fp8_decode_b256"] = measure_fp8_decode(args, torch, pkv, workloads)
+        torch.cuda.empty_cache()
+        res["mla_k_write"] = measure_mla_k_write(args, torch, pkv, workloads)
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         import oracle
         res["cpu_baseline"] = cpu_baseline_decode(torch, t, w, oracle)
     print(json.dumps(res))
+
+
+def measure_fp8_decode(args, torch, pkv, workloads):
+    """Batch-256 mixed-length decode over the 65,536-block fp8 pool: K attention
+    calls back to back on HIP events (the roofline's launches), and K whole steps
+    (new-token write + attention in one call)."""
+    w = workloads.mixed_decode_fp8()
+    t = setup_decode(torch, pkv, workloads, w)
+    stream = torch.cuda.current_stream()
+    for _ in range(max(8, args.warmup)):
+        decode_attn(pkv, t, w)
+    ta, ts = Timer(torch, stream), Timer(torch, stream)
+    ta.start()
+    for _ in range(args.steps):
+        decode_attn(pkv, t, w)
+    ta.stop()
+    ts.start()
+    for _ in range(args.steps):
+        decode_step(pkv, t, w)
+    ts.stop()
+    torch.cuda.synchronize()
+    kv, attn_bytes, _ = decode_bytes(w)
+    ms, step_ms = ta.mean_ms() / args.steps, ts.mean_ms() / args.steps
+    gbps = attn_bytes / (ms * 1e-3) / 1e9
+    del t
+    return {"workload": w.name, "ms": round(ms, 5), "bytes": attn_bytes, "kv_read_bytes": kv,
+            "GBps": round(gbps, 2), "frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "step_ms": round(step_ms, 5), "tokens_per_s": round(w.num_seqs / (step_ms * 1e-3), 1),
+            "traffic": traffic_from_profiles("decode_attention", w.name),
+            "dominant_kernel": kernel_trace_from_profiles("decode_attention", w.name, attn_bytes)}
+
+
+def measure_mla_k_write(args, torch, pkv, workloads):
+    """The MLA K assembly + SWA-remapped K-only write (16,384 tokens x 128 heads):
+    the unfused path (concat to fp32, then the write) and the fused kernel, each
+    K calls back to back (working sets of 4.3 and 1.2 GB, far past the Infinity
+    Cache)."""
+    stream = torch.cuda.current_stream()
+    out = {}
+    for label, builder in (("unfused", mla_unfused_step), ("fused", mla_fused_step)):
+        step, nbytes, kernel, name, T = builder(torch, pkv, workloads)
+        for _ in range(max(3, min(args.warmup, 10))):
+            step()
+        tm = Timer(torch, stream)
+        tm.start()
+        for _ in range(args.steps):
+            step()
+        tm.stop()
+        torch.cuda.synchronize()
+        ms = tm.mean_ms() / args.steps
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        out[label] = {"workload": name, "ms": round(ms, 5), "bytes": nbytes, "GBps": round(gbps, 2),
+                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
+                      "traffic": traffic_from_profiles(kernel, name)}
+        del step
+        torch.cuda.empty_cache()
+    return out
 
 
 def copy_calibration(torch, pkv):
@@ -344,6 +431,30 @@ def traffic_from_profiles(kernel: str, workload: str):
         return int(fields["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def kernel_trace_from_profiles(kernel: str, workload: str, nbytes: int):
+    """The dominant kernel's average duration from the committed kernel-trace
+    summary (rocprofv3 --stats over the same launches), if it was taken on the
+    current kernel source, and the algorithmic bytes of the whole call over that
+    duration as a fraction of HBM peak; otherwise None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.md")
+    src = os.path.join(ROOT, "paged_kv_cache_304_amd", "csrc", f"{kernel}.hip")
+    if not os.path.exists(path) or not os.path.exists(src):
+        return None
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.startswith("- "):
+            k, v = line[2:].split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("source_sha256_16") != sha or "dominant_avg_ns" not in fields:
+        return None
+    ns = float(fields["dominant_avg_ns"])
+    gbps = nbytes / ns
+    return {"kernel": fields.get("dominant_kernel"), "avg_ns": ns, "GBps": round(gbps, 2),
+            "frac": round(gbps / HBM_PEAK_GBPS, 4)}
 
 
 # --------------------------------------------------------------------------- #
@@ -410,7 +521,9 @@ def measure_bulk_write(args, torch, pkv, workloads):
             "traffic": traffic_from_profiles("reshape_and_cache", BULK_WRITE_NAME)}
 
 
-def run_mla(args, torch, pkv, workloads):
+def mla_unfused_step(torch, pkv, workloads):
+    """Workload 5 unfused: concat to an fp32 K, then the K-only bf16 write through
+    the SWA table. Returns (step, algorithmic bytes, kernel, workload name, tokens)."""
     w = workloads.mla_concat_swa()
     T, H, nope, rope, BS, NB = (w["num_tokens"], w["num_heads"], w["nope_dim"], w["rope_dim"],
                                 w["block_size"], w["num_blocks"])
@@ -428,13 +541,12 @@ def run_mla(args, torch, pkv, workloads):
     kept = int((oracle_free_resolve(w) >= 0).sum())
     cat_bytes = T * H * nope * 2 + T * rope * 2 + T * H * (nope + rope) * 4
     write_bytes = 8 * T + 8 * T + kept * H * (nope + rope) * (4 + 2)
-    return generic(args, torch, pkv, step, cat_bytes + write_bytes, "concat_and_cast",
-                   "mla_concat_16384x128_then_swa_write", "bf16", T, "tokens_per_s")
+    return step, cat_bytes + write_bytes, "concat_and_cast", "mla_concat_16384x128_then_swa_write", T
 
 
-def run_mla_fused(args, torch, pkv, workloads):
-    """The same MLA K assembly and SWA write as run_mla, fused into one kernel that
-    writes the bf16 cache rows straight from k_nope / k_rope."""
+def mla_fused_step(torch, pkv, workloads):
+    """Workload 5 fused: one kernel writes the bf16 cache rows straight from
+    k_nope / k_rope through the SWA table."""
     w = workloads.mla_concat_swa()
     T, H, nope, rope, BS, NB = (w["num_tokens"], w["num_heads"], w["nope_dim"], w["rope_dim"],
                                 w["block_size"], w["num_blocks"])
@@ -453,8 +565,18 @@ def run_mla_fused(args, torch, pkv, workloads):
     # kept tokens read their k_nope and k_rope rows; every token reads its slot,
     # tokens past stage one read their SWA entry; kept rows are written once
     nbytes = 8 * T + 8 * kept1 + kept * (H * nope * 2 + rope * 2) + kept * H * (nope + rope) * 2
-    return generic(args, torch, pkv, step, nbytes, "concat_and_cast",
-                   "mla_fused_concat_and_cache_16384x128_swa", "bf16", T, "tokens_per_s")
+    return step, nbytes, "concat_and_cast", "mla_fused_concat_and_cache_16384x128_swa", T
+
+
+def run_mla(args, torch, pkv, workloads):
+    step, nbytes, kernel, name, T = mla_unfused_step(torch, pkv, workloads)
+    return generic(args, torch, pkv, step, nbytes, kernel, name, "bf16", T, "tokens_per_s")
+
+
+def run_mla_fused(args, torch, pkv, workloads):
+    """The same MLA K assembly and SWA write as run_mla, fused into one kernel."""
+    step, nbytes, kernel, name, T = mla_fused_step(torch, pkv, workloads)
+    return generic(args, torch, pkv, step, nbytes, kernel, name, "bf16", T, "tokens_per_s")
 
 
 def oracle_free_resolve(w):
