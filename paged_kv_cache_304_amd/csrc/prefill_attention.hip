@@ -30,7 +30,8 @@
 //    online-softmax state and the row max needs two cross-lane shuffles.
 //  * O = P V: the lane's own probabilities of keys {4g..4g+3} and
 //    {16+4g..16+4g+3} (g = l/16) are its A operand (a permutation of the
-//    contraction index, applied to both operands), and V's B operand comes
+//    contraction index, applied to both operands), split into bf16 hi + lo
+//    (two products) so that P enters at fp32 accuracy, and V's B operand comes
 //    from LDS with ds_read_b64_tr_b16 (transposing reads: lane i of a 16-lane
 //    group receives element (i mod 4) of the 8-byte chunk addressed by lane
 //    4j + i/4, j = 0..3), which returns V[key][d] for four consecutive keys
@@ -457,7 +458,8 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
     }
     set_prio<kPrioSM>();
     constexpr int kSt = kKeys / 32;  // 32-key steps of P.V
-    bf16x8 pop[2][kSt];  // A operands of P.V: [rb][32-key step]
+    // A operands of P.V, [rb][32-key step]: the probabilities as bf16 hi + lo
+    bf16x8 pop[2][kSt], plo[2][kSt];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       bool ok[kKB][4];
@@ -492,13 +494,20 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
       l_run[rb] = l_run[rb] * alpha + ps;
       const bool moved = mn != m_run[rb];
       m_run[rb] = mn;
+      // p = hi + lo with hi = bf16(p) and lo = bf16(p - hi), both rounded to
+      // nearest even: hi + lo is within 2^-17 (relative) of the fp32 p, so P.V
+      // on the bf16 matrix core stays fp32-accurate (l above sums the same p)
 #pragma unroll
       for (int st = 0; st < kSt; ++st) {
-        const uint32_t w0 = f32x2_to_bf16x2(pr[2 * st][0], pr[2 * st][1]);
-        const uint32_t w1 = f32x2_to_bf16x2(pr[2 * st][2], pr[2 * st][3]);
-        const uint32_t w2 = f32x2_to_bf16x2(pr[2 * st + 1][0], pr[2 * st + 1][1]);
-        const uint32_t w3 = f32x2_to_bf16x2(pr[2 * st + 1][2], pr[2 * st + 1][3]);
-        pop[rb][st] = __builtin_bit_cast(bf16x8, u32x4{w0, w1, w2, w3});
+        uint32_t wh[4], wl[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x0 = pr[2 * st + (e >> 1)][2 * (e & 1)], x1 = pr[2 * st + (e >> 1)][2 * (e & 1) + 1];
+          wh[e] = f32x2_to_bf16x2(x0, x1);
+          wl[e] = f32x2_to_bf16x2(x0 - bf16_lo(wh[e]), x1 - bf16_hi(wh[e]));
+        }
+        pop[rb][st] = __builtin_bit_cast(bf16x8, u32x4{wh[0], wh[1], wh[2], wh[3]});
+        plo[rb][st] = __builtin_bit_cast(bf16x8, u32x4{wl[0], wl[1], wl[2], wl[3]});
       }
       // Rescale the accumulator rows 4lg + r by their rows' alpha -- only when
       // some row's max moved (otherwise every alpha is exactly 1).
@@ -541,6 +550,8 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
         const bf16x8 vop = __builtin_bit_cast(bf16x8, w);
         acc[0][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pop[0][st], vop, acc[0][cb], 0, 0, 0);
         acc[1][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pop[1][st], vop, acc[1][cb], 0, 0, 0);
+        acc[0][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo[0][st], vop, acc[0][cb], 0, 0, 0);
+        acc[1][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo[1][st], vop, acc[1][cb], 0, 0, 0);
       }
     }
   };

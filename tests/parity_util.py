@@ -55,37 +55,26 @@ def bf16_half_ulp(x: np.ndarray) -> np.ndarray:
 
 def assert_attention_close(gpu: np.ndarray, ref: np.ndarray, what: str = "",
                            out_bf16: bool = True) -> None:
-    """|gpu - oracle| <= 2e-3 + 2e-3*|oracle| for fp32 outputs. A bf16 output is one
-    more rounding of that fp32 value, so it may also be off by the format's own half
-    ulp (which alone exceeds the bound for |oracle| in [2, 2.9) and [4, 5.8))."""
+    """|gpu - oracle| <= 2e-3 + 2e-3*|oracle| against the unrounded fp64 oracle.
+
+    A bf16 output is one more rounding of the kernel's fp32 value. Below |oracle| = 2
+    that rounding stays inside the bound (half an ulp is at most 2^-8 * |oracle|, and
+    at most 2^-9 * 2 there), so the plain bound applies. Only where |oracle| >= 2
+    can bf16's half ulp alone exceed it (|oracle| in [2, 2.9) and [4, 5.8)); there,
+    and only there, half an ulp of the oracle value is added, and the test says how
+    many outputs took that allowance."""
     assert gpu.shape == ref.shape
     assert np.all(np.isfinite(gpu)), f"{what}: non-finite GPU output"
     err = np.abs(gpu - ref)
     bound = ATOL + RTOL * np.abs(ref)
     if out_bf16:
-        bound = bound + bf16_half_ulp(ref)
+        big = np.abs(ref) >= 2.0
+        if big.any():
+            say(f"{what}: {int(big.sum())} of {ref.size} outputs have |o| >= 2 "
+                f"(bf16 half-ulp allowance applied to those only)")
+            bound = bound + np.where(big, bf16_half_ulp(ref), 0.0)
     bad = err > bound
     if bad.any():
         i = np.unravel_index(np.argmax(err - bound), err.shape)
         raise AssertionError(f"{what}: {bad.sum()} of {err.size} outside tolerance; worst at {i}: "
                              f"gpu={gpu[i]!r} oracle={ref[i]!r} err={err[i]:.3e}")
-
-
-def abs_values(cache_bits):
-    return cache_bits & np.uint16(0x7FFF)   # |x| of bf16 (NaN stays NaN)
-
-
-def check_close(got, ref, ref_abs, what, out_bf16):
-    """Prefill bound: the decode bound plus 2^-9 * sum_j p_j |v_j| / l for the bf16
-    probabilities of the P.V product (ref_abs = the oracle run on |V|)."""
-    assert got.shape == ref.shape
-    assert np.all(np.isfinite(got)), f"{what}: non-finite GPU output"
-    tol = 2e-3 + 2e-3 * np.abs(ref) + 2.0 ** -9 * ref_abs * 1.001
-    if out_bf16:
-        tol = tol + bf16_half_ulp(ref)
-    err = np.abs(got - ref)
-    bad = err > tol
-    if bad.any():
-        i = np.unravel_index(np.argmax(err - tol), err.shape)
-        raise AssertionError(f"{what}: {int(bad.sum())} of {err.size} outside the bound; worst at {i}: "
-                             f"gpu {got[i]!r} oracle {ref[i]!r} tol {tol[i]!r}")

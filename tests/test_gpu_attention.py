@@ -53,8 +53,8 @@ def make_case(seed, ctx, hq, hkv, d, bs, cache_dt, spare=5, width=None):
     perm = rng.permutation(nb).astype(np.int32)
     bt = workloads.deal_block_tables(perm, ctx, bs, W)
     if cache_dt == FP8:
-        kc = workloads.normal_fp8_codes(rng, (nb, bs, hkv, d), 20.0)
-        vc = workloads.normal_fp8_codes(rng, (nb, bs, hkv, d), 25.0)
+        kc = workloads.normal_fp8_codes(rng, (nb, bs, hkv, d), 0.05)
+        vc = workloads.normal_fp8_codes(rng, (nb, bs, hkv, d), 0.04)
     else:
         kc = workloads.normal_bf16_bits(rng, (nb, bs, hkv, d))
         vc = workloads.normal_bf16_bits(rng, (nb, bs, hkv, d))
@@ -190,10 +190,8 @@ def _full_decode(w: workloads.DecodeWorkload, with_write: bool):
     B, HQ, HKV, D, BS, NB = (w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_size,
                              w.block_size, w.num_blocks)
     if w.cache_dtype == "fp8":
-        kc = workloads.device_normal((NB, BS, HKV, D), torch.float8_e4m3fn, "cuda", w.seed,
-                                     std=1.0 / w.k_scale)
-        vc = workloads.device_normal((NB, BS, HKV, D), torch.float8_e4m3fn, "cuda", w.seed + 1,
-                                     std=1.0 / w.v_scale)
+        kc = workloads.device_fp8((NB, BS, HKV, D), "cuda", w.seed, w.k_scale)
+        vc = workloads.device_fp8((NB, BS, HKV, D), "cuda", w.seed + 1, w.v_scale)
         cdt = FP8
     else:
         kc = workloads.device_normal((NB, BS, HKV, D), torch.bfloat16, "cuda", w.seed)
@@ -213,8 +211,10 @@ def _full_decode(w: workloads.DecodeWorkload, with_write: bool):
     vs = None if w.v_scale is None else torch.tensor([w.v_scale], dtype=torch.float32, device="cuda")
     out = torch.empty((B, HQ, D), dtype=torch.bfloat16, device="cuda")
     m.decode_attention(out, q, kc, vc, bt, cl, w.softmax_scale, ks, vs)
+    out32 = torch.empty((B, HQ, D), dtype=torch.float32, device="cuda")
+    m.decode_attention(out32, q, kc, vc, bt, cl, w.softmax_scale, ks, vs)
     torch.cuda.synchronize()
-    host = dict(q=to_host(q, BF16), kc=kc_host, vc=vc_host, cdt=cdt,
+    host = dict(out32=widen_out(out32), q=to_host(q, BF16), kc=kc_host, vc=vc_host, cdt=cdt,
                 new_k=None if new_k is None else to_host(new_k, BF16),
                 new_v=None if new_v is None else to_host(new_v, BF16),
                 gpu_kc=to_host(kc, cdt) if with_write else None)
@@ -223,7 +223,8 @@ def _full_decode(w: workloads.DecodeWorkload, with_write: bool):
 
 def test_qwen3_decode_b64_full_step():
     """Batch 64, ctx ~ U{512..4096}, 32,768-block bf16 pool: write the 64 new tokens,
-    then attend; all 64 x 16 heads are compared with the oracle."""
+    then attend; all 64 x 16 heads are compared with the oracle, with an fp32
+    output at the plain bound and with the bf16 output."""
     w = workloads.qwen3_decode_b64()
     say(f"decode step full size {w.name} kv_bytes={w.kv_read_bytes()}")
     out, h = _full_decode(w, with_write=True)
@@ -232,18 +233,25 @@ def test_qwen3_decode_b64_full_step():
     assert np.array_equal(h["gpu_kc"], kc)  # the GPU write of the step is bit-exact
     ref = oracle.decode_attention(h["q"], BF16, kc, vc, BF16, w.block_tables, w.context_lens,
                                   w.softmax_scale)
-    assert_attention_close(widen_out(out), ref, w.name)
+    say(f"{w.name}: max |o| {np.abs(ref).max():.3f}, max |err| fp32 out "
+        f"{np.abs(h['out32'] - ref).max():.2e}")
+    assert_attention_close(h["out32"], ref, w.name + " out=f32", out_bf16=False)
+    assert_attention_close(widen_out(out), ref, w.name + " out=bf16")
 
 
 def test_mixed_decode_fp8_b256_full():
     """Batch 256, lognormal ctx (median 1024, cap 8192), 65,536-block fp8 pool with
-    per-tensor scales 0.05/0.04; every output compared with the oracle."""
+    per-tensor scales 0.05/0.04; every output compared with the oracle (fp32 output at
+    the plain bound, and the bf16 output)."""
     w = workloads.mixed_decode_fp8()
     say(f"decode full size {w.name} kv_bytes={w.kv_read_bytes()}")
     out, h = _full_decode(w, with_write=False)
     ref = oracle.decode_attention(h["q"], BF16, h["kc"], h["vc"], FP8, w.block_tables,
                                   w.context_lens, w.softmax_scale, w.k_scale, w.v_scale)
-    assert_attention_close(widen_out(out), ref, w.name)
+    say(f"{w.name}: max |o| {np.abs(ref).max():.3f}, max |err| fp32 out "
+        f"{np.abs(h['out32'] - ref).max():.2e}")
+    assert_attention_close(h["out32"], ref, w.name + " out=f32", out_bf16=False)
+    assert_attention_close(widen_out(out), ref, w.name + " out=bf16")
 
 
 def test_long_contexts_several_ranges_per_workgroup():
@@ -260,8 +268,8 @@ def test_long_contexts_several_ranges_per_workgroup():
     ctx = np.full(B, L, dtype=np.int32)
     ctx[7] = L - 5
     bt = workloads.deal_block_tables(perm, ctx, BS, W)
-    kc = workloads.device_normal((NB, BS, HKV, D), torch.float8_e4m3fn, "cuda", 4001, std=20.0)
-    vc = workloads.device_normal((NB, BS, HKV, D), torch.float8_e4m3fn, "cuda", 4002, std=25.0)
+    kc = workloads.device_fp8((NB, BS, HKV, D), "cuda", 4001, 0.05)
+    vc = workloads.device_fp8((NB, BS, HKV, D), "cuda", 4002, 0.04)
     q = workloads.device_normal((B, HQ, D), torch.bfloat16, "cuda", 4003)
     ks = torch.tensor([0.05], dtype=torch.float32, device="cuda")
     vs = torch.tensor([0.04], dtype=torch.float32, device="cuda")

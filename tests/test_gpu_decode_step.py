@@ -45,8 +45,8 @@ def make_step(seed, ctx, hq, hkv, d, bs, cache_dt, spare=6, slot_mode="table"):
     perm = rng.permutation(nb).astype(np.int32)
     bt = workloads.deal_block_tables(perm, ctx, bs, W)
     if cache_dt == FP8:
-        kc = workloads.normal_fp8_codes(rng, (nb, bs, hkv, d), 20.0)
-        vc = workloads.normal_fp8_codes(rng, (nb, bs, hkv, d), 25.0)
+        kc = workloads.normal_fp8_codes(rng, (nb, bs, hkv, d), 0.05)
+        vc = workloads.normal_fp8_codes(rng, (nb, bs, hkv, d), 0.04)
         nan = NAN_FP8
     else:
         kc = workloads.normal_bf16_bits(rng, (nb, bs, hkv, d))
@@ -76,9 +76,9 @@ def make_step(seed, ctx, hq, hkv, d, bs, cache_dt, spare=6, slot_mode="table"):
             if ctx[b] > 0:
                 p = int(ctx[b]) - 1
                 s = int(bt[b, p // bs]) * bs + p % bs
-                kc.reshape(nb * bs, hkv, d)[s] = workloads.normal_fp8_codes(rng, (hkv, d), 20.0) \
+                kc.reshape(nb * bs, hkv, d)[s] = workloads.normal_fp8_codes(rng, (hkv, d), 0.05) \
                     if cache_dt == FP8 else workloads.normal_bf16_bits(rng, (hkv, d))
-                vc.reshape(nb * bs, hkv, d)[s] = workloads.normal_fp8_codes(rng, (hkv, d), 25.0) \
+                vc.reshape(nb * bs, hkv, d)[s] = workloads.normal_fp8_codes(rng, (hkv, d), 0.04) \
                     if cache_dt == FP8 else workloads.normal_bf16_bits(rng, (hkv, d))
     new_k = workloads.normal_bf16_bits(rng, (B, hkv, d))
     new_v = workloads.normal_bf16_bits(rng, (B, hkv, d))

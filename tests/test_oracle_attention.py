@@ -164,8 +164,8 @@ def test_empty_sequence_and_invalid_table_entry():
 def test_fp8_cache_dequantised_by_scales():
     rng = np.random.default_rng(7)
     p = make_paged(rng, [9, 21], hq=4, hkv=2, d=16, bs=4)
-    p["kc"] = workloads.normal_fp8_codes(rng, p["kc"].shape, 20.0)
-    p["vc"] = workloads.normal_fp8_codes(rng, p["vc"].shape, 25.0)
+    p["kc"] = workloads.normal_fp8_codes(rng, p["kc"].shape, 0.05)
+    p["vc"] = workloads.normal_fp8_codes(rng, p["vc"].shape, 0.04)
     ks, vs = float(np.float32(0.05)), float(np.float32(0.04))
     got = run_oracle(p, 0.25, oracle.FP8_E4M3FN, ks, vs)
 

@@ -165,8 +165,8 @@ def _tail_reference(p, scale):
 def test_fp8_dequantisation_multiplies_by_the_scales():
     rng = np.random.default_rng(10)
     p = make_prefill(rng, [11, 20], [4, 20], hq=4, hkv=2, d=16, bs=4)
-    kc = workloads.normal_fp8_codes(rng, p["kc"].shape, 20.0)
-    vc = workloads.normal_fp8_codes(rng, p["vc"].shape, 25.0)
+    kc = workloads.normal_fp8_codes(rng, p["kc"].shape, 0.05)
+    vc = workloads.normal_fp8_codes(rng, p["vc"].shape, 0.04)
     f8 = torch.from_numpy(np.arange(256, dtype=np.uint8)).view(torch.float8_e4m3fn).double().numpy()
     p8 = dict(p, kc=kc, vc=vc)
     got = run_oracle(p8, 0.25, oracle.FP8_E4M3FN, 0.05, 0.04)

@@ -9,9 +9,9 @@ inputs from here, so both sides always see the same bytes.
 Recipe (every workload is seeded by ``numpy.random.PCG64(SeedSequence([304, id]))``):
   - float tensors are drawn as fp32 standard normals (times a stated standard
     deviation) and rounded to bf16 by torch's round-to-nearest-even cast;
-  - fp8 e4m3fn caches are drawn as fp32 normals of standard deviation
-    1/scale (the spread that the cache write produces from N(0,1) data) and
-    cast to fp8 by torch;
+  - fp8 e4m3fn caches hold what the scaled cache write makes of N(0,1) data:
+    fp32 normals rounded to bf16, divided by the per-tensor scale in fp32 and
+    cast to e4m3fn (round to nearest even) by torch;
   - large pools are drawn on the target device with a torch Generator seeded
     from the same SeedSequence (bit-identical between runs on one device);
   - physical blocks are handed out in the order of a seeded permutation of the
@@ -51,18 +51,39 @@ def normal_bf16_bits(rng: np.random.Generator, shape, std: float = 1.0) -> np.nd
     return bf16_bits_from_f32(x)
 
 
-def normal_fp8_codes(rng: np.random.Generator, shape, std: float) -> np.ndarray:
-    x = rng.standard_normal(size=shape, dtype=np.float32) * np.float32(std)
-    return torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+def normal_fp8_codes(rng: np.random.Generator, shape, scale: float) -> np.ndarray:
+    """fp8 cache contents as the scaled cache write makes them from N(0,1) data:
+    fp32 normals rounded to bf16, divided by the fp32 scale (numpy's IEEE fp32
+    division), cast to e4m3fn by torch (round to nearest even)."""
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    xb = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    y = xb / np.float32(scale)
+    return torch.from_numpy(np.ascontiguousarray(y)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def device_fp8(shape, device, seed: int, scale: float, chunk_elems: int = 1 << 28) -> torch.Tensor:
+    """Seeded fp8 e4m3fn cache drawn on ``device`` by the recipe of
+    ``normal_fp8_codes``: N(0,1) -> bf16 -> / scale (fp32) -> e4m3fn, by torch ops."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    out = torch.empty(shape, dtype=torch.float8_e4m3fn, device=device)
+    flat = out.view(-1)
+    sc = torch.tensor(float(np.float32(scale)), dtype=torch.float32, device=device)
+    n = flat.numel()
+    for start in range(0, n, chunk_elems):
+        m = min(chunk_elems, n - start)
+        x = torch.randn(m, generator=g, device=device, dtype=torch.float32)
+        x = x.to(torch.bfloat16).float().div_(sc)
+        flat[start:start + m].copy_(x.to(torch.float8_e4m3fn))
+        del x
+    return out
 
 
 def device_normal(shape, dtype: torch.dtype, device, seed: int, std: float = 1.0,
                   chunk_elems: int = 1 << 28) -> torch.Tensor:
-    """Seeded normal tensor drawn on ``device`` (chunked to bound scratch memory).
-
-    bf16/fp32 results are N(0, std^2) rounded by torch's cast; fp8 results are
-    N(0, std^2) cast to e4m3fn.
-    """
+    """Seeded normal tensor drawn on ``device`` (chunked to bound scratch memory):
+    N(0, std^2) in fp32, rounded to ``dtype`` by torch's cast (fp8 caches of the
+    workloads come from ``device_fp8``)."""
     g = torch.Generator(device=device)
     g.manual_seed(seed)
     out = torch.empty(shape, dtype=dtype, device=device)
