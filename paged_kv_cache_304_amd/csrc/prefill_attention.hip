@@ -574,7 +574,9 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
     if (t < n_kt) start_tile(t, ta_next);
   }
   next_tile_addr(kAhead, ta_next);
-  for (int kt = 0; kt < n_kt; ++kt) {
+  // One pipeline step: tile kt + kAhead is fetched, tile kt has landed in every
+  // wave's share; returns the validity bits of tile kt's 16-key blocks.
+  auto advance = [&](int kt) -> int {
     barrier_no_vmem_wait();  // every wave is done with buffer (kt + kAhead) % kBufs
     const int tn = kt + kAhead;
     if (tn < n_kt) start_tile(tn, ta_next);
@@ -597,12 +599,26 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
     else
       wait_vmem<0>();
     barrier_no_vmem_wait();  // every wave's share of tile kt has landed
-    const int okb = (okring >> (4 * (kt % kBufs))) & 15;
-    const bool clean = kt * kKeys + kKeys - 1 <= p_first && okb == kAll;
-    if (clean)
-      compute(kt, kt % kBufs, okb, std::false_type{});
-    else
-      compute(kt, kt % kBufs, okb, std::true_type{});
+    return (okring >> (4 * (kt % kBufs))) & 15;
+  };
+  // Two loops, each with one variant of the tile step (both variants in one
+  // loop need more registers than a lane has and spill inside the loop, and a
+  // scratch reload waits on the vector-memory counter the tile pipeline runs
+  // on): tiles are clean (no causal, context-end or table mask) up to the
+  // first one that is not; from there on every tile takes the masked step.
+  int kt = 0, okb_first = -1;
+  for (; kt < n_kt; ++kt) {
+    const int okb = advance(kt);
+    if (!(kt * kKeys + kKeys - 1 <= p_first && okb == kAll)) {
+      okb_first = okb;  // tile kt has landed; the masked loop computes it
+      break;
+    }
+    compute(kt, kt % kBufs, okb, std::false_type{});
+  }
+  for (; kt < n_kt; ++kt) {
+    const int okb = okb_first >= 0 ? okb_first : advance(kt);
+    okb_first = -1;
+    compute(kt, kt % kBufs, okb, std::true_type{});
   }
 
   // ---- finish: sum the row sums over the four lane groups, normalise, store
