@@ -27,7 +27,9 @@
 //  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (K rows from LDS as A, the
 //    wave's q rows from registers as B): lane l gets the scores of keys
 //    16*kb + 4*(l/16) + r for query row l%16, so each lane keeps one row's
-//    online-softmax state and the row max needs two cross-lane shuffles.
+//    online-softmax state and the row max needs two cross-row lane swaps.
+//    The running max is raised lazily (only when a tile passes it by more
+//    than 2^8 in probability), so the accumulator is rarely rescaled.
 //  * O = P V: the lane's own probabilities of keys {4g..4g+3} and
 //    {16+4g..16+4g+3} (g = l/16) are its A operand (a permutation of the
 //    contraction index, applied to both operands), split into bf16 hi + lo
@@ -64,22 +66,12 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 #ifndef PA_PREFILL_KEYS
 #define PA_PREFILL_KEYS 32
 #endif
-#ifndef PA_PREFILL_BUFS
-#define PA_PREFILL_BUFS 4
-#endif
 constexpr int kWaves = PA_PREFILL_WAVES;
-#ifndef PA_PREFILL_PRIO_QK
-#define PA_PREFILL_PRIO_QK 0
-#endif
 #ifndef PA_PREFILL_PRIO_SM
 #define PA_PREFILL_PRIO_SM 1
 #endif
-#ifndef PA_PREFILL_PRIO_PV
-#define PA_PREFILL_PRIO_PV 0
-#endif
-// Issue priority of a wave in each phase of a key tile: the S product, the
-// softmax, the P.V product.
-constexpr int kPrioQK = PA_PREFILL_PRIO_QK, kPrioSM = PA_PREFILL_PRIO_SM, kPrioPV = PA_PREFILL_PRIO_PV;
+// Issue priority of a wave during a tile's softmax (0 for the products).
+constexpr int kPrioSM = PA_PREFILL_PRIO_SM;
 template <int P> __device__ __forceinline__ void set_prio() {
   static_assert(P >= 0 && P <= 3, "priority 0..3");
   __builtin_amdgcn_s_setprio(P);
@@ -88,10 +80,9 @@ constexpr int kRowsPerWave = 32;              // two 16-row MFMA blocks
 constexpr int kRows = kWaves * kRowsPerWave;  // (token, head) rows per workgroup
 constexpr int kKeys = PA_PREFILL_KEYS;        // positions per key tile
 constexpr int kKB = kKeys / 16;               // 16-key blocks per tile
-constexpr int kBufs = PA_PREFILL_BUFS;        // LDS ring: the tile in use + the ones in flight
-constexpr int kAhead = kBufs - 1;
+constexpr int kBufs = 4;                      // LDS ring: tiles in P.V, in S, and two in flight
+constexpr float kLazyMax = 8.0f;              // log2 headroom of the running max
 static_assert(kKeys == 32 || kKeys == 64, "key tile");
-static_assert(kBufs >= 2 && kBufs <= 4, "ring depth");
 
 template <int N>
 __device__ __forceinline__ void wait_vmem() {
@@ -158,6 +149,19 @@ struct Geo {
   __device__ static int k_off(int kb, int s, int lane) { return ((kb * KS + s) * 64 + lane) * 16; }
   __device__ static int v_off(int st, int cb, int half, int lane) { return ((st * CB + cb) * 2 + half) * 512 + 8 * lane; }
 };
+
+// Max over the lanes l, l^16, l^32 and l^48 (the four lanes that hold one
+// query row's scores): gfx950's cross-row lane swaps, no LDS round trip. Each
+// swap exchanges one half of a copy of x with the other half of a second copy,
+// so the two results hold, lane by lane, x at l and at its partner lane.
+__device__ __forceinline__ float row_max4(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t w = __float_as_uint(m);
+  const auto b = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
 
 __device__ __forceinline__ float bcast_lane(float x, int src) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(x)));
@@ -430,21 +434,16 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // One key tile. kMask: some score of the tile is causal-masked, past the
-  // context end, or in a block outside the pool.
-  auto compute = [&](int kt, int buf, int okbits, auto mask_tag) {
-    constexpr bool kMask = decltype(mask_tag)::value;
+  // The tile step in three parts. qk: S^T of a tile (sc[rb][kb] holds keys
+  // 16kb + 4lg + r of row (rb, li)). softmax: the online-softmax update of
+  // the running max and sum and the tile's probabilities as bf16 hi + lo P.V
+  // operands; it returns, per 16-row block, whether some row's max moved
+  // (alpha then holds the rescale factor of the lane's row). pv: O += P V.
+  // kMask: some score of the tile is causal-masked, past the context end, or
+  // in a block outside the pool.
+  constexpr int kSt = kKeys / 32;  // 32-key steps of P.V
+  auto qk = [&](int buf, f32x4 (&sc)[2][kKB]) {
     const char* kl = kv_lds[buf][0];
-    const char* vl = kv_lds[buf][1];
-    const int key0 = kt * kKeys;
-    bool kb_ok[kKB];
-    if constexpr (kMask) {
-#pragma unroll
-      for (int kb = 0; kb < kKB; ++kb) kb_ok[kb] = (okbits >> kb) & 1;
-    }
-    // S^T: sc[rb][kb] holds keys 16kb + 4lg + r of row (rb, li)
-    set_prio<kPrioQK>();
-    f32x4 sc[2][kKB];
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb) {
       sc[0][kb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -456,10 +455,14 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
         sc[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[1][s], sc[1][kb], 0, 0, 0);
       }
     }
-    set_prio<kPrioSM>();
-    constexpr int kSt = kKeys / 32;  // 32-key steps of P.V
-    // A operands of P.V, [rb][32-key step]: the probabilities as bf16 hi + lo
-    bf16x8 pop[2][kSt], plo[2][kSt];
+  };
+  auto softmax = [&](int kt, int okbits, const f32x4 (&sc)[2][kKB], bf16x8 (&pop)[2][kSt],
+                     bf16x8 (&plo)[2][kSt], float (&alpha)[2], bool (&moved)[2], auto mask_tag) {
+    constexpr bool kMask = decltype(mask_tag)::value;
+    const int key0 = kt * kKeys;
+    bool kb_ok[kKB];
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb) kb_ok[kb] = kMask ? ((okbits >> kb) & 1) != 0 : true;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       bool ok[kKB][4];
@@ -475,12 +478,15 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
           }
           mx = fmaxf(mx, ok[kb][r] ? sc[rb][kb][r] : -INFINITY);
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = row_max4(mx);
       const float mxs = mx == -INFINITY ? -INFINITY : mx * sl2;  // max of the scaled scores
-      const float mn = fmaxf(m_run[rb], mxs);
+      // The running max m is raised only when the tile's max passes it by more
+      // than kLazyMax (first tile: any finite max): probabilities 2^(s - m) then
+      // stay below 2^kLazyMax, and the accumulator rescale is rare.
+      const bool raise = mxs > m_run[rb] + kLazyMax;
+      const float mn = raise ? mxs : m_run[rb];
       const float mu = (mn == -INFINITY) ? 0.0f : mn;
-      const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - mu);
+      alpha[rb] = raise ? __builtin_amdgcn_exp2f(m_run[rb] - mu) : 1.0f;
       float ps = 0.0f;
       float pr[kKB][4];
 #pragma unroll
@@ -491,8 +497,8 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
           pr[kb][r] = kMask ? (ok[kb][r] ? e2 : 0.0f) : e2;
           ps += pr[kb][r];
         }
-      l_run[rb] = l_run[rb] * alpha + ps;
-      const bool moved = mn != m_run[rb];
+      l_run[rb] = l_run[rb] * alpha[rb] + ps;
+      moved[rb] = raise;
       m_run[rb] = mn;
       // p = hi + lo with hi = bf16(p) and lo = bf16(p - hi), both rounded to
       // nearest even: hi + lo is within 2^-17 (relative) of the fp32 p, so P.V
@@ -509,22 +515,32 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
         pop[rb][st] = __builtin_bit_cast(bf16x8, u32x4{wh[0], wh[1], wh[2], wh[3]});
         plo[rb][st] = __builtin_bit_cast(bf16x8, u32x4{wl[0], wl[1], wl[2], wl[3]});
       }
-      // Rescale the accumulator rows 4lg + r by their rows' alpha -- only when
-      // some row's max moved (otherwise every alpha is exactly 1).
-      if (__builtin_amdgcn_ballot_w64(moved) != 0) {
+    }
+  };
+  // Rescale the accumulator rows 4lg + r of block rb by their rows' alpha --
+  // only when some row's max was raised (otherwise every alpha is exactly 1).
+  auto rescale = [&](const float (&alpha)[2], const bool (&moved)[2]) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      if (__builtin_amdgcn_ballot_w64(moved[rb]) != 0) {
         float al[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) al[r] = bcast_lane(alpha, (lane & 48) + 4 * lg + r);
+        for (int r = 0; r < 4; ++r) al[r] = bcast_lane(alpha[rb], (lane & 48) + 4 * lg + r);
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[rb][cb][r] *= al[r];
       }
     }
-    set_prio<kPrioPV>();
-    // O += P V, V's operand by transposing reads (lane m of a 16-lane group
-    // reads row kbase + m/4, columns 16cb + 4(m%4) .. +3, kbase = 32st + 4g,
-    // then + 16); the two reads are the operand's low and high halves.
+  };
+  // O += P V, V's operand by transposing reads (lane m of a 16-lane group
+  // reads row kbase + m/4, columns 16cb + 4(m%4) .. +3, kbase = 32st + 4g,
+  // then + 16); the two reads are the operand's low and high halves.
+  auto pv = [&](int kt, int buf, int okbits, const bf16x8 (&pop)[2][kSt], const bf16x8 (&plo)[2][kSt],
+                auto mask_tag) {
+    constexpr bool kMask = decltype(mask_tag)::value;
+    const char* vl = kv_lds[buf][1];
+    const int key0 = kt * kKeys;
 #pragma unroll
     for (int st = 0; st < kSt; ++st) {
       u32x4 vmask = {~0u, ~0u, ~0u, ~0u};  // V elements of masked-out keys -> 0
@@ -534,7 +550,7 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
         for (int j = 0; j < 8; ++j) {
           const int kb = 2 * st + (j >> 2);
           const int key = key0 + 16 * kb + 4 * lg + (j & 3);
-          m16[j] = (kb_ok[kb] && key < L) ? 0xFFFFu : 0u;
+          m16[j] = (((okbits >> kb) & 1) && key < L) ? 0xFFFFu : 0u;
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) vmask[i] = m16[2 * i] | (m16[2 * i + 1] << 16);
@@ -556,12 +572,19 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
     }
   };
 
-  // ---- key loop. Pipeline: tile kt + kAhead is fetched while tile kt is computed; the table
-  // entries of a tile are loaded one iteration before its fetch, and the
-  // validity of the 16-key blocks of the tiles in flight is kept as 4 bits per
-  // ring slot. Every wave issues the same number of loads per tile, so the
-  // wait leaves exactly the later tiles' loads outstanding.
+  // ---- key loop. Ring of kBufs = 4 tiles: tile kt (P.V), kt + 1 (its
+  // scores, computed while tile kt's softmax runs) and two tiles in flight.
+  // Iteration kt: wait for this wave's share of tile kt + 1, one barrier
+  // (every wave's share has landed, and every wave is done with tile kt - 1,
+  // whose buffer the fetch of tile kt + 3 then refills), S of tile kt + 1,
+  // then the softmax and P.V of tile kt. Table entries of a tile are read one
+  // tile before its fetch; the validity of the 16-key blocks of the tiles in
+  // the ring is kept as 4 bits per slot. Every wave issues the same number of
+  // loads per tile, so a wait leaves exactly the later tile's loads
+  // outstanding.
+  static_assert(kBufs == 4, "ring: tile in P.V, tile in S, two in flight");
   constexpr int kLoadsPerTile = Gm::IPW;
+  static_assert(2 * kLoadsPerTile <= 63, "vmcnt range");
   constexpr int kAll = (1 << kKB) - 1;
   int okring = 0;  // bits 4 * (t % kBufs) ..: 16-key blocks of tile t inside the pool
   auto start_tile = [&](int t, const TileAddr& ta) {
@@ -569,16 +592,21 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
     okring = (okring & ~(15 << (4 * (t % kBufs)))) | (ta.okbits << (4 * (t % kBufs)));
   };
   TileAddr ta_next;
-  for (int t = 0; t < kAhead; ++t) {
+  for (int t = 0; t < 3; ++t) {
     next_tile_addr(t, ta_next);
     if (t < n_kt) start_tile(t, ta_next);
   }
-  next_tile_addr(kAhead, ta_next);
-  // One pipeline step: tile kt + kAhead is fetched, tile kt has landed in every
-  // wave's share; returns the validity bits of tile kt's 16-key blocks.
-  auto advance = [&](int kt) -> int {
-    barrier_no_vmem_wait();  // every wave is done with buffer (kt + kAhead) % kBufs
-    const int tn = kt + kAhead;
+  next_tile_addr(3, ta_next);
+  // (t >= 1) Wait until this wave's share of tile t has landed (tile t + 1's
+  // loads stay in flight), then a barrier; then fetch tile t + 2 into the
+  // buffer of tile t - 2, which every wave is done with.
+  auto bring_in = [&](int t) {
+    if (t + 1 < n_kt)
+      wait_vmem<kLoadsPerTile>();
+    else
+      wait_vmem<0>();
+    barrier_no_vmem_wait();
+    const int tn = t + 2;
     if (tn < n_kt) start_tile(tn, ta_next);
     // next tile's addresses; restage the table window when the tile runs past
     // it (uniform; once per kTab blocks)
@@ -588,37 +616,59 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
       __syncthreads();
     }
     next_tile_addr(tn + 1, ta_next);
-    static_assert(kAhead * kLoadsPerTile <= 63, "vmcnt range");
-    const int later = min(kAhead, n_kt - 1 - kt);  // tiles still in flight after kt
-    if (kAhead >= 3 && later >= 3)
-      wait_vmem<(kAhead >= 3 ? 3 : 0) * kLoadsPerTile>();
-    else if (kAhead >= 2 && later == 2)
-      wait_vmem<(kAhead >= 2 ? 2 : 0) * kLoadsPerTile>();
-    else if (later == 1)
+  };
+  f32x4 sc_cur[2][kKB], sc_nxt[2][kKB];
+  bf16x8 pop[2][kSt], plo[2][kSt];
+  float alpha[2];
+  bool moved[2];
+  if (n_kt > 0) {  // tile 0 in, with tiles 1 and 2 (if any) still in flight
+    if (n_kt > 2)
+      wait_vmem<2 * kLoadsPerTile>();
+    else if (n_kt > 1)
       wait_vmem<kLoadsPerTile>();
     else
       wait_vmem<0>();
-    barrier_no_vmem_wait();  // every wave's share of tile kt has landed
-    return (okring >> (4 * (kt % kBufs))) & 15;
-  };
-  // Two loops, each with one variant of the tile step (both variants in one
-  // loop need more registers than a lane has and spill inside the loop, and a
-  // scratch reload waits on the vector-memory counter the tile pipeline runs
-  // on): tiles are clean (no causal, context-end or table mask) up to the
-  // first one that is not; from there on every tile takes the masked step.
-  int kt = 0, okb_first = -1;
+    barrier_no_vmem_wait();
+    qk(0, sc_cur);
+  }
+  // Two loops, each with one variant of the softmax and P.V (both variants in
+  // one loop need more registers than a lane has and spill inside the loop,
+  // and a scratch reload waits on the vector-memory counter the tile pipeline
+  // runs on): tiles are clean (no causal, context-end or table mask) up to the
+  // first one that is not; from there on every tile takes the masked variant.
+  int kt = 0;
   for (; kt < n_kt; ++kt) {
-    const int okb = advance(kt);
-    if (!(kt * kKeys + kKeys - 1 <= p_first && okb == kAll)) {
-      okb_first = okb;  // tile kt has landed; the masked loop computes it
-      break;
+    const int okb = (okring >> (4 * (kt % kBufs))) & 15;
+    if (!(kt * kKeys + kKeys - 1 <= p_first && okb == kAll)) break;
+    if (kt + 1 < n_kt) {
+      bring_in(kt + 1);
+      qk((kt + 1) % kBufs, sc_nxt);
     }
-    compute(kt, kt % kBufs, okb, std::false_type{});
+    set_prio<kPrioSM>();
+    softmax(kt, okb, sc_cur, pop, plo, alpha, moved, std::false_type{});
+    rescale(alpha, moved);
+    set_prio<0>();
+    pv(kt, kt % kBufs, okb, pop, plo, std::false_type{});
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int kb = 0; kb < kKB; ++kb) sc_cur[rb][kb] = sc_nxt[rb][kb];
   }
   for (; kt < n_kt; ++kt) {
-    const int okb = okb_first >= 0 ? okb_first : advance(kt);
-    okb_first = -1;
-    compute(kt, kt % kBufs, okb, std::true_type{});
+    const int okb = (okring >> (4 * (kt % kBufs))) & 15;
+    if (kt + 1 < n_kt) {
+      bring_in(kt + 1);
+      qk((kt + 1) % kBufs, sc_nxt);
+    }
+    set_prio<kPrioSM>();
+    softmax(kt, okb, sc_cur, pop, plo, alpha, moved, std::true_type{});
+    rescale(alpha, moved);
+    set_prio<0>();
+    pv(kt, kt % kBufs, okb, pop, plo, std::true_type{});
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int kb = 0; kb < kKB; ++kb) sc_cur[rb][kb] = sc_nxt[rb][kb];
   }
 
   // ---- finish: sum the row sums over the four lane groups, normalise, store
