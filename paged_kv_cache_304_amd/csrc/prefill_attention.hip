@@ -70,6 +70,9 @@ constexpr int kWaves = PA_PREFILL_WAVES;
 #ifndef PA_PREFILL_PRIO_SM
 #define PA_PREFILL_PRIO_SM 1
 #endif
+#ifndef PA_PREFILL_SCHED
+#define PA_PREFILL_SCHED 0   // vector instructions scheduled after each score MFMA (0: no hint)
+#endif
 // Issue priority of a wave during a tile's softmax (0 for the products).
 constexpr int kPrioSM = PA_PREFILL_PRIO_SM;
 template <int P> __device__ __forceinline__ void set_prio() {
@@ -87,6 +90,25 @@ static_assert(kKeys == 32 || kKeys == 64, "key tile");
 template <int N>
 __device__ __forceinline__ void wait_vmem() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// One wave-wide LDS-DMA load: 16 bytes per lane from global memory into LDS at
+// lds_base + 16 * lane (global_load_lds_dwordx4, M0 = LDS base, saved and
+// restored around it). Written as inline asm so that the compiler does not
+// track these LDS writes: it would otherwise put a full vector-memory wait
+// (every tile in flight) before LDS reads it cannot prove disjoint from them,
+// such as the transposing V reads. This kernel orders every tile's loads with
+// its own wait_vmem counts and barriers. The instruction has no register
+// result; its address registers are read at issue.
+__device__ __forceinline__ void dma_16B(const void* gptr, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
+               : "v"(gptr), "s"(lds_base)
+               : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
 // Workgroup barrier without a memory fence. __syncthreads() would also wait
@@ -422,8 +444,7 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
       for (int kb = 1; kb < kKB; ++kb) base = lane_kb[i] == kb ? ta.base[kb] : base;
       const char* src0 = ii < Gm::TI ? kc : vc;
       char* dst = kv_lds[buf][ii < Gm::TI ? 0 : 1] + (ii % Gm::TI) * 1024;
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src0 + (base + lane_el[i]) * 2),
-                                       (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+      dma_16B(src0 + (base + lane_el[i]) * 2, lds_addr(dst));
     }
   };
 
@@ -519,6 +540,19 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
   };
   // Rescale the accumulator rows 4lg + r of block rb by their rows' alpha --
   // only when some row's max was raised (otherwise every alpha is exactly 1).
+  // Issue order of the block holding tile kt+1's score product and tile kt's
+  // softmax: the K operand reads first, then the products one by one with a
+  // few vector instructions between them.
+  auto interleave_hint = [&]() {
+#if PA_PREFILL_SCHED
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * KS, 0);  // DS reads: K operands
+#pragma unroll
+    for (int i = 0; i < 4 * KS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, PA_PREFILL_SCHED, 0);  // vector ALU
+    }
+#endif
+  };
   auto rescale = [&](const float (&alpha)[2], const bool (&moved)[2]) {
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
@@ -640,14 +674,15 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
   for (; kt < n_kt; ++kt) {
     const int okb = (okring >> (4 * (kt % kBufs))) & 15;
     if (!(kt * kKeys + kKeys - 1 <= p_first && okb == kAll)) break;
-    if (kt + 1 < n_kt) {
-      bring_in(kt + 1);
-      qk((kt + 1) % kBufs, sc_nxt);
-    }
-    set_prio<kPrioSM>();
+    if (kt + 1 < n_kt) bring_in(kt + 1);
+    // tile kt+1's scores (after the last tile: a stale buffer, never used) in
+    // the same block as tile kt's softmax, so their issue interleaves
+    if (kPrioSM) set_prio<kPrioSM>();
+    qk((kt + 1) % kBufs, sc_nxt);
     softmax(kt, okb, sc_cur, pop, plo, alpha, moved, std::false_type{});
+    interleave_hint();
     rescale(alpha, moved);
-    set_prio<0>();
+    if (kPrioSM) set_prio<0>();
     pv(kt, kt % kBufs, okb, pop, plo, std::false_type{});
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
@@ -656,14 +691,15 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
   }
   for (; kt < n_kt; ++kt) {
     const int okb = (okring >> (4 * (kt % kBufs))) & 15;
-    if (kt + 1 < n_kt) {
-      bring_in(kt + 1);
-      qk((kt + 1) % kBufs, sc_nxt);
-    }
-    set_prio<kPrioSM>();
+    if (kt + 1 < n_kt) bring_in(kt + 1);
+    // tile kt+1's scores (after the last tile: a stale buffer, never used) in
+    // the same block as tile kt's softmax, so their issue interleaves
+    if (kPrioSM) set_prio<kPrioSM>();
+    qk((kt + 1) % kBufs, sc_nxt);
     softmax(kt, okb, sc_cur, pop, plo, alpha, moved, std::true_type{});
+    interleave_hint();
     rescale(alpha, moved);
-    set_prio<0>();
+    if (kPrioSM) set_prio<0>();
     pv(kt, kt % kBufs, okb, pop, plo, std::true_type{});
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
