@@ -20,6 +20,10 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "pagedkv_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# PAGEDKV_ORACLE_LIB loads another build of the same source (the CPU sanitizer
+# test's AddressSanitizer + UBSan build); it is used as given, never rebuilt.
+_LIB_OVERRIDE = os.environ.get("PAGEDKV_ORACLE_LIB")
+SANITIZED_LIB = os.path.join(os.path.dirname(_HERE), "_build", "asan", "liboracle.so")
 
 # dtype codes of the C oracle (its own numbering)
 BF16, F32, FP8_E4M3FN = 0, 2, 3
@@ -39,13 +43,28 @@ def build(force: bool = True) -> str:
     return _LIB_PATH
 
 
+def build_sanitized() -> str:
+    """The same source compiled with clang's AddressSanitizer and UBSan (shared
+    runtime, OpenMP from the same toolchain) into _build/asan/liboracle.so."""
+    os.makedirs(os.path.dirname(SANITIZED_LIB), exist_ok=True)
+    llvm = "/opt/rocm/llvm"
+    cmd = [f"{llvm}/bin/clang", "-O1", "-g", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer",
+           "-shared-libsan", "-fPIC", "-shared", "-Wall", _SRC, "-o", SANITIZED_LIB, "-lm",
+           f"-Wl,-rpath,{llvm}/lib"]
+    subprocess.run(cmd, check=True)
+    return SANITIZED_LIB
+
+
 def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+    path = _LIB_OVERRIDE or _LIB_PATH
+    if not _LIB_OVERRIDE and (not os.path.exists(_LIB_PATH)
+                              or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
         build()
-    lib = ctypes.CDLL(_LIB_PATH)
+    lib = ctypes.CDLL(path)
     P, I64, I32, F64 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double
     lib.orc_max_threads.argtypes = []
     lib.orc_max_threads.restype = I32
@@ -57,6 +76,8 @@ def _load():
     lib.orc_f32_to_bf16.restype = ctypes.c_uint16
     lib.orc_f32_to_e4m3fn.argtypes = [ctypes.c_float]
     lib.orc_f32_to_e4m3fn.restype = ctypes.c_uint8
+    lib.orc_encode_f32_array.argtypes = [P, I64, P, I32]
+    lib.orc_encode_f32_array.restype = I32
     lib.orc_encode_bf16_to_fp8_scaled.argtypes = [ctypes.c_uint16, ctypes.c_float]
     lib.orc_encode_bf16_to_fp8_scaled.restype = ctypes.c_uint8
     lib.orc_resolve_slot.argtypes = [P, I64, P, I64, I64]
@@ -119,6 +140,17 @@ def f32_to_e4m3fn(x) -> np.ndarray:
     lib = _load()
     x = np.asarray(x, dtype=np.float32).ravel()
     return np.array([lib.orc_f32_to_e4m3fn(float(v)) for v in x], dtype=np.uint8)
+
+
+def encode_f32_array(x, dtype: int) -> np.ndarray:
+    """fp32 array -> bf16 bits (uint16) or e4m3fn codes (uint8), one rounding per
+    element (R4, R5); OpenMP over the elements."""
+    lib = _load()
+    x = np.ascontiguousarray(x, dtype=np.float32).ravel()
+    out = np.empty(x.shape[0], dtype=np.uint16 if dtype == BF16 else np.uint8)
+    if lib.orc_encode_f32_array(_ptr(x), x.shape[0], _ptr(out), dtype) != 0:
+        raise ValueError("unsupported dtype")
+    return out
 
 
 def encode_bf16_to_fp8_scaled(bits, scale: float) -> np.ndarray:

@@ -218,6 +218,16 @@ static void orc_encode(const void* src, int64_t si, int sdt, void* dst, int64_t 
   orc_store_from_f32(dst, di, ddt, y);
 }
 
+/* n fp32 values rounded once to dst_dt (R4, R5), element by element: the
+ * scalar encodes above applied to an array (used to check a conversion over
+ * every fp32 bit pattern). Returns 0, or -1 for an unsupported type. */
+int orc_encode_f32_array(const float* src, int64_t n, void* dst, int dst_dt) {
+  if (dst_dt != ORC_BF16 && dst_dt != ORC_FP8_E4M3FN) return -1;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) orc_store_from_f32(dst, i, dst_dt, src[i]);
+  return 0;
+}
+
 /* Exposed for the pin tests. */
 uint8_t orc_encode_bf16_to_fp8_scaled(uint16_t h, float scale) {
   float x = orc_bf16_to_f32(h);

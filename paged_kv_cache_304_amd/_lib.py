@@ -4,7 +4,10 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
+# PAGEDKV_LIB selects another build of the same library (the CPU sanitizer test
+# loads its host-sanitized copy this way).
+LIB_PATH = os.environ.get("PAGEDKV_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                         "libpagedkv.so")
 
 # pa_status codes
 PA_OK, PA_EINVAL, PA_EDTYPE, PA_EUNSUPPORTED, PA_EHIP, PA_EWORKSPACE, PA_ENOSPACE = 0, 1, 2, 3, 4, 5, 6

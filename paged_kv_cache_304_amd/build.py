@@ -40,10 +40,19 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+# AddressSanitizer + UndefinedBehaviorSanitizer on the host code only (argument
+# checks, launch set-up, the block manager); device code is compiled as usual.
+# Each flag is given for the host side explicitly. CPU test builds only.
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer",
+                  "-Xarch_host", "-shared-libsan", "-g"]
+SANITIZE_DIR = os.path.join(BUILD_DIR, "asan")
+
+
+def _compile(src: str, out_dir: str = BUILD_DIR, extra=()) -> str:
+    obj = os.path.join(out_dir, os.path.basename(src) + ".o")
     flags = HOST_FLAGS if src.endswith(".cpp") else COMMON_FLAGS
-    cmd = [HIPCC, *flags, "-c", src, "-o", obj]
+    cmd = [HIPCC, *flags, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
@@ -54,20 +63,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build_library(jobs: int | None = None) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build_library(jobs: int | None = None, sanitize: bool = False) -> str:
+    """Build libpagedkv.so next to this file; with ``sanitize``, a host-sanitized
+    copy in _build/asan/ instead (for the CPU sanitizer test; load it with the
+    PAGEDKV_LIB environment variable and clang's ASan runtime preloaded)."""
+    out_dir = SANITIZE_DIR if sanitize else BUILD_DIR
+    lib_path = os.path.join(SANITIZE_DIR, "libpagedkv.so") if sanitize else LIB_PATH
+    extra = SANITIZE_FLAGS if sanitize else []
+    os.makedirs(out_dir, exist_ok=True)
     srcs = sources()
     jobs = jobs or min(len(srcs), max(1, (os.cpu_count() or 4)))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB_PATH + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+        objs = list(ex.map(lambda f: _compile(f, out_dir, extra), srcs))
+    tmp = lib_path + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *extra, *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":
-    print(build_library())
+    print(build_library(sanitize="--sanitize" in sys.argv))

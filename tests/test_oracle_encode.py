@@ -112,3 +112,26 @@ def test_bf16_widen_is_exact_and_round_trips():
     x = bf16_bits_to_f32(ALL_BF16)
     ok = ~np.isnan(x)
     assert np.array_equal(oracle.f32_to_bf16(x[ok]), ALL_BF16[ok])
+
+
+def test_array_encode_equals_the_scalar_encodes_and_torch():
+    """The array entry used by the exhaustive GPU sweep is the scalar encodes
+    element by element: 300k fp32 bit patterns drawn over every class (normals,
+    subnormals, zeros, infinities, NaNs of every payload), against the scalar
+    oracle calls and against torch's casts (NaN-ness only for bf16 NaNs)."""
+    rng = np.random.default_rng(32)
+    bits = rng.integers(0, 1 << 32, size=300_000, dtype=np.uint64).astype(np.uint32)
+    bits[:64] = np.array([0, 0x80000000, 0x7F800000, 0xFF800000, 0x7FC00000, 0xFFC00001, 0x00000001,
+                          0x807FFFFF, 0x43E00000, 0x43E80000, 0x43EFFFFF, 0x43F00000] * 5 + [1, 2, 3, 4],
+                         dtype=np.uint32)
+    x = bits.view(np.float32)
+    b16 = oracle.encode_f32_array(x, oracle.BF16)
+    f8 = oracle.encode_f32_array(x, oracle.FP8_E4M3FN)
+    sample = slice(0, 3000)
+    assert np.array_equal(b16[sample], oracle.f32_to_bf16(x[sample]))
+    assert np.array_equal(f8[sample], oracle.f32_to_e4m3fn(x[sample]))
+    nan = np.isnan(x)
+    tb = torch_bf16(x)
+    assert np.array_equal(b16[~nan], tb[~nan])
+    assert np.all((b16[nan] & 0x7FFF) > 0x7F80)
+    assert np.array_equal(f8, torch_fp8(x))
