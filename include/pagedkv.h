@@ -344,7 +344,7 @@ pa_status pa_decode_step(const void* new_k, const void* new_v, pa_dtype new_dtyp
  * attention with GQA: many query tokens per sequence against the sequence's
  * paged K/V, the other half of an engine's attention next to decode.
  *
- * Defined by: "nano-vLLM Qwen3 reading notes", section 2.4 (prefill queries
+ * Defined by: Qwen3-0.6B engine walkthrough page, section 2.4 (prefill queries
  * are packed token-major and delimited by cu_seqlens_q, the prefix sums of
  * the per-sequence query counts) and section 2.6 (the variable-length flash
  * path of prefill); "PagedAttention principle" page, autoregressive dataflow
@@ -485,8 +485,8 @@ pa_status pa_mla_decode_attention(void* out, pa_dtype out_dtype, int64_t out_seq
  * the host knows every request's blocks and copies the table to the device
  * before the launch; and the design must stay usable under graph capture
  * (fixed shapes, no data-dependent host branching in the captured work).
- * The slot of a position is the "Triton paged KV cache write" page's: slot =
- * block * block_size + offset (section 2.6).
+ * The slot of a position is the Qwen3-0.6B engine walkthrough page's
+ * (section 2.6): slot = block * block_size + offset.
  *
  * Sequences are ids 0..max_seqs-1. A sequence's length is the number of
  * token positions it has been given; it holds exactly ceil(length /

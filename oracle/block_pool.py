@@ -5,7 +5,7 @@ memory is handed out in blocks of ``block_size`` token slots, so a request of n
 tokens holds ceil(n / block_size) blocks and wastes less than one block; the
 blocks need not be adjacent, a table keeps their order; the host knows each
 request's blocks and hands the table to the kernels. A position's slot is the
-"Triton paged KV cache write" page's block * block_size + offset (section 2.6).
+Qwen3-0.6B engine walkthrough page's block * block_size + offset (section 2.6).
 
 The pages fix no order in which free blocks are handed out (reading R12): here
 the free list starts as 0, 1, ..., num_blocks - 1; a step takes blocks from its

@@ -10,7 +10,7 @@
  * table or helper with the HIP path.
  *
  * Sources (the web pages this project follows):
- *  - "nano-vLLM Qwen3 reading notes", section 2.6 "Attention": the Triton
+ *  - Qwen3-0.6B engine walkthrough page, section 2.6 "Attention": the Triton
  *    store_kvcache kernel, its cache layout [num_blocks, block_size, H_KV, d_h],
  *    the slot -> (block, offset) split and the skip of slot -1, and the worked
  *    source-offset example (token 5, head 3 -> elements 5504..5631).
@@ -19,7 +19,7 @@
  *    the decode dataflow (the new token is written before attention) and the
  *    block allocation paragraph (a block is [block_size, H_KV, d_h]; blocks are
  *    physically scattered and found through a table).
- *  - "nano-vLLM Qwen3 reading notes", section 2.4 (the LM head): queries of a
+ *  - Qwen3-0.6B engine walkthrough page, section 2.4 (the LM head): queries of a
  *    prefill batch are packed token-major and delimited by cu_seqlens_q
  *    (prefix sums of the per-sequence query counts); section 2.6 names the
  *    variable-length flash path of prefill.

@@ -7,8 +7,8 @@
 // section: a request of n tokens holds ceil(n / block_size) blocks (less than
 // one block wasted), its blocks need not be adjacent and a table keeps their
 // order, and the host copies that table to the device before the kernel runs.
-// Slots are the "Triton paged KV cache write" page's block * block_size +
-// offset (section 2.6).
+// Slots are the Qwen3-0.6B engine walkthrough page's (section 2.6)
+// block * block_size + offset.
 //
 // State is plain arrays sized at creation: a free stack, and per sequence its
 // length, block count and a max_blocks_per_seq row of block ids. Planning a

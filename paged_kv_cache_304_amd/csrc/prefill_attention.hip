@@ -1,7 +1,7 @@
 // pa_prefill_attention: chunked-prefill (variable-length, causal) attention of
 // packed query tokens against their sequences' paged K/V.
 //
-// Operation ("nano-vLLM Qwen3 reading notes", section 2.4: prefill queries are
+// Operation (Qwen3-0.6B engine walkthrough page, section 2.4: prefill queries are
 // packed token-major and delimited by cu_seqlens_q; section 2.6: the
 // variable-length flash path of prefill; "PagedAttention principle" page,
 // autoregressive dataflow: prefill attends causally over the prompt while its
