@@ -15,7 +15,7 @@ bf16 -> fp8 cache write measured in the same run with a cold Infinity Cache.
 
 Other workloads (parity-test configurations, for measurement only):
 ``--workload decode_fp8_b256 | decode_b64_tp2 | prefill_fp8 | mla_concat_swa | mla_fused |
-prefill_chunks | engine_decode_b64 | mla_decode_b64``.
+prefill_chunks | prefill_chunks_fp8 | engine_decode_b64 | mla_decode_b64``.
 """
 from __future__ import annotations
 
@@ -46,7 +46,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--workload", default="decode_b64",
                    choices=["decode_b64", "decode_b64_tp2", "prefill_fp8", "decode_fp8_b256", "mla_concat_swa",
-                            "mla_fused", "prefill_chunks", "engine_decode_b64",
+                            "mla_fused", "prefill_chunks", "prefill_chunks_fp8", "engine_decode_b64",
                             "mla_decode_b64"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--profile-steps", type=int, default=0,
@@ -602,12 +602,20 @@ def prefill_flops(w) -> int:
     return total * w["num_q_heads"] * w["head_size"] * 4
 
 
-def run_prefill_chunks(args, torch, pkv, workloads):
+def run_prefill_chunks(args, torch, pkv, workloads, fp8=False):
     w = workloads.prefill_chunks()
     B, HQ, HKV, D, BS, NB, T = (w["num_seqs"], w["num_q_heads"], w["num_kv_heads"], w["head_size"],
                                 w["block_size"], w["num_blocks"], w["num_tokens"])
-    kc = workloads.device_normal((NB, BS, HKV, D), torch.bfloat16, "cuda", w["seed"])
-    vc = workloads.device_normal((NB, BS, HKV, D), torch.bfloat16, "cuda", w["seed"] + 1)
+    ks = vs = None
+    if fp8:  # the same workload over an fp8 e4m3fn pool (k/v scales 0.05/0.04)
+        w = dict(w, name=w["name"].replace("_bf16", "_fp8"))
+        kc = workloads.device_fp8((NB, BS, HKV, D), "cuda", w["seed"], 0.05)
+        vc = workloads.device_fp8((NB, BS, HKV, D), "cuda", w["seed"] + 1, 0.04)
+        ks = torch.tensor([0.05], dtype=torch.float32, device="cuda")
+        vs = torch.tensor([0.04], dtype=torch.float32, device="cuda")
+    else:
+        kc = workloads.device_normal((NB, BS, HKV, D), torch.bfloat16, "cuda", w["seed"])
+        vc = workloads.device_normal((NB, BS, HKV, D), torch.bfloat16, "cuda", w["seed"] + 1)
     q = workloads.device_normal((T, HQ, D), torch.bfloat16, "cuda", w["seed"] + 2)
     out = torch.empty_like(q)
     cu = torch.from_numpy(w["cu_seqlens_q"]).cuda()
@@ -615,10 +623,10 @@ def run_prefill_chunks(args, torch, pkv, workloads):
     cl = torch.from_numpy(w["context_lens"]).cuda()
 
     def step():
-        pkv.prefill_attention(out, q, cu, kc, vc, bt, cl, w["softmax_scale"])
+        pkv.prefill_attention(out, q, cu, kc, vc, bt, cl, w["softmax_scale"], ks, vs)
 
     flops = prefill_flops(w)
-    kv_bytes = int(2 * int(w["context_lens"].astype(np.int64).sum()) * HKV * D * 2)
+    kv_bytes = int(2 * int(w["context_lens"].astype(np.int64).sum()) * HKV * D * (1 if fp8 else 2))
     stream = torch.cuda.current_stream()
     if args.profile_steps:
         copy_calibration(torch, pkv)
@@ -644,7 +652,8 @@ def run_prefill_chunks(args, torch, pkv, workloads):
         "metric": "chunked-prefill paged attention TFLOP/s (1 MI355X)",
         "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 (fp8_e4m3fn cache)" if fp8 else "bf16",
         "data": "synthetic (seeded N(0,1) K/V/q of Qwen3-0.6B shapes)",
         "config": {"workload": w["name"], "num_seqs": B, "num_tokens": T, "num_q_heads": HQ,
                    "num_kv_heads": HKV, "head_size": D, "block_size": BS,
@@ -658,20 +667,24 @@ def run_prefill_chunks(args, torch, pkv, workloads):
     }
     if not args.no_cpu_baseline:
         import oracle
-        res["cpu_baseline"] = cpu_baseline_prefill(torch, q, kc, vc, w, oracle)
+        res["cpu_baseline"] = cpu_baseline_prefill(torch, q, kc, vc, w, oracle, fp8)
     print(json.dumps(res))
 
 
-def cpu_baseline_prefill(torch, q, kc, vc, w, oracle):
+def cpu_baseline_prefill(torch, q, kc, vc, w, oracle, fp8=False):
     """The oracle on the whole call (every sequence, row and head; about ten
     seconds on 16 host cores), reported in the metric's unit."""
-    import time
     qh = q.view(torch.int16).cpu().numpy().view(np.uint16)
-    kh = kc.view(torch.int16).cpu().numpy().view(np.uint16)
-    vh = vc.view(torch.int16).cpu().numpy().view(np.uint16)
+    if fp8:
+        kh, vh = kc.view(torch.uint8).cpu().numpy(), vc.view(torch.uint8).cpu().numpy()
+        cdt, ks, vs = oracle.FP8_E4M3FN, 0.05, 0.04
+    else:
+        kh = kc.view(torch.int16).cpu().numpy().view(np.uint16)
+        vh = vc.view(torch.int16).cpu().numpy().view(np.uint16)
+        cdt, ks, vs = oracle.BF16, None, None
     n, dt = repeat_for(lambda: oracle.prefill_attention(
-        qh, oracle.BF16, w["cu_seqlens_q"], kh, vh, oracle.BF16, w["block_tables"], w["context_lens"],
-        w["softmax_scale"]))
+        qh, oracle.BF16, w["cu_seqlens_q"], kh, vh, cdt, w["block_tables"], w["context_lens"],
+        w["softmax_scale"], ks, vs))
     flops = prefill_flops(w)
     return {"value": round(n * flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.max_threads(),
             "kind": "oracle",
@@ -1082,6 +1095,8 @@ def main():
         run_prefill_fp8(args, torch, pkv, workloads)
     elif args.workload == "prefill_chunks":
         run_prefill_chunks(args, torch, pkv, workloads)
+    elif args.workload == "prefill_chunks_fp8":
+        run_prefill_chunks(args, torch, pkv, workloads, fp8=True)
     elif args.workload == "mla_fused":
         run_mla_fused(args, torch, pkv, workloads)
     elif args.workload == "engine_decode_b64":

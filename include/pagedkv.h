@@ -370,7 +370,8 @@ pa_status pa_decode_step(const void* new_k, const void* new_v, pa_dtype new_dtyp
  *            cu[num_seqs] = num_tokens (values are clamped into [0, num_tokens]
  *            for memory safety; rows no sequence owns are not written).
  *   key_cache, value_cache, block_tables, context_lens, k_scale, v_scale: as
- *            for pa_decode_attention; cache_dtype PA_BF16.
+ *            for pa_decode_attention; cache_dtype PA_BF16 or PA_FP8_E4M3FN
+ *            (fp8 values are dequantised by multiplying with the scales).
  * No workspace: each query row's softmax is completed inside one workgroup.
  * Supported: head_size in {64, 128}; num_q_heads / num_kv_heads in
  *   {1, 2, 4, 8}; block_size a multiple of 16.

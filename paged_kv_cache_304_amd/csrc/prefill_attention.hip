@@ -189,9 +189,22 @@ __device__ __forceinline__ float bcast_lane(float x, int src) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(x)));
 }
 
-template <int D, int G>
+// fp8 caches: the tile's K and V arrive as e4m3fn into a staging ring in row
+// order (row r of the tile at r * D bytes), and each lane converts the 16-byte
+// chunks it fetched into the bf16 reader-ordered tiles (fp8 values are exact
+// in bf16) before the tile's products read them.
+template <int D>
+struct Geo8 {
+  static constexpr int TB = kKeys * D;         // bytes per fp8 K (or V) tile
+  static constexpr int TI = TB / 1024;         // 1 KB wave loads per K (or V) tile
+  static constexpr int IPW = 2 * TI / kWaves;  // ... per wave and tile, K and V together
+  static_assert(TB % 1024 == 0 && (2 * TI) % kWaves == 0 && IPW >= 1, "fp8 tile / wave split");
+};
+
+template <int D, int G, bool kFp8>
 __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma_kernel(PfArgs a) {
   using Gm = Geo<D>;
+  using G8 = Geo8<D>;
   constexpr int KS = Gm::KS, CB = Gm::CB;
   constexpr int QT = kRows / G;  // query tokens per workgroup
   const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, lg = lane >> 4;
@@ -210,17 +223,25 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
   // One shared object with the K/V ring first, so that every LDS-DMA
   // destination lies in the first 64 KB of LDS (the range the DMA path is used
   // in throughout this library).
+  // bf16 caches: a kBufs-slot ring of bf16 tiles filled by the DMA. fp8
+  // caches: a kBufs-slot ring of fp8 tiles filled by the DMA (first, below
+  // 64 KB) and two bf16 tiles (the tile in P.V and the tile in S).
+  constexpr int kDmaBufs = kBufs, kBfBufs = kFp8 ? 2 : kBufs;
+  constexpr int kDmaTile = kFp8 ? G8::TB : Gm::TB;
   struct Smem {
-    char kv[kBufs][2][Gm::TB];  // [buffer][K, V]
+    char dma[kDmaBufs][2][kDmaTile];  // [slot][K, V]: the DMA ring (bf16: the operand tiles)
+    char bf[kFp8 ? kBfBufs : 1][2][kFp8 ? Gm::TB : 16];  // fp8: converted operand tiles
     int tab[kTab];              // validated table entries of blocks tab_base ..
     int64_t wave_tiles[kWaves];
     int found[2];               // sequence, tile index within it
     int bins[kBins];            // query tiles per length class
     int64_t pick[2];            // the class holding this workgroup's tile, its rank inside
   };
-  static_assert(sizeof(Smem::kv) <= 65536, "LDS-DMA targets stay below 64 KB");
+  static_assert(sizeof(Smem::dma) <= 65536, "LDS-DMA targets stay below 64 KB");
   __shared__ __attribute__((aligned(16))) Smem sm;
-  auto& kv_lds = sm.kv;
+  // operand tiles (bf16, reader-ordered) of key tile t
+  auto ktile = [&](int t) -> const char* { return kFp8 ? sm.bf[t % kBfBufs][0] : sm.dma[t % kBufs][0]; };
+  auto vtile = [&](int t) -> const char* { return kFp8 ? sm.bf[t % kBfBufs][1] : sm.dma[t % kBufs][1]; };
   auto& wave_tiles = sm.wave_tiles;
   auto& found = sm.found;
   auto& tab = sm.tab;
@@ -413,38 +434,87 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
   const char* kc = static_cast<const char*>(a.kc);
   const char* vc = static_cast<const char*>(a.vc);
   // This wave's IPW of the tile's 2*TI 1 KB loads (K loads first, then V):
-  // lane l of a load fills LDS slot l of that kilobyte, so it fetches the
-  // chunk the reader-ordered layout puts there. The lane's element offset
-  // inside its 16-key block is fixed; only the blocks' bases change per tile.
-  int64_t lane_el[Gm::IPW];
-  int lane_kb[Gm::IPW];
+  // lane l of a load fills LDS slot l of that kilobyte. bf16: it fetches the
+  // chunk the reader-ordered layout puts there. fp8: the tile is staged in row
+  // order, slot l of load ii holding row (1024 ii + 16 l) / D, 16 dims from
+  // 16 * (((1024 ii + 16 l) % D) / 16). The lane's element offset inside its
+  // 16-key block is fixed; only the blocks' bases change per tile.
+  constexpr int kIPW = kFp8 ? G8::IPW : Gm::IPW;
+  constexpr int kTI = kFp8 ? G8::TI : Gm::TI;
+  constexpr int kEB = kFp8 ? 1 : 2;  // bytes per cache element
+  int64_t lane_el[kIPW];
+  int lane_kb[kIPW];
+  int lane_row[kIPW], lane_chunk[kIPW];  // fp8: tile row and 16-dim chunk of the staged slot
 #pragma unroll
-  for (int i = 0; i < Gm::IPW; ++i) {
-    const int ii = wave * Gm::IPW + i;
-    int row, chunk;
-    if (ii < Gm::TI) {  // K read (kb, s) = (ii / KS, ii % KS)
+  for (int i = 0; i < kIPW; ++i) {
+    const int ii = wave * kIPW + i;
+    int row, el;
+    if constexpr (kFp8) {
+      const int byte = 1024 * (ii % kTI) + 16 * lane;
+      row = byte / D;
+      lane_row[i] = row;
+      lane_chunk[i] = (byte % D) / 16;
+      el = 16 * lane_chunk[i];
+    } else if (ii < Gm::TI) {  // K read (kb, s) = (ii / KS, ii % KS)
       row = 16 * (ii / Gm::KS) + (lane & 15);
-      chunk = 4 * (ii % Gm::KS) + (lane >> 4);
+      el = 8 * (4 * (ii % Gm::KS) + (lane >> 4));
     } else {            // V regions 2(ii - TI) and 2(ii - TI) + 1
       const int region = 2 * (ii - Gm::TI) + (lane >> 5);
       const int q = lane & 31;
       const int st = region / (2 * Gm::CB), cb = (region >> 1) % Gm::CB, half = region & 1;
       row = 32 * st + 16 * half + 4 * (q >> 3) + ((q & 7) >> 1);
-      chunk = 2 * cb + (q & 1);
+      el = 8 * (2 * cb + (q & 1));
     }
     lane_kb[i] = row >> 4;
-    lane_el[i] = (int64_t)(row & 15) * row_el + (int64_t)g * D + 8 * chunk;
+    lane_el[i] = (int64_t)(row & 15) * row_el + (int64_t)g * D + el;
   }
   auto fetch = [&](int buf, const TileAddr& ta) {
 #pragma unroll
-    for (int i = 0; i < Gm::IPW; ++i) {
-      const int ii = wave * Gm::IPW + i;
+    for (int i = 0; i < kIPW; ++i) {
+      const int ii = wave * kIPW + i;
       int64_t base = ta.base[0];
 #pragma unroll
       for (int kb = 1; kb < kKB; ++kb) base = lane_kb[i] == kb ? ta.base[kb] : base;
-      const char* src0 = ii < Gm::TI ? kc : vc;
-      char* dst = kv_lds[buf][ii < Gm::TI ? 0 : 1] + (ii % Gm::TI) * 1024;
-      dma_16B(src0 + (base + lane_el[i]) * 2, lds_addr(dst));
+      const char* src0 = ii < kTI ? kc : vc;
+      char* dst = sm.dma[buf][ii < kTI ? 0 : 1] + (ii % kTI) * 1024;
+      dma_16B(src0 + (base + lane_el[i]) * kEB, lds_addr(dst));
+    }
+  };
+  // fp8: this lane's staged chunks of tile t (landed) -> the bf16 operand tiles.
+  // K chunk (row r, dims 16c..+15) -> reads (kb, s) = (r/16, c/2), lanes
+  // 16 (2(c%2)) + r%16 and 16 (2(c%2) + 1) + r%16; V chunk -> 16-byte slots q0,
+  // q0 + 1 of block (cb, half) = (c, r/16), q0 = 8 ((r%16)/4) + 2 (r%4).
+  auto convert = [&](int t) {
+    if constexpr (kFp8) {
+#pragma unroll
+      for (int i = 0; i < kIPW; ++i) {
+        const int ii = wave * kIPW + i;
+        const bool is_k = ii < kTI;
+        const u32x4 w = *reinterpret_cast<const u32x4*>(sm.dma[t % kBufs][is_k ? 0 : 1] + (ii % kTI) * 1024 +
+                                                         16 * lane);
+        u32x4 lo8, hi8;  // dims +0..7 and +8..15 as bf16
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const f32x2 a0 = fp8x2_lo(w[e]), a1 = fp8x2_hi(w[e]);
+          lo8[2 * e] = f32x2_to_bf16x2(a0[0], a0[1]);
+          lo8[2 * e + 1] = f32x2_to_bf16x2(a1[0], a1[1]);
+          const f32x2 b0 = fp8x2_lo(w[2 + e]), b1 = fp8x2_hi(w[2 + e]);
+          hi8[2 * e] = f32x2_to_bf16x2(b0[0], b0[1]);
+          hi8[2 * e + 1] = f32x2_to_bf16x2(b1[0], b1[1]);
+        }
+        const int r = lane_row[i], c = lane_chunk[i];
+        char* bt = sm.bf[t % kBfBufs][is_k ? 0 : 1];
+        if (is_k) {
+          const int kb = r >> 4, s = c >> 1, l0 = 16 * (2 * (c & 1)) + (r & 15);
+          *reinterpret_cast<u32x4*>(bt + Gm::k_off(kb, s, l0)) = lo8;
+          *reinterpret_cast<u32x4*>(bt + Gm::k_off(kb, s, l0 + 16)) = hi8;
+        } else {
+          const int q0 = 8 * ((r & 15) >> 2) + 2 * (r & 3);
+          char* blk = bt + ((0 * CB + c) * 2 + (r >> 4)) * 512 + 16 * q0;
+          *reinterpret_cast<u32x4*>(blk) = lo8;
+          *reinterpret_cast<u32x4*>(blk + 16) = hi8;
+        }
+      }
     }
   };
 
@@ -463,8 +533,8 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
   // kMask: some score of the tile is causal-masked, past the context end, or
   // in a block outside the pool.
   constexpr int kSt = kKeys / 32;  // 32-key steps of P.V
-  auto qk = [&](int buf, f32x4 (&sc)[2][kKB]) {
-    const char* kl = kv_lds[buf][0];
+  auto qk = [&](int t, f32x4 (&sc)[2][kKB]) {
+    const char* kl = ktile(t);
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb) {
       sc[0][kb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -570,10 +640,10 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
   // O += P V, V's operand by transposing reads (lane m of a 16-lane group
   // reads row kbase + m/4, columns 16cb + 4(m%4) .. +3, kbase = 32st + 4g,
   // then + 16); the two reads are the operand's low and high halves.
-  auto pv = [&](int kt, int buf, int okbits, const bf16x8 (&pop)[2][kSt], const bf16x8 (&plo)[2][kSt],
+  auto pv = [&](int kt, int okbits, const bf16x8 (&pop)[2][kSt], const bf16x8 (&plo)[2][kSt],
                 auto mask_tag) {
     constexpr bool kMask = decltype(mask_tag)::value;
-    const char* vl = kv_lds[buf][1];
+    const char* vl = vtile(kt);
     const int key0 = kt * kKeys;
 #pragma unroll
     for (int st = 0; st < kSt; ++st) {
@@ -606,7 +676,9 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
     }
   };
 
-  // ---- key loop. Ring of kBufs = 4 tiles: tile kt (P.V), kt + 1 (its
+  // ---- key loop (fp8 caches: after a tile's barrier each lane converts its
+  // staged chunks into the tile's bf16 slot, then a second barrier; the bf16
+  // slot of tile t is free once tile t - 2's P.V is done). Ring of kBufs = 4 tiles: tile kt (P.V), kt + 1 (its
   // scores, computed while tile kt's softmax runs) and two tiles in flight.
   // Iteration kt: wait for this wave's share of tile kt + 1, one barrier
   // (every wave's share has landed, and every wave is done with tile kt - 1,
@@ -617,7 +689,7 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
   // loads per tile, so a wait leaves exactly the later tile's loads
   // outstanding.
   static_assert(kBufs == 4, "ring: tile in P.V, tile in S, two in flight");
-  constexpr int kLoadsPerTile = Gm::IPW;
+  constexpr int kLoadsPerTile = kIPW;
   static_assert(2 * kLoadsPerTile <= 63, "vmcnt range");
   constexpr int kAll = (1 << kKB) - 1;
   int okring = 0;  // bits 4 * (t % kBufs) ..: 16-key blocks of tile t inside the pool
@@ -650,6 +722,10 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
       __syncthreads();
     }
     next_tile_addr(tn + 1, ta_next);
+    if constexpr (kFp8) {  // tile t into its bf16 slot (freed by tile t - 2's P.V), then visible
+      convert(t);
+      barrier_no_vmem_wait();
+    }
   };
   f32x4 sc_cur[2][kKB], sc_nxt[2][kKB];
   bf16x8 pop[2][kSt], plo[2][kSt];
@@ -663,6 +739,10 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
     else
       wait_vmem<0>();
     barrier_no_vmem_wait();
+    if constexpr (kFp8) {  // tile 0 into bf16, visible to every wave
+      convert(0);
+      barrier_no_vmem_wait();
+    }
     qk(0, sc_cur);
   }
   // Two loops, each with one variant of the softmax and P.V (both variants in
@@ -678,12 +758,12 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
     // tile kt+1's scores (after the last tile: a stale buffer, never used) in
     // the same block as tile kt's softmax, so their issue interleaves
     if (kPrioSM) set_prio<kPrioSM>();
-    qk((kt + 1) % kBufs, sc_nxt);
+    qk(kt + 1, sc_nxt);
     softmax(kt, okb, sc_cur, pop, plo, alpha, moved, std::false_type{});
     interleave_hint();
     rescale(alpha, moved);
     if (kPrioSM) set_prio<0>();
-    pv(kt, kt % kBufs, okb, pop, plo, std::false_type{});
+    pv(kt, okb, pop, plo, std::false_type{});
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
@@ -695,12 +775,12 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
     // tile kt+1's scores (after the last tile: a stale buffer, never used) in
     // the same block as tile kt's softmax, so their issue interleaves
     if (kPrioSM) set_prio<kPrioSM>();
-    qk((kt + 1) % kBufs, sc_nxt);
+    qk(kt + 1, sc_nxt);
     softmax(kt, okb, sc_cur, pop, plo, alpha, moved, std::true_type{});
     interleave_hint();
     rescale(alpha, moved);
     if (kPrioSM) set_prio<0>();
-    pv(kt, kt % kBufs, okb, pop, plo, std::true_type{});
+    pv(kt, okb, pop, plo, std::true_type{});
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
@@ -740,14 +820,14 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
   }
 }
 
-template <int D>
+template <int D, bool kFp8>
 bool launch_g(int G, const PfArgs& a, hipStream_t st) {
   const unsigned grid = (unsigned)((a.tiles_ub * a.HKV + 7) / 8 * 8);
   switch (G) {
-    case 1: prefill_mfma_kernel<D, 1><<<grid, 64 * kWaves, 0, st>>>(a); return true;
-    case 2: prefill_mfma_kernel<D, 2><<<grid, 64 * kWaves, 0, st>>>(a); return true;
-    case 4: prefill_mfma_kernel<D, 4><<<grid, 64 * kWaves, 0, st>>>(a); return true;
-    case 8: prefill_mfma_kernel<D, 8><<<grid, 64 * kWaves, 0, st>>>(a); return true;
+    case 1: prefill_mfma_kernel<D, 1, kFp8><<<grid, 64 * kWaves, 0, st>>>(a); return true;
+    case 2: prefill_mfma_kernel<D, 2, kFp8><<<grid, 64 * kWaves, 0, st>>>(a); return true;
+    case 4: prefill_mfma_kernel<D, 4, kFp8><<<grid, 64 * kWaves, 0, st>>>(a); return true;
+    case 8: prefill_mfma_kernel<D, 8, kFp8><<<grid, 64 * kWaves, 0, st>>>(a); return true;
     default: return false;
   }
 }
@@ -783,7 +863,8 @@ extern "C" pa_status pa_prefill_attention(void* out, pa_dtype out_dtype, int64_t
   if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX) return fail(PA_EINVAL, "%s: max_blocks_per_seq*block_size too large", fn);
   if (out_dtype != PA_BF16 && out_dtype != PA_F32) return fail(PA_EDTYPE, "%s: out dtype %s not supported", fn, dtype_name(out_dtype));
   if (q_dtype != PA_BF16) return fail(PA_EDTYPE, "%s: q dtype %s not supported (bf16)", fn, dtype_name(q_dtype));
-  if (cache_dtype != PA_BF16) return fail(PA_EDTYPE, "%s: cache dtype %s not supported (bf16)", fn, dtype_name(cache_dtype));
+  if (cache_dtype != PA_BF16 && cache_dtype != PA_FP8_E4M3FN)
+    return fail(PA_EDTYPE, "%s: cache dtype %s not supported (bf16, fp8_e4m3fn)", fn, dtype_name(cache_dtype));
   if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return fail(PA_EINVAL, "%s: softmax_scale is not finite", fn);
   const int64_t row = (int64_t)num_q_heads * head_size;
   if (out_token_stride < row || q_token_stride < row) return fail(PA_EINVAL, "%s: token strides smaller than H_Q*head_size", fn);
@@ -795,8 +876,11 @@ extern "C" pa_status pa_prefill_attention(void* out, pa_dtype out_dtype, int64_t
   const int ob = dtype_bytes(out_dtype);
   if (!aligned(q, 16) || (q_token_stride * 2) % 16 != 0) return fail(PA_EINVAL, "%s: q must be 16-byte aligned per token", fn);
   if (!aligned(out, 16) || (out_token_stride * ob) % 16 != 0) return fail(PA_EINVAL, "%s: out must be 16-byte aligned per token", fn);
-  if (!aligned(key_cache, 16) || !aligned(value_cache, 16) || (block_stride * 2) % 16 != 0)
+  const int cbytes = dtype_bytes(cache_dtype);
+  if (!aligned(key_cache, 16) || !aligned(value_cache, 16) || (block_stride * cbytes) % 16 != 0)
     return fail(PA_EINVAL, "%s: caches must be 16-byte aligned per block", fn);
+  if (((int64_t)num_kv_heads * head_size * cbytes) % 16 != 0)
+    return fail(PA_EINVAL, "%s: cache rows must be a multiple of 16 bytes", fn);
 
   PfArgs a;
   a.out = out;
@@ -830,7 +914,9 @@ extern "C" pa_status pa_prefill_attention(void* out, pa_dtype out_dtype, int64_t
   }
   if (a.tiles_ub * num_kv_heads + 7 > 0x7FFFFFFF) return fail(PA_EINVAL, "%s: too many query tiles", fn);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const bool ok = head_size == 64 ? launch_g<64>(G, a, st) : launch_g<128>(G, a, st);
+  const bool fp8 = cache_dtype == PA_FP8_E4M3FN;
+  const bool ok = head_size == 64 ? (fp8 ? launch_g<64, true>(G, a, st) : launch_g<64, false>(G, a, st))
+                                  : (fp8 ? launch_g<128, true>(G, a, st) : launch_g<128, false>(G, a, st));
   if (!ok) return fail(PA_EUNSUPPORTED, "%s: no kernel for this shape", fn);
   return after_launch(fn);
 }

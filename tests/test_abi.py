@@ -204,7 +204,8 @@ def prefill(L, **over):
     (dict(B=-1), "PA_EINVAL"),
     (dict(odt=3), "PA_EDTYPE"),
     (dict(qdt=2), "PA_EDTYPE"),
-    (dict(cdt=3), "PA_EDTYPE"),              # fp8 prefill is not built
+    (dict(cdt=2), "PA_EDTYPE"),              # f32 caches
+    (dict(cdt=3, bstride=16 * 8 * 128 + 8), "PA_EINVAL"),  # fp8 blocks not 16-byte aligned
     (dict(scale=float("inf")), "PA_EINVAL"),
     (dict(qs=100), "PA_EINVAL"),
     (dict(bstride=10), "PA_EINVAL"),

@@ -6,8 +6,9 @@ bf16 outputs are one more rounding, allowed half a bf16 ulp only where
 Cases: ragged chunks on cached prefixes and whole prompts over every group
 size, both head sizes and block sizes 16..64 (48 included), many sequences
 with empties, chunks longer than their context, bad table entries and
-NaN-filled unwritten slots, bit-identical output under block relabelling, and
-the full-size prefill batch (every row and head)."""
+NaN-filled unwritten slots, bit-identical output under block relabelling, the
+full-size prefill batch (every row and head), and the same kinds of cases over
+fp8 e4m3fn caches with k/v scales."""
 import zlib
 
 import numpy as np
@@ -20,8 +21,10 @@ from parity_util import assert_attention_close, say, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
-BF16, F32 = oracle.BF16, oracle.F32
+BF16, F32, FP8 = oracle.BF16, oracle.F32, oracle.FP8_E4M3FN
 NAN_BF16 = 0x7FC0
+NAN_FP8 = 0x7F
+SCALES = (0.05, 0.04)  # fp8 k_scale, v_scale
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -35,7 +38,7 @@ def pkv():
     return m
 
 
-def make_case(seed, ctx, nq, hq, hkv, d, bs, spare=4, width=None):
+def make_case(seed, ctx, nq, hq, hkv, d, bs, spare=4, width=None, cache_dt=BF16):
     """Caches holding each sequence's first ctx_b positions (NaN in every slot no
     sequence owns), packed queries, cu_seqlens."""
     rng = np.random.default_rng(seed)
@@ -46,34 +49,42 @@ def make_case(seed, ctx, nq, hq, hkv, d, bs, spare=4, width=None):
     W = width or max(max(nblk), 1)
     perm = rng.permutation(nb).astype(np.int32)
     bt = workloads.deal_block_tables(perm, ctx, bs, W)
-    kc = workloads.normal_bf16_bits(rng, (nb, bs, hkv, d))
-    vc = workloads.normal_bf16_bits(rng, (nb, bs, hkv, d))
+    if cache_dt == FP8:
+        kc = workloads.normal_fp8_codes(rng, (nb, bs, hkv, d), SCALES[0])
+        vc = workloads.normal_fp8_codes(rng, (nb, bs, hkv, d), SCALES[1])
+    else:
+        kc = workloads.normal_bf16_bits(rng, (nb, bs, hkv, d))
+        vc = workloads.normal_bf16_bits(rng, (nb, bs, hkv, d))
     owned = np.zeros((nb, bs), dtype=bool)
     for b, c in enumerate(ctx):
         pos = np.arange(int(c))
         owned[bt[b, pos // bs], pos % bs] = True
-    kc[~owned] = NAN_BF16
-    vc[~owned] = NAN_BF16
+    kc[~owned] = NAN_FP8 if cache_dt == FP8 else NAN_BF16
+    vc[~owned] = NAN_FP8 if cache_dt == FP8 else NAN_BF16
     cu = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
     q = workloads.normal_bf16_bits(rng, (int(cu[-1]), hq, d))
     return q, kc, vc, bt, ctx, cu
 
 
-def gpu_prefill(q, kc, vc, bt, ctx, cu, scale, out_dt=BF16):
+def gpu_prefill(q, kc, vc, bt, ctx, cu, scale, out_dt=BF16, cache_dt=BF16):
     m = pkv()
     dq = to_dev(q, BF16)
     out = torch.full(dq.shape, float("nan"), dtype=torch.float32 if out_dt == F32 else torch.bfloat16,
                      device="cuda")
-    m.prefill_attention(out, dq, torch.from_numpy(cu).cuda(), to_dev(kc, BF16), to_dev(vc, BF16),
-                        torch.from_numpy(bt).cuda(), torch.from_numpy(ctx).cuda(), scale)
+    ks = vs = None
+    if cache_dt == FP8:
+        ks, vs = (torch.tensor([x], dtype=torch.float32, device="cuda") for x in SCALES)
+    m.prefill_attention(out, dq, torch.from_numpy(cu).cuda(), to_dev(kc, cache_dt), to_dev(vc, cache_dt),
+                        torch.from_numpy(bt).cuda(), torch.from_numpy(ctx).cuda(), scale, ks, vs)
     torch.cuda.synchronize()
     return out
 
 
-def run_and_check(name, q, kc, vc, bt, ctx, cu, scale):
-    ref = oracle.prefill_attention(q, BF16, cu, kc, vc, BF16, bt, ctx, scale)
+def run_and_check(name, q, kc, vc, bt, ctx, cu, scale, cache_dt=BF16):
+    ks, vs = SCALES if cache_dt == FP8 else (None, None)
+    ref = oracle.prefill_attention(q, BF16, cu, kc, vc, cache_dt, bt, ctx, scale, ks, vs)
     for out_dt in (F32, BF16):
-        got = gpu_prefill(q, kc, vc, bt, ctx, cu, scale, out_dt).float().cpu().numpy().astype(np.float64)
+        got = gpu_prefill(q, kc, vc, bt, ctx, cu, scale, out_dt, cache_dt).float().cpu().numpy().astype(np.float64)
         assert_attention_close(got, ref, f"{name} out={'f32' if out_dt == F32 else 'bf16'}",
                                out_bf16=out_dt == BF16)
 
@@ -105,6 +116,49 @@ def test_prefill_matches_oracle(case):
     say(f"prefill_attention {name} B={len(ctx)} T={sum(nq)} H_Q={hq} H_KV={hkv} D={d} bs={bs}")
     q, kc, vc, bt, ctx, cu = make_case(zlib.crc32(name.encode()), ctx, nq, hq, hkv, d, bs, width=width)
     run_and_check(name, q, kc, vc, bt, ctx, cu, float(np.float32(1.0 / np.sqrt(d))))
+
+
+FP8_CASES = [
+    # name, ctx, nq, hq, hkv, d, bs, width -- fp8 e4m3fn caches with k/v scales 0.05/0.04
+    ("fp8 G2 D128 chunks on prefixes", [100, 700, 64, 1000, 129], [37, 128, 64, 1, 129], 16, 8, 128, 16, None),
+    ("fp8 G2 D128 whole prompts", [1, 17, 65, 300], [1, 17, 65, 300], 16, 8, 128, 16, None),
+    ("fp8 G4 D64 bs32", [513, 33, 90], [200, 33, 90], 16, 4, 64, 32, None),
+    ("fp8 G1 D128 bs48", [250, 49], [80, 49], 8, 8, 128, 48, None),
+    ("fp8 G8 D64", [333, 20], [40, 20], 8, 1, 64, 16, None),
+    ("fp8 G2 D128 chunk longer than context, empty sequences",
+     [5, 0, 40, 0, 3], [20, 0, 40, 3, 1], 16, 8, 128, 16, 4),
+    ("fp8 G2 D128 70 sequences",
+     [1 + (i * 97) % 900 for i in range(70)], [(0 if i % 9 == 0 else 1 + (i * 13) % 70) for i in range(70)],
+     16, 8, 128, 16, None),
+]
+
+
+@pytest.mark.parametrize("case", FP8_CASES, ids=[c[0] for c in FP8_CASES])
+def test_prefill_fp8_cache_matches_oracle(case):
+    name, ctx, nq, hq, hkv, d, bs, width = case
+    nq = [min(n, c) if "longer" not in name else n for n, c in zip(nq, ctx)]
+    say(f"prefill_attention {name} B={len(ctx)} T={sum(nq)} H_Q={hq} H_KV={hkv} D={d} bs={bs}")
+    q, kc, vc, bt, ctx, cu = make_case(zlib.crc32(name.encode()), ctx, nq, hq, hkv, d, bs, width=width,
+                                       cache_dt=FP8)
+    run_and_check(name, q, kc, vc, bt, ctx, cu, float(np.float32(1.0 / np.sqrt(d))), cache_dt=FP8)
+
+
+def test_fp8_bad_table_entries_and_relabelling():
+    """fp8 caches: an entry outside the pool drops its positions, and relabelling the
+    physical blocks leaves the output bit-identical."""
+    say("prefill_attention fp8 bad entries + relabelling")
+    q, kc, vc, bt, ctx, cu = make_case(78, [90, 300, 48], [50, 128, 40], 16, 8, 128, 16, spare=12,
+                                       cache_dt=FP8)
+    bt = bt.copy()
+    bt[0, 2] = kc.shape[0] + 3
+    run_and_check("fp8 bad entries", q, kc, vc, bt, ctx, cu, 0.09, cache_dt=FP8)
+    a = gpu_prefill(q, kc, vc, bt, ctx, cu, 0.09, BF16, FP8)
+    perm = np.random.default_rng(2).permutation(kc.shape[0])
+    kc2, vc2 = np.empty_like(kc), np.empty_like(vc)
+    kc2[perm], vc2[perm] = kc, vc
+    bt2 = np.where((bt >= 0) & (bt < kc.shape[0]), perm[np.clip(bt, 0, kc.shape[0] - 1)], bt).astype(np.int32)
+    b = gpu_prefill(q, kc2, vc2, bt2, ctx, cu, 0.09, BF16, FP8)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
 def test_bad_table_entries_and_clamped_lengths():
