@@ -14,7 +14,7 @@ timed on this host on the same step; ``bulk_cache_write`` is the 32,768-token
 bf16 -> fp8 cache write measured in the same run with a cold Infinity Cache.
 
 Other workloads (parity-test configurations, for measurement only):
-``--workload decode_fp8_b256 | decode_b64_tp2 | prefill_fp8 | mla_concat_swa | mla_fused |
+``--workload decode_fp8_b256 | decode_b64_tp2 | decode_b64_bs8 | prefill_fp8 | mla_concat_swa | mla_fused |
 prefill_chunks | prefill_chunks_fp8 | engine_decode_b64 | mla_decode_b64``.
 """
 from __future__ import annotations
@@ -45,7 +45,8 @@ def parse():
     # to 15% slower, so the default warm-up covers well past that
     p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--workload", default="decode_b64",
-                   choices=["decode_b64", "decode_b64_tp2", "prefill_fp8", "decode_fp8_b256", "mla_concat_swa",
+                   choices=["decode_b64", "decode_b64_tp2", "decode_b64_bs8", "prefill_fp8", "decode_fp8_b256",
+                            "mla_concat_swa",
                             "mla_fused", "prefill_chunks", "prefill_chunks_fp8", "engine_decode_b64",
                             "mla_decode_b64"])
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -1001,6 +1002,17 @@ def run_decode_tp2(args, torch, pkv, workloads):
                       "paged decode attn KV-read GB/s & % HBM peak; cache-write GB/s (1 MI355X)")
 
 
+def run_decode_bs8(args, torch, pkv, workloads):
+    """The batch-64 decode step with 8-position cache blocks (same contexts,
+    twice the blocks): a block size that is not a multiple of 16 runs the
+    vector-ALU split kernel instead of the matrix-core persistent one."""
+    import dataclasses
+    w = workloads.qwen3_decode_b64(block_size=8, num_blocks=65536, width=512)
+    w = dataclasses.replace(w, name="qwen3_0.6b_decode_b64_bf16_bs8")
+    return run_decode(args, torch, pkv, workloads, w,
+                      "paged decode attn KV-read GB/s & % HBM peak; cache-write GB/s (1 MI355X)")
+
+
 def run_decode_fp8(args, torch, pkv, workloads):
     w = workloads.mixed_decode_fp8()
     return run_decode(args, torch, pkv, workloads, w,
@@ -1089,6 +1101,8 @@ def main():
         run_decode(args, torch, pkv, workloads, workloads.qwen3_decode_b64(), metric)
     elif args.workload == "decode_b64_tp2":
         run_decode_tp2(args, torch, pkv, workloads)
+    elif args.workload == "decode_b64_bs8":
+        run_decode_bs8(args, torch, pkv, workloads)
     elif args.workload == "decode_fp8_b256":
         run_decode_fp8(args, torch, pkv, workloads)
     elif args.workload == "prefill_fp8":

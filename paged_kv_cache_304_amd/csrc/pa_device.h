@@ -217,4 +217,40 @@ __device__ __forceinline__ int64_t resolve_token_slot(const int64_t* slot_mappin
   return s < pool_slots ? s : -1;
 }
 
+// ------------------------------------------------------- LDS-DMA
+
+// One wave-wide LDS-DMA load: 16 bytes per lane from global memory into LDS at
+// lds_base + 16 * lane (global_load_lds_dwordx4, M0 = LDS base, saved and
+// restored around it). Written as inline asm so that the compiler does not
+// track these LDS writes: it would otherwise put a full vector-memory wait
+// (every load in flight) before LDS reads it cannot prove disjoint from them.
+// A kernel using it orders every load with its own vmcnt waits and barriers.
+// The instruction has no register result; its address registers are read at
+// issue.
+__device__ __forceinline__ void dma_16B(const void* gptr, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
+               : "v"(gptr), "s"(lds_base)
+               : "memory");
+}
+// The same with 4 bytes per lane (global_load_lds_dword): LDS lds_base + 4 * lane.
+__device__ __forceinline__ void dma_4B(const void* gptr, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
+               : "v"(gptr), "s"(lds_base)
+               : "memory");
+}
+// Wait until at most N of this wave's vector-memory operations are in flight
+// (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
 }  // namespace pa

@@ -87,30 +87,6 @@ constexpr int kBufs = 4;                      // LDS ring: tiles in P.V, in S, a
 constexpr float kLazyMax = 8.0f;              // log2 headroom of the running max
 static_assert(kKeys == 32 || kKeys == 64, "key tile");
 
-template <int N>
-__device__ __forceinline__ void wait_vmem() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// One wave-wide LDS-DMA load: 16 bytes per lane from global memory into LDS at
-// lds_base + 16 * lane (global_load_lds_dwordx4, M0 = LDS base, saved and
-// restored around it). Written as inline asm so that the compiler does not
-// track these LDS writes: it would otherwise put a full vector-memory wait
-// (every tile in flight) before LDS reads it cannot prove disjoint from them,
-// such as the transposing V reads. This kernel orders every tile's loads with
-// its own wait_vmem counts and barriers. The instruction has no register
-// result; its address registers are read at issue.
-__device__ __forceinline__ void dma_16B(const void* gptr, uint32_t lds_base) {
-  uint32_t saved;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
-               : "=&s"(saved)
-               : "v"(gptr), "s"(lds_base)
-               : "memory");
-}
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
 // Workgroup barrier without a memory fence. __syncthreads() would also wait
 // for every outstanding vector-memory operation, i.e. drain the K/V tiles in
 // flight; LDS-DMA landing is waited for explicitly with wait_vmem, and every

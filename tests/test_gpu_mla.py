@@ -12,8 +12,8 @@ Cases: ragged contexts around the 32-position tile and the 256-position piece,
 with and without a RoPE part, block sizes 1, 16, 48, 64, other qk / v widths,
 empty contexts, bad table entries and clamped lengths, NaN in every slot no
 sequence owns, bit-identical output under block relabelling, the full batch-64
-workload on sampled sequences, and a decode step whose latent rows are first
-written by concat_and_cache_mla_k."""
+workload on every sequence (one head each), and a decode step whose latent rows
+are first written by concat_and_cache_mla_k."""
 import zlib
 
 import numpy as np
@@ -149,25 +149,37 @@ def full_size_tensors(w):
     return cache, q_nope, q_rope, w_uk, w_uv
 
 
-def test_full_size_mla_batch_sampled():
-    """The batch-64 MLA workload in the launch the benchmark times; two
-    sequences (the shortest and the longest) against the oracle."""
+def test_full_size_mla_batch_every_sequence():
+    """The batch-64 MLA workload in the launch the benchmark times (bf16 out),
+    and again with an fp32 output at the plain bound: every sequence against the
+    oracle on one of its heads (head b % 16, so each head is checked on four
+    sequences). Heads are independent, so head h of sequences b = h (mod 16) is
+    a one-head MLA problem of its own (W_UK and W_UV columns of head h) that the
+    oracle solves at 1/16 of the full cost."""
     m = pkv()
     w = workloads.mla_decode_b64()
     say(f"mla_decode full size {w['name']}")
     cache, q_nope, q_rope, w_uk, w_uv = full_size_tensors(w)
-    out = torch.empty((w["num_seqs"], H, w["v_dim"]), dtype=torch.bfloat16, device="cuda")
-    m.mla_decode_attention(out, q_nope, q_rope, w_uk, w_uv, cache, torch.from_numpy(w["block_tables"]).cuda(),
-                           torch.from_numpy(w["context_lens"]).cuda(), w["softmax_scale"])
-    torch.cuda.synchronize()
-    got = widen_out(out)
+    bt, ctx = w["block_tables"], w["context_lens"]
+    outs = {}
+    for dt in (torch.bfloat16, torch.float32):
+        out = torch.empty((w["num_seqs"], H, w["v_dim"]), dtype=dt, device="cuda")
+        m.mla_decode_attention(out, q_nope, q_rope, w_uk, w_uv, cache, torch.from_numpy(bt).cuda(),
+                               torch.from_numpy(ctx).cuda(), w["softmax_scale"])
+        torch.cuda.synchronize()
+        outs[dt] = widen_out(out)
     ch = to_host(cache, BF16)
-    args = [to_host(t, BF16) for t in (q_nope, q_rope, w_uk, w_uv)]
-    ctx = w["context_lens"]
-    for b in (int(np.argmin(ctx)), int(np.argmax(ctx))):
-        ref = oracle.mla_decode(args[0][b:b + 1], args[1][b:b + 1], args[2], args[3], ch,
-                                w["block_tables"][b:b + 1], ctx[b:b + 1], w["softmax_scale"])
-        assert_attention_close(got[b:b + 1], ref, f"{w['name']} sequence {b} (ctx {ctx[b]})", out_bf16=True)
+    qn, qr, wk, wv = (to_host(t, BF16) for t in (q_nope, q_rope, w_uk, w_uv))
+    QK, DV = w["qk_nope_dim"], w["v_dim"]
+    for h in range(H):
+        sel = np.arange(h, w["num_seqs"], H)
+        ref = oracle.mla_decode(np.ascontiguousarray(qn[sel, h:h + 1]), np.ascontiguousarray(qr[sel, h:h + 1]),
+                                np.ascontiguousarray(wk[:, h * QK:(h + 1) * QK]),
+                                np.ascontiguousarray(wv[:, h * DV:(h + 1) * DV]), ch,
+                                np.ascontiguousarray(bt[sel]), np.ascontiguousarray(ctx[sel]), w["softmax_scale"])
+        for dt, name in ((torch.bfloat16, "bf16"), (torch.float32, "f32")):
+            assert_attention_close(outs[dt][sel, h:h + 1], ref, f"{w['name']} head {h} sequences {list(sel)} out={name}",
+                                   out_bf16=dt == torch.bfloat16)
 
 
 def test_mla_decode_step_writes_latent_rows_then_attends():
