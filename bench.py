@@ -861,28 +861,49 @@ def cpu_baseline_engine(torch, w, W, oracle, kc, vc, q, nk, nv, lens):
                       f"{dt:.1f} s), KV-read bytes / time per step"}
 
 
-def mla_bytes(w) -> dict:
+def mla_segments(ctx: np.ndarray, grid: int, tile: int = 32) -> int:
+    """(workgroup, sequence) segments of the persistent MLA split: the tiles of
+    32 positions of all sequences, in sequence order, cut into ``grid`` even
+    ranges (the first T % grid ranges one tile longer); a segment is a
+    sequence's tiles within one range."""
+    tiles = -(-ctx.astype(np.int64) // tile)
+    ts = np.concatenate([[0], np.cumsum(tiles)])
+    T = int(ts[-1])
+    q, r = divmod(T, grid)
+    starts = np.array([w * q + min(w, r) for w in range(grid + 1)], dtype=np.int64)
+    n = 0
+    for w in range(grid):
+        t0, t1 = starts[w], starts[w + 1]
+        if t1 > t0:
+            n += int(np.sum((np.minimum(t1, ts[1:]) > np.maximum(t0, ts[:-1]))))
+    return n
+
+
+def mla_bytes(w, grid: int = 256) -> dict:
     """HBM bytes of one MLA decode call. ``algorithmic``: the latent rows, block
     tables and lengths, weights and queries read once and the output written
     (what the roofline is measured on). ``call``: that plus the workspace
-    traffic of this design -- the absorbed query written and read back per
-    256-position piece and the pieces' partial outputs written and read once."""
+    traffic of this design on a ``grid``-workgroup split -- the absorbed query
+    (hi + lo) written once and read once per segment, the segments' partial
+    outputs written and read once, the tile plan written and read."""
     ctx = w["context_lens"].astype(np.int64)
     B, H, QK, R, DC, DV = (w["num_seqs"], w["num_heads"], w["qk_nope_dim"], w["rope_dim"],
                            w["kv_lora_rank"], w["v_dim"])
     row = DC + R
-    pieces = int(np.sum(-(-ctx // 256)))
+    segs = mla_segments(ctx, grid)
     latent = int(ctx.sum() * row * 2)
     tables = int(np.sum(-(-ctx // w["block_size"])) * 4 + 4 * B)
     weights = DC * H * (QK + DV) * 2
     q = B * H * (QK + R) * 2
     qt = B * H * row * 2 * 2
-    partial = pieces * H * (DC + 2) * 4
+    partial = segs * H * (DC + 2) * 4
+    plan = (B + 1) * 4
     out = B * H * DV * 2
-    split = latent + tables + pieces * H * row * 2 * 2 + partial
-    return {"latent": latent, "split": split,
+    split = latent + tables + segs * H * row * 2 * 2 + partial
+    return {"latent": latent, "split": split, "segments": segs,
             "algorithmic": latent + tables + weights + q + out,
-            "call": latent + tables + weights + q + 2 * qt + 2 * partial + out + pieces * H * row * 4}
+            "call": (latent + tables + weights + q + qt + segs * H * row * 2 * 2 + 2 * partial
+                     + 2 * plan + out)}
 
 
 def run_mla_decode(args, torch, pkv, workloads):
@@ -944,7 +965,7 @@ def run_mla_decode(args, torch, pkv, workloads):
     ta.stop()
     torch.cuda.synchronize()
     attn_ms = ta.mean_ms() / args.steps
-    nb = mla_bytes(w)
+    nb = mla_bytes(w, grid=min(256, torch.cuda.get_device_properties(0).multi_processor_count))
     value = nb["latent"] / (ms * 1e-3) / 1e9
     achieved = nb["algorithmic"] / (attn_ms * 1e-3) / 1e9
     ctx = w["context_lens"]

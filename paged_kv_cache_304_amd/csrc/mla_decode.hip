@@ -19,17 +19,22 @@
 //    matrix-core GEMM per head accumulated in fp32, then split into bf16
 //    hi + lo (x - hi rounded again), so that the products below keep ~16 more
 //    bits than a bf16 q~ would.
-//  * split: one workgroup per live (sequence, 256-position piece) -- found by
-//    a scan of the sequences' piece counts, so the grid holds no idle runs --,
-//    4 waves, tiles of 32 positions staged in LDS (three workgroups per CU).
-//    Scores S^T = C q~^T on v_mfma_f32_16x16x32_bf16 (hi and lo; each wave
-//    takes a quarter of the 576-dim contraction with its q~ operands held in
-//    registers, and the partial sums meet in LDS); online softmax in the log2
-//    domain; O += P C with P split into hi + lo as well and C's operand from
-//    LDS by transposing reads, each wave owning 128 of the 512 latent dims.
-//    Writes the unnormalised O, its running max and sum per head.
+//  * split: persistent, one workgroup per compute unit over an even share of
+//    the 32-position tiles of all sequences; 4 computing waves and 2 fetching
+//    waves that meet through LDS counters (no workgroup barrier per tile).
+//    The fetching waves move each item -- a segment's q~, then its latent
+//    tiles -- by LDS-DMA into a 4-deep ring. Scores S^T = C q~^T on
+//    v_mfma_f32_16x16x32_bf16 (hi and lo; each computing wave takes a quarter
+//    of the 576-dim contraction with its q~ operands held in registers, and
+//    the partial sums meet in LDS); online softmax in the log2 domain;
+//    O += P C with P split into hi + lo as well and C's operand from LDS by
+//    transposing reads, each wave owning 128 of the 512 latent dims. Writes
+//    the unnormalised O, its running max and sum per head for each
+//    (workgroup, sequence) segment.
 //  * merge: combines the pieces of a sequence and applies W_UV per head.
 #include <math.h>
+
+#include <type_traits>
 
 #include "pa_device.h"
 #include "pa_internal.h"
@@ -44,20 +49,28 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kDC = 512;        // latent (kv_lora_rank) dims
 constexpr int kHeads = 16;      // query heads (the MFMA's 16-wide operand)
 constexpr int kTile = 32;       // positions per tile
-constexpr int kSplit = 256;     // positions per workgroup piece
-constexpr int kWaves = 4;
-constexpr int kPad = 16;        // LDS row padding (bytes)
+constexpr int kWaves = 4;       // compute waves of a split workgroup
+constexpr int kProducers = 2;   // ... and its fetching waves (16 rows of an item each)
+constexpr int kRing = 4;        // LDS item buffers: one being computed, three in flight
+constexpr int kTabSlots = 8;    // LDS slots of fetched block-table entries
+constexpr int kAhead = 3;       // items a fetching wave keeps in flight
+constexpr uint32_t kSpinLimit = 1u << 20;  // polls before a wait gives up (never, when the counts are right)
 
 template <int DR>
 struct MlaGeo {
   static constexpr int ROW = kDC + DR;           // values per cached row
   static constexpr int RB = ROW * 2;             // bytes per cached row
-  static constexpr int RS = RB + kPad;           // LDS row stride
-  static constexpr int KSTEPS = ROW / 32;        // MFMA steps over the row
-  static constexpr int HALF = KSTEPS / 2;        // steps per wave pair
-  static constexpr int LOADS = RB / 128;          // 16-byte loads per thread and tile:
-                                                  // 8 threads per row, 32 rows
-  static_assert(RB % 128 == 0 && kTile * 8 == 64 * kWaves, "row-per-8-threads tile loads");
+  static constexpr int CH = RB / 16;             // 16-byte chunks per row (64 or 72)
+  static constexpr int TILE = kTile * RB;        // bytes per LDS tile (rows back to back)
+  static constexpr int LOADS = TILE / 1024;      // 1 KB LDS-DMA wave loads per tile
+  static constexpr int LPP = LOADS / kProducers; // ... per fetching wave: 16 rows
+  static constexpr int KSTEPS = ROW / 32;        // 16x16x32 MFMA steps over the row
+  static_assert(CH % 8 == 0 && TILE % 1024 == 0 && LPP * 1024 == 16 * RB, "tile geometry");
+  // Chunk swizzle: physical chunk of logical chunk lc in row r is lc ^ sw(r),
+  // so that 16 consecutive rows read at one logical chunk hit 16 different
+  // 16-byte bank groups (a row start advances 8 groups when CH % 16 == 8).
+  __device__ static int sw(int r) { return CH % 16 == 0 ? (r & 15) : ((r >> 1) & 7); }
+  __device__ static int phys(int r, int lc) { return lc ^ sw(r); }
 };
 
 struct MlaArgs {
@@ -71,12 +84,14 @@ struct MlaArgs {
   const int32_t* ctx_lens;
   uint16_t* q_hi;   // [B, 16, ROW]
   uint16_t* q_lo;
-  float* ws_m;      // [B, S, 16]
+  int32_t* ts;      // [B + 1] first global tile of each sequence; ts[B] = all tiles
+  float* ws_m;      // [G + B, 16] per (workgroup, sequence) partial
   float* ws_l;
-  float* ws_o;      // [B, S, 16, 512]
+  float* ws_o;      // [G + B, 16, 512]
   int64_t out_seq_stride, qn_seq_stride, qr_seq_stride;
   int64_t block_stride, num_blocks;
-  int32_t block_size, W, num_seqs, qk, dr, dv, splits;
+  int32_t block_size, W, num_seqs, qk, dr, dv, grid;
+  int32_t bs_log2;  // log2(block_size) when a power of two, else -1
   int32_t out_f32;
   float scale_log2;
 };
@@ -93,6 +108,43 @@ __device__ __forceinline__ void split_hi_lo(float x, uint16_t& hi, uint16_t& lo)
   lo = (uint16_t)f32_to_bf16(x - __uint_as_float((uint32_t)hi << 16));
 }
 
+// The tiles of all sequences in sequence order form one list of T tiles;
+// workgroup w of G serves tiles range_start(w) .. range_start(w + 1) - 1 (an
+// even split), tile t belongs to workgroup tile_owner(t).
+__device__ __forceinline__ int range_start(int w, int T, int G) {
+  const int q = T / G, r = T % G;
+  return w * q + min(w, r);
+}
+__device__ __forceinline__ int tile_owner(int t, int T, int G) {
+  const int q = T / G, r = T % G, big = r * (q + 1);
+  return t < big ? t / (q + 1) : r + (t - big) / q;
+}
+__device__ __forceinline__ int tiles_of(const MlaArgs& a, int b) { return (clamp_ctx(a, b) + kTile - 1) / kTile; }
+
+// ts[b] = tiles of sequences 0 .. b - 1 (ts[B] = T), by one workgroup of 256.
+__device__ void plan_tiles(const MlaArgs& a) {
+  __shared__ int part[256];
+  const int tid = threadIdx.x, B = a.num_seqs;
+  const int per = (B + 255) / 256;
+  const int lo = min(B, tid * per), hi = min(B, lo + per);
+  int mine = 0;
+  for (int b = lo; b < hi; ++b) mine += tiles_of(a, b);
+  part[tid] = mine;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {  // inclusive prefix over the threads
+    const int v = tid >= o ? part[tid - o] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int run = part[tid] - mine;
+  for (int b = lo; b < hi; ++b) {
+    a.ts[b] = run;
+    run += tiles_of(a, b);
+  }
+  if (tid == 255) a.ts[B] = part[255];
+}
+
 // ---------------------------------------------------------------- absorb
 // q~^T [512 c x B] = W_UK,h [512 x qk] q_h^T [qk x B] per head on the matrix
 // cores (bf16 x bf16 products are exact in fp32, sums in fp32). grid (16
@@ -100,6 +152,7 @@ __device__ __forceinline__ void split_hi_lo(float x, uint16_t& hi, uint16_t& lo)
 // dims 64 cb + 16 w .. +15 for 16 sequences. The A operand is 16 bytes of a
 // W_UK row (dims 8 (l/16) .. of row l%16), the B operand 16 bytes of a q row.
 __global__ __launch_bounds__(256) void mla_absorb_kernel(MlaArgs a, int row) {
+  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) plan_tiles(a);  // uniform per workgroup
   const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
   const int c0 = 64 * blockIdx.y + 16 * wave, b0 = 16 * blockIdx.z;
@@ -159,175 +212,405 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(MlaArgs a, int row) {
 }
 
 // ---------------------------------------------------------------- split
-// A workgroup barrier for LDS traffic only: the next tile's global loads stay
-// in flight across it (a full __syncthreads would wait for them too).
+// A workgroup barrier for LDS traffic only: loads in flight stay in flight
+// across it (a full __syncthreads would wait for them too).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 __device__ __forceinline__ float bcast_lane(float x, int src) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(x)));
 }
 
-__device__ __forceinline__ int pieces_of(const MlaArgs& a, int b) { return (clamp_ctx(a, b) + kSplit - 1) / kSplit; }
+// max over the four lanes l % 16 + 16 j: each permlane swap exchanges one half
+// of a copy of x with the other half of a second copy, so the two results hold,
+// lane by lane, x at l and at its partner lane (l ^ 32, then l ^ 16).
+__device__ __forceinline__ float max_over_groups(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t v = __float_as_uint(m);
+  const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
 
-// Workgroup L serves the L-th live piece in (sequence, piece) order: wave 0
-// scans the sequences' piece counts (each lane a run of sequences) and finds
-// it. Returns false when L is past the last piece.
-__device__ bool find_piece(const MlaArgs& a, int L, int lane, int& b_out, int& s_out) {
-  const int per = (a.num_seqs + 63) / 64;
-  const int lo = min(a.num_seqs, lane * per), hi = min(a.num_seqs, lo + per);
-  int mine = 0;
-  for (int b = lo; b < hi; ++b) mine += pieces_of(a, b);
-  int incl = mine;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, (unsigned)o, 64);
-    if (lane >= o) incl += y;
+// block and offset of a position (a shift when the block size is a power of two)
+__device__ __forceinline__ void block_of(const MlaArgs& a, int pos, int& blk, int& off) {
+  if (a.bs_log2 >= 0) {
+    blk = pos >> a.bs_log2;
+    off = pos & (a.block_size - 1);
+  } else {
+    blk = pos / a.block_size;
+    off = pos - blk * a.block_size;
   }
-  const uint64_t past = __builtin_amdgcn_ballot_w64(incl <= L);  // lanes wholly before L
-  const int owner = __builtin_popcountll(past);
-  if (owner >= 64) return false;
-  int found_b = -1, found_s = 0;
-  if (lane == owner) {
-    int run = incl - mine;
-    for (int b = lo; b < hi; ++b) {
-      const int n = pieces_of(a, b);
-      if (L < run + n) {
-        found_b = b;
-        found_s = L - run;
-        break;
-      }
-      run += n;
+}
+
+constexpr float kLazyMax = 8.0f;  // log2 headroom of a segment's running max
+
+// Persistent: one workgroup per compute unit, each over an even share of the
+// T tiles of all sequences (sequence order). Its share falls into segments,
+// one per sequence it touches; a segment is processed as an item stream --
+// the sequence's q~ (hi and lo, 32 rows of the row length: exactly one tile's
+// bytes), then its tiles -- and ends with a partial (running max, sum and
+// unnormalised O of the 16 heads) at slot w + b of the workspace (w + b is
+// unique: a later workgroup never serves an earlier sequence).
+//
+// Roles: waves 0..3 compute (each a quarter of the score contraction and 128
+// latent dims of O), waves 4 and 5 fetch. Every item goes global -> LDS by
+// LDS-DMA into a ring of kRing buffers; fetching wave p moves rows 16 p ..
+// 16 p + 15 of each item and, kAhead + 1 items ahead, the block-table entries
+// of those rows (4 bytes a lane), so that no load the compiler sees sits in its
+// loop (vector-memory counters complete in order; waiting for such a load
+// would wait for the items in flight too). The two roles meet through LDS
+// counters instead of workgroup barriers, so that a fetching wave whose DMA
+// issue stalls on a full memory pipeline never holds a computing wave, nor
+// the other way round:
+//  * ready[p]: items whose share from fetching wave p has landed (raised
+//    after its own vmcnt wait); a computing wave starts item i when both are
+//    past i;
+//  * consumed: +1 per computing wave and finished item; a fetching wave
+//    refills item i's buffer (with item i + kRing) only when it reaches
+//    kWaves (i + 1);
+//  * sx_in / sx_out: the computing waves' exchange of partial scores (written,
+//    then read by all four) for the k-th tile.
+// Every wait polls with a bound: counts that never arrive end the kernel (with
+// wrong results) instead of hanging the device.
+__device__ __forceinline__ uint32_t lds_load_u32(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void lds_add_u32(uint32_t* p, uint32_t v) {
+  __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void lds_store_u32(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+// Polls until *p >= target (uniform); false after kSpinLimit polls.
+__device__ __forceinline__ bool wait_at_least(const uint32_t* p, uint32_t target) {
+  for (uint32_t n = 0; n < kSpinLimit; ++n) {
+    if (__builtin_amdgcn_readfirstlane(lds_load_u32(p)) >= target) {
+      compiler_fence();
+      return true;
     }
+    __builtin_amdgcn_s_sleep(1);
   }
-  b_out = __shfl(found_b, owner, 64);
-  s_out = __shfl(found_s, owner, 64);
-  return b_out >= 0;
+  return false;
 }
 
 template <int DR>
-__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3, 3))) void mla_split_kernel(MlaArgs a) {
+__global__ __launch_bounds__(64 * (kWaves + kProducers)) void mla_split_kernel(MlaArgs a) {
   using Gm = MlaGeo<DR>;
-  constexpr int ROW = Gm::ROW, RS = Gm::RS, LOADS = Gm::LOADS;
-  constexpr int KSTEPS = ROW / 32, QMAX = (KSTEPS + kWaves - 1) / kWaves;
+  constexpr int ROW = Gm::ROW, RB = Gm::RB, LPP = Gm::LPP;
+  constexpr int KSTEPS = Gm::KSTEPS, QMAX = (KSTEPS + kWaves - 1) / kWaves;
   const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, lg = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = (int)gridDim.x, w = (int)blockIdx.x, B = a.num_seqs;
 
-  __shared__ __attribute__((aligned(16))) char tile_lds[kTile * RS];
+  __shared__ __attribute__((aligned(16))) char ring[kRing][Gm::TILE];
   __shared__ f32x4 sx[kWaves][2][64];
-  __shared__ int64_t rowoff[kSplit];  // byte offset of each position's row; -1: none
-  __shared__ int which[2];
-
-  if (wave == 0) {
-    int b, s;
-    const bool ok = find_piece(a, (int)blockIdx.x, lane, b, s);
-    if (lane == 0) {
-      which[0] = ok ? b : -1;
-      which[1] = s;
-    }
+  __shared__ __attribute__((aligned(16))) int32_t tab[kProducers][kTabSlots][64];
+  __shared__ int desc[kRing][4];  // item: local tile (-1 q~, -2 none), sequence, last tile of its segment
+  __shared__ uint32_t rowmask[kRing][kProducers];
+  __shared__ uint32_t ready[kProducers], consumed, sx_in, sx_out;
+  if (tid == 0) {
+    for (int p2 = 0; p2 < kProducers; ++p2) ready[p2] = 0u;
+    consumed = sx_in = sx_out = 0u;
   }
-  __syncthreads();
-  const int b = which[0], sp = which[1];
-  if (b < 0) return;  // uniform: past the last live piece
-  const int ctx = clamp_ctx(a, b);
-  const int p0 = sp * kSplit;
-  const int p1 = min(ctx, p0 + kSplit);
-  const int ntiles = (p1 - p0 + kTile - 1) / kTile;
-  const int64_t piece = (int64_t)b * a.splits + sp;
-  if (a.num_blocks == 0) {  // uniform: an empty pool -- no position takes part
-    if (tid < kHeads) {
-      a.ws_m[piece * kHeads + tid] = -INFINITY;
-      a.ws_l[piece * kHeads + tid] = 0.0f;
+  __syncthreads();  // the counters start at zero (before any load is in flight)
+
+  const int T = uniform(a.ts[B]);
+  const int t0 = range_start(w, T, G), t1 = range_start(w + 1, T, G);
+  if (t0 >= t1) return;  // uniform: no tiles for this workgroup
+
+  if (wave >= kWaves) {
+    // ================================================================ fetch
+    const int pw = wave - kWaves;
+    // ---- segments: lane j of sg_* holds the j-th segment of the current list
+    // (up to 64 sequences at a time): sequence, first local tile, tiles, length.
+    int b_first;
+    {  // the last sequence whose first tile is <= t0 (it holds tile t0)
+      int lo = 0, hi = B;
+      while (hi - lo > 1) {
+        const int step = (hi - lo + 63) / 64;
+        const int idx = lo + lane * step;
+        const int v = idx < hi ? a.ts[idx] : INT32_MAX;
+        const uint64_t le = __builtin_amdgcn_ballot_w64(v <= t0);  // a prefix of the lanes, lane 0 included
+        const int j = 63 - __builtin_clzll(le);
+        lo = lo + j * step;
+        hi = min(hi, lo + step);
+      }
+      b_first = uniform(lo);
     }
+    int sg_b = 0, sg_lt0 = 0, sg_nt = 0, sg_ctx = 0, nseg = 0, b_next = b_first;
+    bool more = true;
+    auto fill = [&]() {  // the next 64 sequences from b_next, compacted to the live ones
+      const int b = b_next + lane;
+      bool live = false;
+      int lt0 = 0, nt = 0, cx = 0;
+      if (b < B) {
+        const int tsb = a.ts[b], tse = a.ts[b + 1];
+        const int lo_t = max(t0, tsb), hi_t = min(t1, tse);
+        live = hi_t > lo_t;
+        lt0 = lo_t - tsb;
+        nt = hi_t - lo_t;
+        cx = clamp_ctx(a, b);
+      }
+      const uint64_t m = __builtin_amdgcn_ballot_w64(live);
+      const int below = __builtin_popcountll(m & ((1ull << lane) - 1ull));
+      const int cnt = __builtin_popcountll(m);
+      const int dst = 4 * (live ? below : cnt + (lane - below));  // a permutation: live lanes first
+      sg_b = __builtin_amdgcn_ds_permute(dst, b);
+      sg_lt0 = __builtin_amdgcn_ds_permute(dst, lt0);
+      sg_nt = __builtin_amdgcn_ds_permute(dst, nt);
+      sg_ctx = __builtin_amdgcn_ds_permute(dst, cx);
+      nseg = cnt;
+      const int nb = b_next + 64;
+      more = nb < B && uniform(a.ts[nb < B ? nb : B]) < t1;  // tiles of later sequences remain
+      b_next = nb;
+    };
+    int cur_k = 0, cur_idx = 0;  // item cursor: segment, item within it (0: q~)
+    fill();
+    // descriptor of the next item: lt (-1: q~, -2: none, else local tile),
+    // sequence, length, last tile of its segment
+    auto next_item = [&](int& lt, int& bb, int& cx, int& last) {
+      while (cur_k >= nseg && more) {  // uniform; a refill waits for every load in flight (rare)
+        fill();
+        cur_k = 0;
+      }
+      if (cur_k >= nseg) {
+        lt = -2;
+        bb = 0;
+        cx = 0;
+        last = 0;
+        return;
+      }
+      const int sb = __builtin_amdgcn_readlane(sg_b, cur_k), s0 = __builtin_amdgcn_readlane(sg_lt0, cur_k);
+      const int sn = __builtin_amdgcn_readlane(sg_nt, cur_k), sc = __builtin_amdgcn_readlane(sg_ctx, cur_k);
+      bb = sb;
+      cx = sc;
+      lt = cur_idx == 0 ? -1 : s0 + cur_idx - 1;
+      last = cur_idx == sn ? 1 : 0;
+      if (++cur_idx > sn) {
+        cur_idx = 0;
+        ++cur_k;
+      }
+    };
+
+    if (a.num_blocks == 0) {  // an empty pool -- every position is masked (the computing waves left)
+      if (pw == 0) {
+        for (;;) {
+          if (lane < nseg) {
+#pragma unroll
+            for (int h = 0; h < kHeads; ++h) {
+              a.ws_m[(int64_t)(w + sg_b) * kHeads + h] = -INFINITY;
+              a.ws_l[(int64_t)(w + sg_b) * kHeads + h] = 0.0f;
+            }
+          }
+          if (!more) break;
+          fill();
+        }
+      }
+      return;
+    }
+
+    const char* cache = static_cast<const char*>(a.cache);
+    // entries of rows 16 pw + lane % 16 of a tile item (a fixed valid entry otherwise)
+    auto fetch_tab = [&](int slot, int lt, int bb) {
+      const int32_t* src = a.bt;
+      if (lt >= 0) {
+        int blk, o;
+        block_of(a, kTile * lt + 16 * pw + (lane & 15), blk, o);
+        src = a.bt + (int64_t)bb * a.W + min(blk, a.W - 1);
+      }
+      dma_4B(src, lds_addr(&tab[pw][slot][0]));
+    };
+    // This wave's LPP loads of an item fill buffer bytes 1024 (pw LPP + k) ..
+    // +1023: exactly rows 16 pw .. 16 pw + 15, a load spanning at most two
+    // rows. Lane l's 16 bytes of load k are physical chunk pc of one of them,
+    // so it fetches logical chunk phys(row, pc) of that row. Lanes r < 16 find
+    // row 16 pw + r's source (an offset from base in 16-byte units; a masked
+    // position reads the base's first row instead, its values masked) and the
+    // rows that take part (bit r for row 16 pw + r); the sixteen offsets reach
+    // every lane through readlane.
+    const int64_t qlo_delta16 = ((const char*)a.q_lo - (const char*)a.q_hi) / 16;
+    struct RowSrc {
+      const char* base;
+      uint32_t roff[16];
+      uint32_t rows;
+    };
+    auto find_rows = [&](int tslot, int lt, int bb, int cx, RowSrc& rs) {
+      const int r = lane & 15;
+      int64_t off16;
+      bool ok;
+      if (lt == -1) {  // q~: rows 0..15 the hi parts of heads 0..15, rows 16..31 the lo parts
+        rs.base = reinterpret_cast<const char*>(a.q_hi);
+        off16 = (pw == 0 ? 0 : qlo_delta16) + ((int64_t)bb * kHeads + r) * (RB / 16);
+        ok = true;
+      } else {
+        rs.base = cache;
+        const int e = tab[pw][tslot][lane];
+        const int pos = kTile * lt + 16 * pw + r;
+        int blk, o;
+        block_of(a, pos, blk, o);
+        (void)blk;
+        ok = pos < cx && e >= 0 && (int64_t)e < a.num_blocks;
+        off16 = ok ? ((int64_t)e * a.block_stride + (int64_t)o * ROW) / 8 : 0;  // bf16 elements / 8
+      }
+      rs.rows = (uint32_t)__builtin_amdgcn_ballot_w64(ok) & 0xFFFFu;
+#pragma unroll
+      for (int j2 = 0; j2 < 16; ++j2) rs.roff[j2] = __builtin_amdgcn_readlane((uint32_t)off16, j2);
+    };
+    // loads k0 .. k1 - 1 of this wave's share of an item into ring slot rslot
+    auto issue = [&](int rslot, const RowSrc& rs, auto k0c, auto k1c) {
+      constexpr int k0 = decltype(k0c)::value, k1 = decltype(k1c)::value;
+      char* dst = ring[rslot] + 1024 * (pw * LPP);
+#pragma unroll
+      for (int k = k0; k < k1; ++k) {
+        const int ra = (1024 * k) / RB;                     // first of the load's rows (wave-local)
+        const int split = (RB * (ra + 1) - 1024 * k) / 16;  // lanes below it are in row ra
+        const bool second = lane >= split;
+        const int rl = second ? ra + 1 : ra;
+        const int pc = (1024 * k + 16 * lane - RB * rl) / 16;
+        const int lc = Gm::phys(16 * pw + rl, pc);
+        const uint32_t ro = second ? rs.roff[ra + 1 < 16 ? ra + 1 : 15] : rs.roff[ra];
+        dma_16B(rs.base + 16 * ((uint64_t)ro + lc), lds_addr(dst + 1024 * k));
+      }
+    };
+    using KZero = std::integral_constant<int, 0>;
+    using KAll = std::integral_constant<int, LPP>;
+    auto post = [&](int slot, int lt, int bb, int last, uint32_t rows) {  // to the computing waves
+      if (lane == 0) {
+        rowmask[slot][pw] = rows << (16 * pw);
+        if (pw == 0) {
+          desc[slot][0] = lt;
+          desc[slot][1] = bb;
+          desc[slot][2] = last;
+        }
+      }
+    };
+
+    // descriptors of items j .. j + kAhead + 1
+    constexpr int ND = kAhead + 2;
+    int dl[ND], db[ND], dc[ND], dz[ND];
+#pragma unroll
+    for (int s2 = 0; s2 < ND; ++s2) next_item(dl[s2], db[s2], dc[s2], dz[s2]);
+    // entries of items 0 .. kAhead
+#pragma unroll
+    for (int s2 = 0; s2 <= kAhead; ++s2) fetch_tab(s2, dl[s2], db[s2]);
+    wait_vmem<0>();
+    bool ok_run = true;
+    for (int j = 0; ok_run; ++j) {
+      // Step j: item j goes into buffer j % kRing once item j - kRing is done
+      // with; item j - kAhead is published once this wave's share of it has
+      // landed -- this wave's later operations, the entries and data of items
+      // j - kAhead + 1 .. j - 1 (entries run kAhead + 1 items ahead of data),
+      // are then all that may be in flight.
+      if (j >= kRing) ok_run = wait_at_least(&consumed, (uint32_t)(kWaves * (j - kRing + 1)));
+      if (!ok_run) break;
+      if (j >= kAhead) {
+        static_assert(kAhead == 3, "the wait below counts two steps of (LPP + 1) operations");
+        wait_vmem<2 * (LPP + 1)>();
+        compiler_fence();
+        if (lane == 0) lds_store_u32(&ready[pw], (uint32_t)(j - kAhead + 1));
+      }
+      if (dl[0] == -2) {  // item j is past the last one: the end marker in its buffer's slot
+        if (pw == 0 && lane == 0) desc[j % kRing][0] = -2;
+        break;
+      }
+      RowSrc rs;
+      find_rows(j % kTabSlots, dl[0], db[0], dc[0], rs);  // its entries arrived with item j - kAhead - 1
+      fetch_tab((j + kAhead + 1) % kTabSlots, dl[ND - 1], db[ND - 1]);
+      issue(j % kRing, rs, KZero{}, KAll{});
+      post(j % kRing, dl[0], db[0], dz[0], rs.rows);
+#pragma unroll
+      for (int s2 = 0; s2 < ND - 1; ++s2) {
+        dl[s2] = dl[s2 + 1];
+        db[s2] = db[s2 + 1];
+        dc[s2] = dc[s2 + 1];
+        dz[s2] = dz[s2 + 1];
+      }
+      next_item(dl[ND - 1], db[ND - 1], dc[ND - 1], dz[ND - 1]);
+    }
+    // everything issued has landed: publish the rest and the end marker
+    wait_vmem<0>();
+    compiler_fence();
+    if (lane == 0) lds_store_u32(&ready[pw], 0x7FFFFFFFu);
     return;
   }
 
-  // where each position's row lives (the only division by block_size)
-  const int bs = a.block_size;
-  for (int i = tid; i < kSplit; i += 64 * kWaves) {
-    const int pos = p0 + i;
-    int64_t off = -1;
-    if (pos < p1) {
-      const int e = a.bt[(int64_t)b * a.W + pos / bs];
-      if (e >= 0 && (int64_t)e < a.num_blocks) off = ((int64_t)e * a.block_stride + (int64_t)(pos % bs) * ROW) * 2;
-    }
-    rowoff[i] = off;
-  }
-
+  // ================================================================ compute
+  if (a.num_blocks == 0) return;  // uniform: the fetching waves write the partials
   // This wave's share of the score contraction: steps s0 .. s0 + nst - 1 of
-  // KSTEPS (32 dims each); its q~ operands (head li, dims 32 s + 8 lg ..) stay
-  // in registers for the whole piece.
+  // KSTEPS (32 dims each); its q~ operands (head li, dims 32 s + 8 lg ..) are
+  // read from a q~ item into registers for the segment.
   const int base_n = KSTEPS / kWaves, rem = KSTEPS % kWaves;
   const int nst = base_n + (wave < rem ? 1 : 0);
   const int s0 = wave * base_n + min(wave, rem);
   bf16x8 qh[QMAX], ql[QMAX];
-  {
-    const uint16_t* qhb = a.q_hi + ((int64_t)b * kHeads + li) * ROW;
-    const uint16_t* qlb = a.q_lo + ((int64_t)b * kHeads + li) * ROW;
 #pragma unroll
-    for (int i = 0; i < QMAX; ++i) {
-      const int k0 = 32 * (s0 + (i < nst ? i : 0)) + 8 * lg;
-      qh[i] = *reinterpret_cast<const bf16x8*>(qhb + k0);
-      ql[i] = *reinterpret_cast<const bf16x8*>(qlb + k0);
-    }
-  }
-  __syncthreads();
-
-  // Tile loads: thread t loads row t / 8 of the tile, 16 bytes at columns
-  // 16 (t % 8) + 128 i -- one row offset per thread and tile, immediate
-  // offsets after it. Every thread loads (a row past the piece or with a bad
-  // table entry reads the pool's first row instead) and such rows are zeroed
-  // when stored to LDS: a load under a divergent branch would make the
-  // compiler wait for it before the other branch writes the register. Their
-  // scores are -inf, and 0 * 0 keeps P V finite.
-  const char* cache = static_cast<const char*>(a.cache) + 16 * (tid & 7);
-  const int lrow = tid >> 3;
-  char* const lds_dst = tile_lds + lrow * RS + 16 * (tid & 7);
-  u32x4 pre[LOADS];
-  bool row_ok = false;
-  auto load_tile = [&](int t) {
-    const int64_t ro = rowoff[kTile * t + lrow];
-    row_ok = ro >= 0;
-    const char* src = cache + (row_ok ? ro : 0);
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) pre[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + 128 * i));
-  };
-  auto store_tile = [&]() {
-    const u32x4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) *reinterpret_cast<u32x4*>(lds_dst + 128 * i) = row_ok ? pre[i] : z;
-  };
+  for (int i = 0; i < QMAX; ++i) qh[i] = ql[i] = bf16x8{};
 
   const int dim0 = 128 * wave;  // this wave's 128 latent dims of O
   float m_run = -INFINITY, l_run = 0.0f;
   f32x4 acc[8];
 #pragma unroll
   for (int cb = 0; cb < 8; ++cb) acc[cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  uint32_t ntile = 0;  // tiles this workgroup has computed (the score exchange count)
 
-  load_tile(0);
-  for (int t = 0; t < ntiles; ++t) {
-    lds_barrier();  // every wave is done reading the previous tile
-    store_tile();
-    lds_barrier();
-    if (t + 1 < ntiles) load_tile(t + 1);
-
-    // partial S^T of both 16-position blocks over this wave's contraction
-    // steps: rows = positions 16 pb + 4 lg + r, column = head li
-    f32x4 spb[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+  for (int i = 0;; ++i) {
+    bool ok = true;
 #pragma unroll
-    for (int i = 0; i < QMAX; ++i) {
-      if (i < nst) {
-        const int k0 = 32 * (s0 + i) + 8 * lg;
+    for (int p2 = 0; p2 < kProducers; ++p2) ok = ok && wait_at_least(&ready[p2], (uint32_t)(i + 1));
+    if (!ok) break;
+    const int slot = i % kRing;
+    const int lt = uniform(desc[slot][0]);
+    if (lt == -2) break;
+    const int bb = uniform(desc[slot][1]);
+    const int last = uniform(desc[slot][2]);
+    const char* tile = ring[slot];
+
+    if (lt == -1) {  // q~ of a new segment
+#pragma unroll
+      for (int q = 0; q < QMAX; ++q) {
+        if (q < nst) {
+          const int lc = 4 * (s0 + q) + lg;
+          qh[q] = *reinterpret_cast<const bf16x8*>(tile + li * RB + 16 * Gm::phys(li, lc));
+          ql[q] = *reinterpret_cast<const bf16x8*>(tile + (16 + li) * RB + 16 * Gm::phys(16 + li, lc));
+        }
+      }
+      m_run = -INFINITY;
+      l_run = 0.0f;
+#pragma unroll
+      for (int cb = 0; cb < 8; ++cb) acc[cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // its reads are done: the buffer may be refilled
+      if (lane == 0) lds_add_u32(&consumed, 1u);
+      continue;
+    }
+    const uint32_t valid = uniform(rowmask[slot][0]) | uniform(rowmask[slot][1]);  // bit r: position r takes part
+    // partial S^T of both 16-position blocks over this wave's contraction
+    // steps: rows = positions 16 pb + 4 lg + r, column = head li (hi and lo
+    // products in separate accumulators: four independent chains)
+    f32x4 sph[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+    f32x4 spl[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+    for (int q = 0; q < QMAX; ++q) {
+      if (q < nst) {
+        const int lc = 4 * (s0 + q) + lg;  // logical chunk of dims 32 s + 8 lg ..
 #pragma unroll
         for (int pb = 0; pb < 2; ++pb) {
-          const bf16x8 cop = *reinterpret_cast<const bf16x8*>(tile_lds + (16 * pb + li) * RS + 2 * k0);
-          spb[pb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cop, qh[i], spb[pb], 0, 0, 0);
-          spb[pb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cop, ql[i], spb[pb], 0, 0, 0);
+          const int r = 16 * pb + li;
+          const bf16x8 cop = *reinterpret_cast<const bf16x8*>(tile + r * RB + 16 * Gm::phys(r, lc));
+          sph[pb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cop, qh[q], sph[pb], 0, 0, 0);
+          spl[pb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cop, ql[q], spl[pb], 0, 0, 0);
         }
       }
     }
-    sx[wave][0][lane] = spb[0];
-    sx[wave][1][lane] = spb[1];
-    lds_barrier();
+    // exchange: every wave is done reading the previous tile's partials, write
+    // this one's, then wait for all four
+    if (ntile > 0 && !wait_at_least(&sx_out, kWaves * ntile)) break;
+    sx[wave][0][lane] = sph[0] + spl[0];
+    sx[wave][1][lane] = sph[1] + spl[1];
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (lane == 0) lds_add_u32(&sx_in, 1u);
+    if (!wait_at_least(&sx_in, kWaves * (ntile + 1))) break;
     // full scores of head li at positions 4 lg + r (block 0) and 16 + 4 lg + r
     // (block 1), summed over the waves in one fixed order
     float sc[8];
@@ -335,23 +618,29 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3, 
     for (int pb = 0; pb < 2; ++pb) {
       f32x4 s4 = sx[0][pb][lane];
 #pragma unroll
-      for (int w = 1; w < kWaves; ++w) s4 += sx[w][pb][lane];
+      for (int v = 1; v < kWaves; ++v) s4 += sx[v][pb][lane];
 #pragma unroll
       for (int r = 0; r < 4; ++r) sc[4 * pb + r] = s4[r];
     }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (lane == 0) lds_add_u32(&sx_out, 1u);
+    ++ntile;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const bool ok = rowoff[kTile * t + 16 * (k >> 2) + 4 * lg + (k & 3)] >= 0;  // -1 past p1 too
-      sc[k] = ok ? sc[k] : -INFINITY;
+      const bool okp = (valid >> (16 * (k >> 2) + 4 * lg + (k & 3))) & 1u;
+      sc[k] = okp ? sc[k] : -INFINITY;
     }
     float mx = sc[0];
 #pragma unroll
     for (int k = 1; k < 8; ++k) mx = fmaxf(mx, sc[k]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mn = fmaxf(m_run, mx);
+    mx = max_over_groups(mx);
+    // The running max is raised only when the tile's max passes it by more
+    // than kLazyMax (first tile: any finite max): probabilities 2^(s - m)
+    // then stay below 2^kLazyMax and the rescale of O is rare.
+    const bool raise = mx > m_run + kLazyMax;
+    const float mn = raise ? mx : m_run;
     const float mu = (mn == -INFINITY) ? 0.0f : mn;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - mu);
+    const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - mu) : 1.0f;
     float pr[8];
     float ps = 0.0f;
 #pragma unroll
@@ -362,7 +651,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3, 
     l_run = l_run * alpha + ps;
     m_run = mn;
     // rescale O rows (heads 4 lg + r) by their heads' alpha
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
       float al[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) al[r] = bcast_lane(alpha, 4 * lg + r);
@@ -371,8 +660,8 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3, 
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[cb][r] *= al[r];
     }
-    // P as the A operand (row = head li, contraction = this lane's 8 positions)
-    // in hi + lo halves
+    // P as the A operand (row = head li, contraction = this lane's 8
+    // positions) in hi + lo halves
     uint32_t phw[4], plw[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -381,61 +670,87 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3, 
     }
     const bf16x8 ph = __builtin_bit_cast(bf16x8, u32x4{phw[0], phw[1], phw[2], phw[3]});
     const bf16x8 pl = __builtin_bit_cast(bf16x8, u32x4{plw[0], plw[1], plw[2], plw[3]});
+    // C rows of masked positions -> 0 in the operand (their slots may hold
+    // NaN; their probabilities are 0): element e is row 4 lg + e (e < 4) or
+    // 16 + 4 lg + e - 4
+    u32x4 vmask = {~0u, ~0u, ~0u, ~0u};
+    if (valid != 0xFFFFFFFFu) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e0 = 2 * q, e1 = 2 * q + 1;
+        const int r0 = (e0 < 4 ? 0 : 16) + 4 * lg + (e0 & 3), r1 = (e1 < 4 ? 0 : 16) + 4 * lg + (e1 & 3);
+        vmask[q] = (((valid >> r0) & 1u) ? 0xFFFFu : 0u) | (((valid >> r1) & 1u) ? 0xFFFF0000u : 0u);
+      }
+    }
     // O += P C over this wave's dims: transposing reads give lane (m, g)
     // C[4g + j][d0 + m] (low half) and C[16 + 4g + j][d0 + m] (high half)
     const int trow = 4 * lg + (li >> 2);
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb) {
-      const int col = 2 * (dim0 + 16 * cb + 4 * (li & 3));
+      const int col = 2 * (dim0 + 16 * cb + 4 * (li & 3));  // byte column of the 8-byte read
+      const int lc = col >> 4, within = col & 15;
       const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4*)(tile_lds + trow * RS + col));
-      const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4*)(tile_lds + (trow + 16) * RS + col));
-      const bf16x8 vop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+          (__attribute__((address_space(3))) i16x4*)(tile + trow * RB + 16 * Gm::phys(trow, lc) + within));
+      const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(
+          tile + (trow + 16) * RB + 16 * Gm::phys(trow + 16, lc) + within));
+      u32x4 wv = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+      wv &= vmask;
+      const bf16x8 vop = __builtin_bit_cast(bf16x8, wv);
       acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vop, acc[cb], 0, 0, 0);
       acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vop, acc[cb], 0, 0, 0);
     }
-  }
-
-  // the four lane groups saw different positions under one running max
-  l_run += __shfl_xor(l_run, 16, 64);
-  l_run += __shfl_xor(l_run, 32, 64);
-  if (wave == 0 && lane < kHeads) {
-    a.ws_m[piece * kHeads + lane] = m_run;
-    a.ws_l[piece * kHeads + lane] = l_run;
-  }
-  float* o = a.ws_o + piece * kHeads * kDC;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the tile's reads are done: its buffer may be refilled
+    if (lane == 0) lds_add_u32(&consumed, 1u);
+    if (last) {  // the segment's last tile: its partial
+      // the four lane groups saw different positions under one running max
+      float lsum = l_run + __shfl_xor(l_run, 16, 64);
+      lsum += __shfl_xor(lsum, 32, 64);
+      const int64_t pslot = (int64_t)w + bb;
+      if (wave == 0 && lane < kHeads) {
+        a.ws_m[pslot * kHeads + lane] = m_run;
+        a.ws_l[pslot * kHeads + lane] = lsum;
+      }
+      float* o = a.ws_o + pslot * kHeads * kDC;
 #pragma unroll
-  for (int cb = 0; cb < 8; ++cb)
+      for (int cb = 0; cb < 8; ++cb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) o[(4 * lg + r) * kDC + dim0 + 16 * cb + li] = acc[cb][r];
+        for (int r = 0; r < 4; ++r) o[(4 * lg + r) * kDC + dim0 + 16 * cb + li] = acc[cb][r];
+    }
+  }
 }
 
 // ---------------------------------------------------------------- merge
-// grid (16 heads, ceil(B / 4)): the pieces of each of 4 sequences combined
+// grid (16 heads, ceil(B / 4)): the partials of each of 4 sequences combined
 // into o~ [512] (normalised), then o = o~ W_UV,h.
 __global__ __launch_bounds__(256) void mla_merge_kernel(MlaArgs a) {
   const int h = blockIdx.x, b0 = 4 * blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   __shared__ float ot[4][kDC];
   __shared__ float mM[4], mInv[4];
-  __shared__ int nps[4];
+  __shared__ int nps[4], pfirst[4];
   __shared__ float red[256 * 32];
   const int nb = min(4, a.num_seqs - b0);
-  {  // wave bb: pieces, global max and 1 / sum of sequence b0 + bb
+  {  // wave bb: partials, global max and 1 / sum of sequence b0 + bb; its
+     // partials sit in slots w + b of the workgroups w that served its tiles
     const int bb = wave;
-    int n = 0;
+    int n = 0, p0 = 0;
     float M = -INFINITY;
     if (bb < nb) {
-      n = pieces_of(a, b0 + bb);
-      for (int s = lane; s < n; s += 64) M = fmaxf(M, a.ws_m[((int64_t)(b0 + bb) * a.splits + s) * kHeads + h]);
+      const int b = b0 + bb, T = a.ts[a.num_seqs];
+      const int tsb = a.ts[b], tse = a.ts[b + 1];
+      if (tse > tsb) {
+        const int wf = tile_owner(tsb, T, a.grid), wl = tile_owner(tse - 1, T, a.grid);
+        n = wl - wf + 1;
+        p0 = wf + b;
+      }
+      for (int s = lane; s < n; s += 64) M = fmaxf(M, a.ws_m[((int64_t)p0 + s) * kHeads + h]);
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
     }
     float L = 0.0f;
     if (M != -INFINITY) {
       for (int s = lane; s < n; s += 64) {
-        const int64_t i = ((int64_t)(b0 + bb) * a.splits + s) * kHeads + h;
+        const int64_t i = ((int64_t)p0 + s) * kHeads + h;
         L += __builtin_amdgcn_exp2f(a.ws_m[i] - M) * a.ws_l[i];
       }
 #pragma unroll
@@ -443,6 +758,7 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(MlaArgs a) {
     }
     if (lane == 0) {
       nps[bb] = (M == -INFINITY || !(L > 0.0f)) ? 0 : n;
+      pfirst[bb] = p0;
       mM[bb] = M;
       mInv[bb] = L > 0.0f ? 1.0f / L : 0.0f;
     }
@@ -453,7 +769,7 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(MlaArgs a) {
     const int n = nps[bb];
     const float M = mM[bb];
     float v[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-    const int64_t p0 = (int64_t)(b0 + bb) * a.splits;
+    const int64_t p0 = pfirst[bb];
     constexpr int kBatch = 4;  // pieces whose loads are in flight together
     for (int s0 = 0; s0 < n; s0 += kBatch) {
       f32x4 x[kBatch][2];
@@ -526,28 +842,42 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(MlaArgs a) {
 }
 
 struct MlaPlan {
-  int row, splits;
-  size_t off_qhi, off_qlo, off_m, off_l, off_o, bytes;
+  int row;
+  size_t off_qhi, off_qlo, off_ts, off_m, off_l, off_o, bytes;
 };
 
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
-MlaPlan mla_plan(int32_t num_seqs, int32_t rope_dim, int32_t max_blocks_per_seq, int32_t block_size) {
+// One split workgroup per compute unit of the current device, at most
+// kMaxGrid (the workspace holds kMaxGrid + B partial slots).
+constexpr int kMaxGrid = 256;
+pa_status split_grid(const char* fn, int* grid) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return fail(PA_EHIP, "%s: cannot read the device's compute-unit count", fn);
+  *grid = cus < kMaxGrid ? cus : kMaxGrid;
+  return PA_OK;
+}
+
+MlaPlan mla_plan(int32_t num_seqs, int32_t rope_dim) {
   MlaPlan p;
   p.row = kDC + rope_dim;
-  p.splits = (int)(((int64_t)max_blocks_per_seq * block_size + kSplit - 1) / kSplit);
   const size_t B = (size_t)(num_seqs > 0 ? num_seqs : 1);
+  const size_t slots = (size_t)kMaxGrid + B;  // partial slot w + b
   size_t off = 0;
   p.off_qhi = off;
   off = round256(off + B * kHeads * p.row * 2);
   p.off_qlo = off;
   off = round256(off + B * kHeads * p.row * 2);
+  p.off_ts = off;
+  off = round256(off + (B + 1) * 4);
   p.off_m = off;
-  off = round256(off + B * p.splits * kHeads * 4);
+  off = round256(off + slots * kHeads * 4);
   p.off_l = off;
-  off = round256(off + B * p.splits * kHeads * 4);
+  off = round256(off + slots * kHeads * 4);
   p.off_o = off;
-  off = round256(off + B * p.splits * kHeads * (size_t)kDC * 4);
+  off = round256(off + slots * kHeads * (size_t)kDC * 4);
   p.bytes = off;
   return p;
 }
@@ -577,7 +907,7 @@ extern "C" size_t pa_mla_decode_workspace_size(int32_t num_seqs, int32_t num_hea
   if (check_mla_shape("pa_mla_decode_workspace_size", num_seqs, num_heads, qk_nope_dim, rope_dim, kv_lora_rank, v_dim,
                       max_blocks_per_seq, block_size) != PA_OK)
     return 0;
-  return mla_plan(num_seqs, rope_dim, max_blocks_per_seq, block_size).bytes;
+  return mla_plan(num_seqs, rope_dim).bytes;
 }
 
 extern "C" pa_status pa_mla_decode_attention(void* out, pa_dtype out_dtype, int64_t out_seq_stride, const void* q_nope,
@@ -612,10 +942,16 @@ extern "C" pa_status pa_mla_decode_attention(void* out, pa_dtype out_dtype, int6
     return fail(PA_EINVAL, "%s: null pointer argument", fn);
   if (!aligned(latent_cache, 16) || (block_stride * 2) % 16 != 0)
     return fail(PA_EINVAL, "%s: latent cache must be 16-byte aligned per block", fn);
+  if (num_blocks > 0 && (num_blocks * block_stride * 2) / 16 > (int64_t)UINT32_MAX)
+    return fail(PA_EUNSUPPORTED, "%s: latent cache above 64 GiB", fn);
+  if (num_seqs > (1 << 20)) return fail(PA_EUNSUPPORTED, "%s: more than 2^20 sequences per call", fn);
   if (!aligned(w_uk, 16) || !aligned(w_uv, 16)) return fail(PA_EINVAL, "%s: weights must be 16-byte aligned", fn);
   if (!aligned(q_nope, 16) || (q_nope_seq_stride * 2) % 16 != 0)
     return fail(PA_EINVAL, "%s: q_nope must be 16-byte aligned per sequence", fn);
-  const MlaPlan p = mla_plan(num_seqs, rope_dim, max_blocks_per_seq, block_size);
+  // tiles of 32 positions over all sequences must count in 32 bits
+  if ((int64_t)num_seqs * (((int64_t)max_blocks_per_seq * block_size + kTile - 1) / kTile) > INT32_MAX / 2)
+    return fail(PA_EINVAL, "%s: too many (sequence, tile) items", fn);
+  const MlaPlan p = mla_plan(num_seqs, rope_dim);
   if (!workspace || workspace_bytes < p.bytes || !aligned(workspace, 256))
     return fail(PA_EWORKSPACE, "%s: workspace needs %zu bytes, 256-byte aligned (got %zu)", fn, p.bytes, workspace_bytes);
 
@@ -631,6 +967,7 @@ extern "C" pa_status pa_mla_decode_attention(void* out, pa_dtype out_dtype, int6
   char* ws = static_cast<char*>(workspace);
   a.q_hi = reinterpret_cast<uint16_t*>(ws + p.off_qhi);
   a.q_lo = reinterpret_cast<uint16_t*>(ws + p.off_qlo);
+  a.ts = reinterpret_cast<int32_t*>(ws + p.off_ts);
   a.ws_m = reinterpret_cast<float*>(ws + p.off_m);
   a.ws_l = reinterpret_cast<float*>(ws + p.off_l);
   a.ws_o = reinterpret_cast<float*>(ws + p.off_o);
@@ -640,26 +977,25 @@ extern "C" pa_status pa_mla_decode_attention(void* out, pa_dtype out_dtype, int6
   a.block_stride = block_stride;
   a.num_blocks = num_blocks;
   a.block_size = block_size;
+  a.bs_log2 = (block_size & (block_size - 1)) == 0 ? __builtin_ctz((unsigned)block_size) : -1;
   a.W = max_blocks_per_seq;
   a.num_seqs = num_seqs;
   a.qk = qk_nope_dim;
   a.dr = rope_dim;
   a.dv = v_dim;
-  a.splits = p.splits;
   a.out_f32 = out_dtype == PA_F32;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
 
-  // one workgroup per live piece at most: sum over sequences of ceil(ctx / 256)
-  // <= num_seqs * splits; workgroups past the last live piece exit at once.
-  // Checked before the first launch, so a refusal leaves nothing enqueued.
-  const int64_t items = (int64_t)num_seqs * p.splits;
-  if (items > INT32_MAX / 2) return fail(PA_EINVAL, "%s: too many (sequence, piece) items", fn);
+  int grid = 0;
+  s = split_grid(fn, &grid);
+  if (s != PA_OK) return s;
+  a.grid = grid;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   mla_absorb_kernel<<<dim3(kHeads, kDC / 64, (unsigned)((num_seqs + 15) / 16)), 256, 0, st>>>(a, row);
   if (rope_dim == 64)
-    mla_split_kernel<64><<<(unsigned)items, 64 * kWaves, 0, st>>>(a);
+    mla_split_kernel<64><<<(unsigned)grid, 64 * (kWaves + kProducers), 0, st>>>(a);
   else
-    mla_split_kernel<0><<<(unsigned)items, 64 * kWaves, 0, st>>>(a);
+    mla_split_kernel<0><<<(unsigned)grid, 64 * (kWaves + kProducers), 0, st>>>(a);
   mla_merge_kernel<<<dim3(kHeads, (unsigned)((num_seqs + 3) / 4)), 256, 0, st>>>(a);
   return after_launch(fn);
 }
