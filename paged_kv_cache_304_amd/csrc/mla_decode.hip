@@ -20,17 +20,16 @@
 //    hi + lo (x - hi rounded again), so that the products below keep ~16 more
 //    bits than a bf16 q~ would.
 //  * split: persistent, one workgroup per compute unit over an even share of
-//    the 32-position tiles of all sequences; 4 computing waves and 2 fetching
-//    waves that meet through LDS counters (no workgroup barrier per tile).
-//    The fetching waves move each item -- a segment's q~, then its latent
-//    tiles -- by LDS-DMA into a 4-deep ring. Scores S^T = C q~^T on
-//    v_mfma_f32_16x16x32_bf16 (hi and lo; each computing wave takes a quarter
-//    of the 576-dim contraction with its q~ operands held in registers, and
-//    the partial sums meet in LDS); online softmax in the log2 domain;
-//    O += P C with P split into hi + lo as well and C's operand from LDS by
-//    transposing reads, each wave owning 128 of the 512 latent dims. Writes
-//    the unnormalised O, its running max and sum per head for each
-//    (workgroup, sequence) segment.
+//    the 32-position tiles of all sequences; 2 fetching waves move each item
+//    -- a segment's q~, then its latent tiles -- by LDS-DMA into a 4-deep LDS
+//    ring, and the computing waves meet them and each other through LDS
+//    counters (no workgroup barrier per tile). Two score waves (8 heads each)
+//    form S^T = C [q~hi | q~lo] on v_mfma_f32_16x16x32_bf16 with q~ held in
+//    registers, add the hi and lo columns, run the online softmax in the log2
+//    domain and hand P over as bf16 hi + lo rows; four P.V waves (128 latent
+//    dims each) form O += P C on v_mfma_f32_32x32x16_bf16 with C's operand
+//    from LDS by transposing reads. Writes the unnormalised O, its running
+//    max and sum per head for each (workgroup, sequence) segment.
 //  * merge: combines the pieces of a sequence and applies W_UV per head.
 #include <math.h>
 
@@ -49,7 +48,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kDC = 512;        // latent (kv_lora_rank) dims
 constexpr int kHeads = 16;      // query heads (the MFMA's 16-wide operand)
 constexpr int kTile = 32;       // positions per tile
-constexpr int kWaves = 4;       // compute waves of a split workgroup
+constexpr int kScore = 2;       // score waves of a split workgroup (8 heads each)
+constexpr int kPV = 4;          // P.V waves (128 latent dims each)
+constexpr int kWaves = kScore + kPV;  // computing waves: each takes part in every item
 constexpr int kProducers = 2;   // ... and its fetching waves (16 rows of an item each)
 constexpr int kRing = 4;        // LDS item buffers: one being computed, three in flight
 constexpr int kTabSlots = 8;    // LDS slots of fetched block-table entries
@@ -64,7 +65,7 @@ struct MlaGeo {
   static constexpr int TILE = kTile * RB;        // bytes per LDS tile (rows back to back)
   static constexpr int LOADS = TILE / 1024;      // 1 KB LDS-DMA wave loads per tile
   static constexpr int LPP = LOADS / kProducers; // ... per fetching wave: 16 rows
-  static constexpr int KSTEPS = ROW / 32;        // 16x16x32 MFMA steps over the row
+  static constexpr int KS = ROW / 32;            // 16x16x32 MFMA steps over the row
   static_assert(CH % 8 == 0 && TILE % 1024 == 0 && LPP * 1024 == 16 * RB, "tile geometry");
   // Chunk swizzle: physical chunk of logical chunk lc in row r is lc ^ sw(r),
   // so that 16 consecutive rows read at one logical chunk hit 16 different
@@ -148,11 +149,15 @@ __device__ void plan_tiles(const MlaArgs& a) {
 // ---------------------------------------------------------------- absorb
 // q~^T [512 c x B] = W_UK,h [512 x qk] q_h^T [qk x B] per head on the matrix
 // cores (bf16 x bf16 products are exact in fp32, sums in fp32). grid (16
-// heads, 8 blocks of 64 latent dims, ceil(B / 16)); wave w computes latent
+// heads, 8 blocks of 64 latent dims, ceil(B / 16) + 1: the last layer writes the
+// tile plan of the split and nothing else); wave w computes latent
 // dims 64 cb + 16 w .. +15 for 16 sequences. The A operand is 16 bytes of a
 // W_UK row (dims 8 (l/16) .. of row l%16), the B operand 16 bytes of a q row.
 __global__ __launch_bounds__(256) void mla_absorb_kernel(MlaArgs a, int row) {
-  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) plan_tiles(a);  // uniform per workgroup
+  if (blockIdx.z == gridDim.z - 1) {  // the extra layer: its first workgroup writes the tile plan
+    if (blockIdx.x == 0 && blockIdx.y == 0) plan_tiles(a);
+    return;
+  }
   const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
   const int c0 = 64 * blockIdx.y + 16 * wave, b0 = 16 * blockIdx.z;
@@ -232,6 +237,16 @@ __device__ __forceinline__ float max_over_groups(float x) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+// sum over the four lanes l % 16 + 16 j (every lane gets the same sum)
+__device__ __forceinline__ float sum_over_groups(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const float m = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const uint32_t v = __float_as_uint(m);
+  const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // block and offset of a position (a shift when the block size is a power of two)
 __device__ __forceinline__ void block_of(const MlaArgs& a, int pos, int& blk, int& off) {
   if (a.bs_log2 >= 0) {
@@ -253,24 +268,26 @@ constexpr float kLazyMax = 8.0f;  // log2 headroom of a segment's running max
 // unnormalised O of the 16 heads) at slot w + b of the workspace (w + b is
 // unique: a later workgroup never serves an earlier sequence).
 //
-// Roles: waves 0..3 compute (each a quarter of the score contraction and 128
-// latent dims of O), waves 4 and 5 fetch. Every item goes global -> LDS by
-// LDS-DMA into a ring of kRing buffers; fetching wave p moves rows 16 p ..
-// 16 p + 15 of each item and, kAhead + 1 items ahead, the block-table entries
-// of those rows (4 bytes a lane), so that no load the compiler sees sits in its
-// loop (vector-memory counters complete in order; waiting for such a load
-// would wait for the items in flight too). The two roles meet through LDS
-// counters instead of workgroup barriers, so that a fetching wave whose DMA
-// issue stalls on a full memory pipeline never holds a computing wave, nor
-// the other way round:
+// Roles: waves 0 and 1 score (8 heads each), waves 2..5 multiply P by the
+// latent rows (128 latent dims of O each), waves 6 and 7 fetch. Every item
+// goes global -> LDS by LDS-DMA into a ring of kRing buffers; fetching wave p
+// moves rows 16 p .. 16 p + 15 of each item and, kAhead + 1 items ahead, the
+// block-table entries of those rows (4 bytes a lane), so that no load the
+// compiler sees sits in its loop (vector-memory counters complete in order;
+// waiting for such a load would wait for the items in flight too). Every
+// computing wave reads what it needs of an item into registers and gives the
+// buffer back at once; the roles meet through LDS counters instead of
+// workgroup barriers, so that a fetching wave whose DMA issue stalls on a full
+// memory pipeline never holds a computing wave, nor the other way round:
 //  * ready[p]: items whose share from fetching wave p has landed (raised
 //    after its own vmcnt wait); a computing wave starts item i when both are
 //    past i;
-//  * consumed: +1 per computing wave and finished item; a fetching wave
-//    refills item i's buffer (with item i + kRing) only when it reaches
+//  * consumed: +1 per computing wave once it has read item i; a fetching
+//    wave refills item i's buffer (with item i + kRing) only when it reaches
 //    kWaves (i + 1);
-//  * sx_in / sx_out: the computing waves' exchange of partial scores (written,
-//    then read by all four) for the k-th tile.
+//  * p_ready / p_done: the score waves' P of the k-th tile (bf16 hi and lo,
+//    in one of two LDS buffers) is written (+1 per score wave) and read
+//    (+1 per P.V wave).
 // Every wait polls with a bound: counts that never arrive end the kernel (with
 // wrong results) instead of hanging the device.
 __device__ __forceinline__ uint32_t lds_load_u32(const uint32_t* p) {
@@ -299,20 +316,23 @@ template <int DR>
 __global__ __launch_bounds__(64 * (kWaves + kProducers)) void mla_split_kernel(MlaArgs a) {
   using Gm = MlaGeo<DR>;
   constexpr int ROW = Gm::ROW, RB = Gm::RB, LPP = Gm::LPP;
-  constexpr int KSTEPS = Gm::KSTEPS, QMAX = (KSTEPS + kWaves - 1) / kWaves;
+  constexpr int KS = Gm::KS;
   const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, lg = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = (int)gridDim.x, w = (int)blockIdx.x, B = a.num_seqs;
 
   __shared__ __attribute__((aligned(16))) char ring[kRing][Gm::TILE];
-  __shared__ f32x4 sx[kWaves][2][64];
+  constexpr int kPRow = 64;  // bytes per P row (32 positions)
+  __shared__ __attribute__((aligned(16))) char pbuf[2][32 * kPRow];  // P of tiles k, k + 1 (hi rows, then lo)
+  __shared__ float palpha[2][kHeads];                                // their rescale factors of O
+  __shared__ int praise[2][kScore];                                  // some head's max was raised
   __shared__ __attribute__((aligned(16))) int32_t tab[kProducers][kTabSlots][64];
   __shared__ int desc[kRing][4];  // item: local tile (-1 q~, -2 none), sequence, last tile of its segment
   __shared__ uint32_t rowmask[kRing][kProducers];
-  __shared__ uint32_t ready[kProducers], consumed, sx_in, sx_out;
+  __shared__ uint32_t ready[kProducers], consumed, p_ready, p_done;
   if (tid == 0) {
     for (int p2 = 0; p2 < kProducers; ++p2) ready[p2] = 0u;
-    consumed = sx_in = sx_out = 0u;
+    consumed = p_ready = p_done = 0u;
   }
   __syncthreads();  // the counters start at zero (before any load is in flight)
 
@@ -495,22 +515,32 @@ __global__ __launch_bounds__(64 * (kWaves + kProducers)) void mla_split_kernel(M
     // entries of items 0 .. kAhead
 #pragma unroll
     for (int s2 = 0; s2 <= kAhead; ++s2) fetch_tab(s2, dl[s2], db[s2]);
-    wait_vmem<0>();
     bool ok_run = true;
     for (int j = 0; ok_run; ++j) {
-      // Step j: item j goes into buffer j % kRing once item j - kRing is done
-      // with; item j - kAhead is published once this wave's share of it has
+      // Step j: item j - kAhead is published once this wave's share of it has
       // landed -- this wave's later operations, the entries and data of items
       // j - kAhead + 1 .. j - 1 (entries run kAhead + 1 items ahead of data),
-      // are then all that may be in flight.
-      if (j >= kRing) ok_run = wait_at_least(&consumed, (uint32_t)(kWaves * (j - kRing + 1)));
-      if (!ok_run) break;
-      if (j >= kAhead) {
-        static_assert(kAhead == 3, "the wait below counts two steps of (LPP + 1) operations");
+      // are then all that may be in flight --, before the wait for a buffer,
+      // so that a landed item never waits for one; item j goes into buffer
+      // j % kRing once item j - kRing is done with.
+      // In flight at the start of step j: the prologue's entries of items
+      // min(j, kAhead + 1) .. kAhead, then per earlier step the entries of
+      // one item and the data of another (LPP + 1 operations). Item 0 is a
+      // segment's q~ (it needs no entries); steps 2 and 3 wait for items 0
+      // and 1 themselves, so that the first tile is published a step early.
+      static_assert(kAhead == 3, "the waits below count steps of (LPP + 1) operations");
+      if (j == 1) wait_vmem<LPP + 3>();  // item 1's entries (the prologue's second)
+      if (j == 2 || j == 3) {
+        wait_vmem<LPP + 1>();  // items j - 2 and all before them, with the prologue's entries
+        compiler_fence();
+        if (lane == 0) lds_store_u32(&ready[pw], (uint32_t)(j - 1));
+      } else if (j > kAhead) {
         wait_vmem<2 * (LPP + 1)>();
         compiler_fence();
         if (lane == 0) lds_store_u32(&ready[pw], (uint32_t)(j - kAhead + 1));
       }
+      if (j >= kRing) ok_run = wait_at_least(&consumed, (uint32_t)(kWaves * (j - kRing + 1)));
+      if (!ok_run) break;
       if (dl[0] == -2) {  // item j is past the last one: the end marker in its buffer's slot
         if (pw == 0 && lane == 0) desc[j % kRing][0] = -2;
         break;
@@ -536,25 +566,130 @@ __global__ __launch_bounds__(64 * (kWaves + kProducers)) void mla_split_kernel(M
     return;
   }
 
-  // ================================================================ compute
+  // ================================================================ score waves
   if (a.num_blocks == 0) return;  // uniform: the fetching waves write the partials
-  // This wave's share of the score contraction: steps s0 .. s0 + nst - 1 of
-  // KSTEPS (32 dims each); its q~ operands (head li, dims 32 s + 8 lg ..) are
-  // read from a q~ item into registers for the segment.
-  const int base_n = KSTEPS / kWaves, rem = KSTEPS % kWaves;
-  const int nst = base_n + (wave < rem ? 1 : 0);
-  const int s0 = wave * base_n + min(wave, rem);
-  bf16x8 qh[QMAX], ql[QMAX];
+  typedef float f32x16 __attribute__((ext_vector_type(16)));
+  const int r32 = lane & 31, h32 = lane >> 5;
+  if (wave < kScore) {
+    // Score wave sw takes heads 8 sw .. 8 sw + 7: S^T = C [q~hi | q~lo] on
+    // v_mfma_f32_16x16x32_bf16 per 16-position block rb, A = positions
+    // 16 rb + li (dims 32 s + 8 lg ..), B = 16 columns: the hi parts of its 8
+    // heads, then their lo parts (held in registers for the segment). Lane l
+    // gets column li at positions 16 rb + 4 lg + r; columns li and li ^ 8 add
+    // up to head 8 sw + li % 8's score.
+    const int sw = wave;
+    const int qrow = (li < 8 ? 0 : 16) + 8 * sw + (li & 7);  // q~ item row of column li, and P row
+    bf16x8 qb[KS];
+    float m_run = -INFINITY, l_run = 0.0f;  // of head 8 sw + li % 8 (every lane of that head agrees)
+    uint32_t k = 0;                         // tiles scored in this workgroup
+    for (int i = 0;; ++i) {
+      bool ok = true;
 #pragma unroll
-  for (int i = 0; i < QMAX; ++i) qh[i] = ql[i] = bf16x8{};
-
-  const int dim0 = 128 * wave;  // this wave's 128 latent dims of O
-  float m_run = -INFINITY, l_run = 0.0f;
-  f32x4 acc[8];
+      for (int p2 = 0; p2 < kProducers; ++p2) ok = ok && wait_at_least(&ready[p2], (uint32_t)(i + 1));
+      if (!ok) break;
+      const int slot = i % kRing;
+      const int lt = uniform(desc[slot][0]);
+      if (lt == -2) break;
+      const int bb = uniform(desc[slot][1]);
+      const int last = uniform(desc[slot][2]);
+      const char* tile = ring[slot];
+      if (lt == -1) {  // q~ of a new segment: rows 0..15 its hi parts, 16..31 its lo parts
 #pragma unroll
-  for (int cb = 0; cb < 8; ++cb) acc[cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  uint32_t ntile = 0;  // tiles this workgroup has computed (the score exchange count)
+        for (int s = 0; s < KS; ++s)
+          qb[s] = *reinterpret_cast<const bf16x8*>(tile + qrow * RB + 16 * Gm::phys(qrow, 4 * s + lg));
+        m_run = -INFINITY;
+        l_run = 0.0f;
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // its reads are done: the buffer may be refilled
+        if (lane == 0) lds_add_u32(&consumed, 1u);
+        continue;
+      }
+      const uint32_t valid = uniform(rowmask[slot][0]) | uniform(rowmask[slot][1]);  // bit r: position r takes part
+      f32x4 S[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          const int r = 16 * rb + li;
+          const bf16x8 cop = *reinterpret_cast<const bf16x8*>(tile + r * RB + 16 * Gm::phys(r, 4 * s + lg));
+          S[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cop, qb[s], S[rb], 0, 0, 0);
+        }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the tile's reads are done
+      if (lane == 0) lds_add_u32(&consumed, 1u);
+      float sc[8];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float x = S[rb][r];
+          const float y = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));  // lane li ^ 8
+          const int p = 16 * rb + 4 * lg + r;
+          sc[4 * rb + r] = ((valid >> p) & 1u) ? x + y : -INFINITY;
+        }
+      float mx = sc[0];
+#pragma unroll
+      for (int v = 1; v < 8; ++v) mx = fmaxf(mx, sc[v]);
+      mx = max_over_groups(mx);
+      // lazy running max: raised only when the tile's max passes it by more
+      // than kLazyMax (first tile: any finite max), so p = 2^(s - m) <= 2^kLazyMax
+      const bool raise = mx > m_run + kLazyMax;
+      const float mn = raise ? mx : m_run;
+      const float mu = (mn == -INFINITY) ? 0.0f : mn;
+      const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - mu) : 1.0f;
+      float pr[8], ps = 0.0f;
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        pr[v] = __builtin_amdgcn_exp2f(sc[v] - mu);
+        ps += pr[v];
+      }
+      ps = sum_over_groups(ps);
+      l_run = l_run * alpha + ps;
+      m_run = mn;
+      // P to the P.V waves: P row qrow holds head 8 sw + li % 8's bf16 hi part
+      // (li < 8) or its lo part, lo = bf16(p - hi): hi + lo is within 2^-17 of
+      // the fp32 p. Lane l writes positions 16 rb + 4 lg .. + 3 (8 bytes each).
+      const uint32_t pb = k & 1u;
+      if (k >= 2 && !wait_at_least(&p_done, kPV * (k - 1))) break;  // tile k - 2 has left this buffer
+      char* prow = pbuf[pb] + qrow * kPRow;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        uint32_t wd[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const float x0 = pr[4 * rb + 2 * e], x1 = pr[4 * rb + 2 * e + 1];
+          const uint32_t hi = f32x2_to_bf16x2(x0, x1);
+          wd[e] = li < 8 ? hi : f32x2_to_bf16x2(x0 - bf16_lo(hi), x1 - bf16_hi(hi));
+        }
+        *reinterpret_cast<u32x2*>(prow + 2 * (16 * rb + 4 * lg)) = u32x2{wd[0], wd[1]};
+      }
+      if (lane < 8) palpha[pb][8 * sw + lane] = alpha;
+      if (lane == 0) praise[pb][sw] = __builtin_amdgcn_ballot_w64(raise) != 0 ? 1 : 0;
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (lane == 0) lds_add_u32(&p_ready, 1u);
+      ++k;
+      if (last && lane < 8) {  // the segment's running max and sum of this wave's heads
+        const int64_t pslot = (int64_t)w + bb;
+        a.ws_m[pslot * kHeads + 8 * sw + lane] = m_run;
+        a.ws_l[pslot * kHeads + 8 * sw + lane] = l_run;
+      }
+    }
+    return;
+  }
 
+  // ================================================================ P.V waves
+  // O2 [32 x 512] += P2 [32 x 32] C [32 x 512] on v_mfma_f32_32x32x16_bf16:
+  // P2's rows are the heads' P hi parts, then their lo parts (so O = rows h
+  // + rows 16 + h); wave pv owns latent dims 128 pv .. + 127 as 4 blocks of
+  // 32. P2's A operand: lane l row r32, positions 16 ks + 8 h32 .. + 7. C's B
+  // operand (lane: dim r32 of a block, the same positions) comes by
+  // transposing reads: the read of a 16-lane group with base row R and base
+  // column Q gives lane i C[R + j][Q + i], j = 0..3. Lane l gets O2's column
+  // r32 at rows 8 (v / 4) + 4 h32 + v % 4.
+  const int pv = wave - kScore;
+  f32x16 acc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) acc[db] = f32x16{};
+  uint32_t k = 0;  // tiles multiplied in this workgroup
+  const int g = lane >> 4, li16 = lane & 15;
   for (int i = 0;; ++i) {
     bool ok = true;
 #pragma unroll
@@ -565,156 +700,77 @@ __global__ __launch_bounds__(64 * (kWaves + kProducers)) void mla_split_kernel(M
     if (lt == -2) break;
     const int bb = uniform(desc[slot][1]);
     const int last = uniform(desc[slot][2]);
-    const char* tile = ring[slot];
-
-    if (lt == -1) {  // q~ of a new segment
+    if (lt == -1) {  // a new segment
 #pragma unroll
-      for (int q = 0; q < QMAX; ++q) {
-        if (q < nst) {
-          const int lc = 4 * (s0 + q) + lg;
-          qh[q] = *reinterpret_cast<const bf16x8*>(tile + li * RB + 16 * Gm::phys(li, lc));
-          ql[q] = *reinterpret_cast<const bf16x8*>(tile + (16 + li) * RB + 16 * Gm::phys(16 + li, lc));
-        }
-      }
-      m_run = -INFINITY;
-      l_run = 0.0f;
-#pragma unroll
-      for (int cb = 0; cb < 8; ++cb) acc[cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // its reads are done: the buffer may be refilled
+      for (int db = 0; db < 4; ++db) acc[db] = f32x16{};
       if (lane == 0) lds_add_u32(&consumed, 1u);
       continue;
     }
-    const uint32_t valid = uniform(rowmask[slot][0]) | uniform(rowmask[slot][1]);  // bit r: position r takes part
-    // partial S^T of both 16-position blocks over this wave's contraction
-    // steps: rows = positions 16 pb + 4 lg + r, column = head li (hi and lo
-    // products in separate accumulators: four independent chains)
-    f32x4 sph[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
-    f32x4 spl[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+    const uint32_t valid = uniform(rowmask[slot][0]) | uniform(rowmask[slot][1]);
+    const char* tile = ring[slot];
+    u32x4 cv[4][2];
 #pragma unroll
-    for (int q = 0; q < QMAX; ++q) {
-      if (q < nst) {
-        const int lc = 4 * (s0 + q) + lg;  // logical chunk of dims 32 s + 8 lg ..
+    for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-        for (int pb = 0; pb < 2; ++pb) {
-          const int r = 16 * pb + li;
-          const bf16x8 cop = *reinterpret_cast<const bf16x8*>(tile + r * RB + 16 * Gm::phys(r, lc));
-          sph[pb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cop, qh[q], sph[pb], 0, 0, 0);
-          spl[pb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cop, ql[q], spl[pb], 0, 0, 0);
-        }
+      for (int db = 0; db < 4; ++db) {
+        const int q0 = 128 * pv + 32 * db + 16 * (g & 1) + 4 * (li16 & 3);  // this lane's column address
+        const int lc = (2 * q0) >> 4, within = (2 * q0) & 15;
+        const int R0 = 16 * ks + 8 * (g >> 1) + (li16 >> 2), R1 = R0 + 4;
+        const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(tile + R0 * RB + 16 * Gm::phys(R0, lc) + within));
+        const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(tile + R1 * RB + 16 * Gm::phys(R1, lc) + within));
+        cv[db][ks] = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
       }
-    }
-    // exchange: every wave is done reading the previous tile's partials, write
-    // this one's, then wait for all four
-    if (ntile > 0 && !wait_at_least(&sx_out, kWaves * ntile)) break;
-    sx[wave][0][lane] = sph[0] + spl[0];
-    sx[wave][1][lane] = sph[1] + spl[1];
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if (lane == 0) lds_add_u32(&sx_in, 1u);
-    if (!wait_at_least(&sx_in, kWaves * (ntile + 1))) break;
-    // full scores of head li at positions 4 lg + r (block 0) and 16 + 4 lg + r
-    // (block 1), summed over the waves in one fixed order
-    float sc[8];
-#pragma unroll
-    for (int pb = 0; pb < 2; ++pb) {
-      f32x4 s4 = sx[0][pb][lane];
-#pragma unroll
-      for (int v = 1; v < kWaves; ++v) s4 += sx[v][pb][lane];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sc[4 * pb + r] = s4[r];
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if (lane == 0) lds_add_u32(&sx_out, 1u);
-    ++ntile;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const bool okp = (valid >> (16 * (k >> 2) + 4 * lg + (k & 3))) & 1u;
-      sc[k] = okp ? sc[k] : -INFINITY;
-    }
-    float mx = sc[0];
-#pragma unroll
-    for (int k = 1; k < 8; ++k) mx = fmaxf(mx, sc[k]);
-    mx = max_over_groups(mx);
-    // The running max is raised only when the tile's max passes it by more
-    // than kLazyMax (first tile: any finite max): probabilities 2^(s - m)
-    // then stay below 2^kLazyMax and the rescale of O is rare.
-    const bool raise = mx > m_run + kLazyMax;
-    const float mn = raise ? mx : m_run;
-    const float mu = (mn == -INFINITY) ? 0.0f : mn;
-    const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - mu) : 1.0f;
-    float pr[8];
-    float ps = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      pr[k] = __builtin_amdgcn_exp2f(sc[k] - mu);
-      ps += pr[k];
-    }
-    l_run = l_run * alpha + ps;
-    m_run = mn;
-    // rescale O rows (heads 4 lg + r) by their heads' alpha
-    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-      float al[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) al[r] = bcast_lane(alpha, 4 * lg + r);
-#pragma unroll
-      for (int cb = 0; cb < 8; ++cb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[cb][r] *= al[r];
-    }
-    // P as the A operand (row = head li, contraction = this lane's 8
-    // positions) in hi + lo halves
-    uint32_t phw[4], plw[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      phw[e] = f32x2_to_bf16x2(pr[2 * e], pr[2 * e + 1]);
-      plw[e] = f32x2_to_bf16x2(pr[2 * e] - bf16_lo(phw[e]), pr[2 * e + 1] - bf16_hi(phw[e]));
-    }
-    const bf16x8 ph = __builtin_bit_cast(bf16x8, u32x4{phw[0], phw[1], phw[2], phw[3]});
-    const bf16x8 pl = __builtin_bit_cast(bf16x8, u32x4{plw[0], plw[1], plw[2], plw[3]});
-    // C rows of masked positions -> 0 in the operand (their slots may hold
-    // NaN; their probabilities are 0): element e is row 4 lg + e (e < 4) or
-    // 16 + 4 lg + e - 4
-    u32x4 vmask = {~0u, ~0u, ~0u, ~0u};
-    if (valid != 0xFFFFFFFFu) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int e0 = 2 * q, e1 = 2 * q + 1;
-        const int r0 = (e0 < 4 ? 0 : 16) + 4 * lg + (e0 & 3), r1 = (e1 < 4 ? 0 : 16) + 4 * lg + (e1 & 3);
-        vmask[q] = (((valid >> r0) & 1u) ? 0xFFFFu : 0u) | (((valid >> r1) & 1u) ? 0xFFFF0000u : 0u);
-      }
-    }
-    // O += P C over this wave's dims: transposing reads give lane (m, g)
-    // C[4g + j][d0 + m] (low half) and C[16 + 4g + j][d0 + m] (high half)
-    const int trow = 4 * lg + (li >> 2);
-#pragma unroll
-    for (int cb = 0; cb < 8; ++cb) {
-      const int col = 2 * (dim0 + 16 * cb + 4 * (li & 3));  // byte column of the 8-byte read
-      const int lc = col >> 4, within = col & 15;
-      const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4*)(tile + trow * RB + 16 * Gm::phys(trow, lc) + within));
-      const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(
-          tile + (trow + 16) * RB + 16 * Gm::phys(trow + 16, lc) + within));
-      u32x4 wv = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-      wv &= vmask;
-      const bf16x8 vop = __builtin_bit_cast(bf16x8, wv);
-      acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vop, acc[cb], 0, 0, 0);
-      acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vop, acc[cb], 0, 0, 0);
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the tile's reads are done: its buffer may be refilled
     if (lane == 0) lds_add_u32(&consumed, 1u);
-    if (last) {  // the segment's last tile: its partial
-      // the four lane groups saw different positions under one running max
-      float lsum = l_run + __shfl_xor(l_run, 16, 64);
-      lsum += __shfl_xor(lsum, 32, 64);
-      const int64_t pslot = (int64_t)w + bb;
-      if (wave == 0 && lane < kHeads) {
-        a.ws_m[pslot * kHeads + lane] = m_run;
-        a.ws_l[pslot * kHeads + lane] = lsum;
+    // C elements of masked positions -> 0 (their slots may hold NaN; their p are 0)
+    u32x4 vmask[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int p0 = 16 * ks + 8 * h32 + 2 * q;
+        vmask[ks][q] = (((valid >> p0) & 1u) ? 0xFFFFu : 0u) | (((valid >> (p0 + 1)) & 1u) ? 0xFFFF0000u : 0u);
       }
-      float* o = a.ws_o + pslot * kHeads * kDC;
+    const uint32_t pb = k & 1u;
+    if (!wait_at_least(&p_ready, kScore * (k + 1u))) break;
+    // rescale O's rows by their heads' alpha when a score wave raised the max
+    if ((uniform(praise[pb][0]) | uniform(praise[pb][1])) != 0) {
+      float al[8];  // heads 8 jj + 4 h32 + r: rows 8 j + 4 h32 + r, j = jj, jj + 2
 #pragma unroll
-      for (int cb = 0; cb < 8; ++cb)
+      for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[(4 * lg + r) * kDC + dim0 + 16 * cb + li] = acc[cb][r];
+        for (int r = 0; r < 4; ++r) al[4 * jj + r] = palpha[pb][8 * jj + 4 * h32 + r];
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[db][v] *= al[4 * ((v >> 2) & 1) + (v & 3)];
+    }
+    bf16x8 pa[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      pa[ks] = *reinterpret_cast<const bf16x8*>(pbuf[pb] + r32 * kPRow + 2 * (16 * ks + 8 * h32));
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (lane == 0) lds_add_u32(&p_done, 1u);
+    ++k;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[ks], __builtin_bit_cast(bf16x8, cv[db][ks] & vmask[ks]),
+                                                         acc[db], 0, 0, 0);
+    if (last) {  // the segment's partial O: rows h and 16 + h summed
+      const int64_t pslot = (int64_t)w + bb;
+      float* o = a.ws_o + pslot * kHeads * kDC + 128 * pv + r32;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          const int h = 8 * (v >> 2) + 4 * h32 + (v & 3);
+          o[h * kDC + 32 * db] = acc[db][v] + acc[db][v + 8];
+        }
     }
   }
 }
@@ -991,7 +1047,7 @@ extern "C" pa_status pa_mla_decode_attention(void* out, pa_dtype out_dtype, int6
   if (s != PA_OK) return s;
   a.grid = grid;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  mla_absorb_kernel<<<dim3(kHeads, kDC / 64, (unsigned)((num_seqs + 15) / 16)), 256, 0, st>>>(a, row);
+  mla_absorb_kernel<<<dim3(kHeads, kDC / 64, (unsigned)((num_seqs + 15) / 16 + 1)), 256, 0, st>>>(a, row);
   if (rope_dim == 64)
     mla_split_kernel<64><<<(unsigned)grid, 64 * (kWaves + kProducers), 0, st>>>(a);
   else
