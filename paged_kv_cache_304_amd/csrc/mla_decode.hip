@@ -776,96 +776,111 @@ __global__ __launch_bounds__(64 * (kWaves + kProducers)) void mla_split_kernel(M
 }
 
 // ---------------------------------------------------------------- merge
-// grid (16 heads, ceil(B / 4)): the partials of each of 4 sequences combined
-// into o~ [512] (normalised), then o = o~ W_UV,h.
-__global__ __launch_bounds__(256) void mla_merge_kernel(MlaArgs a) {
+// grid (16 heads, ceil(B / 4)), 8 waves: the partials of each of 4 sequences
+// combined into o~ [512] (normalised), then o = o~ W_UV,h. Once the tile plan
+// is read, every load the workgroup needs goes out in one round: the
+// partials' maxima and sums, their first kMergeBatch outputs, and behind them
+// this thread's first kMergeW rows of W_UV,h (waiting for the partials leaves
+// those in flight). Wave w combines sequence b0 + w % 4 over latent dims
+// 256 (w / 4) + 4 lane .. + 3; thread (jg, cg) of the product takes 8 output
+// dims 8 jg .. and latent rows cg * rows .., and the row groups meet in LDS.
+constexpr int kMergeThreads = 512;
+constexpr int kMergeBatch = 12; // partial outputs of a sequence loaded in the first round
+constexpr int kMergeW = 16;     // W_UV rows of a thread loaded in the first round
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+__global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(MlaArgs a) {
   const int h = blockIdx.x, b0 = 4 * blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  __shared__ float ot[4][kDC];
-  __shared__ float mM[4], mInv[4];
-  __shared__ int nps[4], pfirst[4];
-  __shared__ float red[256 * 32];
-  const int nb = min(4, a.num_seqs - b0);
-  {  // wave bb: partials, global max and 1 / sum of sequence b0 + bb; its
-     // partials sit in slots w + b of the workgroups w that served its tiles
-    const int bb = wave;
-    int n = 0, p0 = 0;
-    float M = -INFINITY;
-    if (bb < nb) {
-      const int b = b0 + bb, T = a.ts[a.num_seqs];
-      const int tsb = a.ts[b], tse = a.ts[b + 1];
-      if (tse > tsb) {
-        const int wf = tile_owner(tsb, T, a.grid), wl = tile_owner(tse - 1, T, a.grid);
-        n = wl - wf + 1;
-        p0 = wf + b;
-      }
-      for (int s = lane; s < n; s += 64) M = fmaxf(M, a.ws_m[((int64_t)p0 + s) * kHeads + h]);
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-    }
-    float L = 0.0f;
-    if (M != -INFINITY) {
-      for (int s = lane; s < n; s += 64) {
-        const int64_t i = ((int64_t)p0 + s) * kHeads + h;
-        L += __builtin_amdgcn_exp2f(a.ws_m[i] - M) * a.ws_l[i];
-      }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o, 64);
-    }
-    if (lane == 0) {
-      nps[bb] = (M == -INFINITY || !(L > 0.0f)) ? 0 : n;
-      pfirst[bb] = p0;
-      mM[bb] = M;
-      mInv[bb] = L > 0.0f ? 1.0f / L : 0.0f;
-    }
-  }
-  __syncthreads();
-  {  // thread (bb, c8): o~[bb][8 c8 .. +8] as a weighted sum over the pieces
-    const int bb = wave, c = 8 * lane;
-    const int n = nps[bb];
-    const float M = mM[bb];
-    float v[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-    const int64_t p0 = pfirst[bb];
-    constexpr int kBatch = 4;  // pieces whose loads are in flight together
-    for (int s0 = 0; s0 < n; s0 += kBatch) {
-      f32x4 x[kBatch][2];
-      float w[kBatch];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int s = s0 + u < n ? s0 + u : s0;
-        const float* src = a.ws_o + ((p0 + s) * kHeads + h) * kDC + c;
-        x[u][0] = *reinterpret_cast<const f32x4*>(src);
-        x[u][1] = *reinterpret_cast<const f32x4*>(src + 4);
-        w[u] = s0 + u < n ? __builtin_amdgcn_exp2f(a.ws_m[(p0 + s) * kHeads + h] - M) : 0.0f;
-      }
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v[e] = fmaf(w[u], x[u][0][e], v[e]);
-          v[4 + e] = fmaf(w[u], x[u][1][e], v[4 + e]);
-        }
-    }
-    const float inv = mInv[bb];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) ot[bb][c + e] = v[e] * inv;
-  }
-  __syncthreads();
-  // o = o~ W_UV,h: thread (jg, cg) takes 8 output dims 8 jg.. and a slice of
-  // the 512 latent dims; the slices meet in LDS.
-  const int jgs = a.dv / 8, cgs = 256 / jgs;
+  __shared__ __attribute__((aligned(16))) float ot[4][kDC];
+  __shared__ float red[4 * 8 * kMergeThreads];  // [cg][4][dv]: cgs * dv = 8 * kMergeThreads
+  const int jgs = a.dv / 8, cgs = kMergeThreads / jgs, rows = kDC / cgs;
   const int jg = tid % jgs, cg = tid / jgs;
-  const int per = kDC / cgs;
+  const int64_t wrow = (int64_t)kHeads * a.dv;
+  const uint16_t* wbase = static_cast<const uint16_t*>(a.w_uv) + (int64_t)h * a.dv + 8 * jg + (int64_t)cg * rows * wrow;
+
+  // ---- sequence b0 + bb's partials sit in slots w + b of the workgroups w that served its tiles
+  const int bb = wave & 3, hd = wave >> 2;
+  const int b = b0 + bb;
+  int n = 0, p0 = 0;
+  if (b < a.num_seqs) {
+    const int T = a.ts[a.num_seqs], tsb = a.ts[b], tse = a.ts[b + 1];
+    if (tse > tsb) {
+      const int wf = tile_owner(tsb, T, a.grid), wl = tile_owner(tse - 1, T, a.grid);
+      n = wl - wf + 1;
+      p0 = wf + b;
+    }
+  }
+  n = uniform(n);
+  p0 = uniform(p0);
+
+  // ---- one round of loads
+  const int c4 = 256 * hd + 4 * lane;
+  float ms = -INFINITY, ls = 0.0f;  // lane s: piece s's max and sum
+  if (lane < n) {
+    const int64_t i = ((int64_t)p0 + lane) * kHeads + h;
+    ms = a.ws_m[i];
+    ls = a.ws_l[i];
+  }
+  f32x4 x[kMergeBatch];
+#pragma unroll
+  for (int u = 0; u < kMergeBatch; ++u)  // (n is uniform: no load past the count)
+    x[u] = u < n ? *reinterpret_cast<const f32x4*>(a.ws_o + (((int64_t)p0 + u) * kHeads + h) * kDC + c4)
+                 : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  u32x4 wv[kMergeW];
+#pragma unroll
+  for (int r = 0; r < kMergeW; ++r)
+    wv[r] = r < rows ? *reinterpret_cast<const u32x4*>(wbase + (int64_t)r * wrow) : u32x4{0u, 0u, 0u, 0u};
+
+  // ---- weights 2^(m_s - M), the sum L of their l_s, and o~ = sum_s w_s o_s / L
+  float M = ms;
+  for (int s = lane + 64; s < n; s += 64) M = fmaxf(M, a.ws_m[((int64_t)p0 + s) * kHeads + h]);
+  M = wave_max(M);
+  float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float inv = 0.0f;
+  if (n > 0 && M != -INFINITY) {  // uniform
+    const float wl = lane < n ? __builtin_amdgcn_exp2f(ms - M) : 0.0f;
+    float L = wl * ls;
+    for (int s = lane + 64; s < n; s += 64) {
+      const int64_t i = ((int64_t)p0 + s) * kHeads + h;
+      L += __builtin_amdgcn_exp2f(a.ws_m[i] - M) * a.ws_l[i];
+    }
+    L = wave_sum(L);
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), u));  // 0 past the count
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = fmaf(wu, x[u][e], v[e]);
+    }
+    for (int s = kMergeBatch; s < n; ++s) {  // sequences with more pieces
+      const int64_t i = ((int64_t)p0 + s) * kHeads + h;
+      const float ws = __builtin_amdgcn_exp2f(a.ws_m[i] - M);
+      const f32x4 xs = *reinterpret_cast<const f32x4*>(a.ws_o + i * kDC + c4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = fmaf(ws, xs[e], v[e]);
+    }
+    inv = L > 0.0f ? 1.0f / L : 0.0f;
+  }
+  *reinterpret_cast<f32x4*>(&ot[bb][c4]) = f32x4{v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv};
+  __syncthreads();
+
+  // ---- o = o~ W_UV,h over this thread's rows
   float acc[4][8];
 #pragma unroll
-  for (int bb = 0; bb < 4; ++bb)
+  for (int q = 0; q < 4; ++q)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[bb][e] = 0.0f;
-  const int64_t wrow = (int64_t)kHeads * a.dv;
-  const uint16_t* wbase = static_cast<const uint16_t*>(a.w_uv) + (int64_t)h * a.dv + 8 * jg;
-#pragma unroll 8
-  for (int c = cg * per; c < (cg + 1) * per; ++c) {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(wbase + c * wrow);
+    for (int e = 0; e < 8; ++e) acc[q][e] = 0.0f;
+  auto row_step = [&](const u32x4& w, int c) {
     float wf[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -873,27 +888,31 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(MlaArgs a) {
       wf[2 * e + 1] = bf16_hi(w[e]);
     }
 #pragma unroll
-    for (int bb = 0; bb < 4; ++bb) {
-      const float x = ot[bb][c];
+    for (int q = 0; q < 4; ++q) {
+      const float xo = ot[q][c];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[bb][e] = fmaf(x, wf[e], acc[bb][e]);
+      for (int e = 0; e < 8; ++e) acc[q][e] = fmaf(xo, wf[e], acc[q][e]);
     }
-  }
+  };
 #pragma unroll
-  for (int bb = 0; bb < 4; ++bb)
+  for (int r = 0; r < kMergeW; ++r)
+    if (r < rows) row_step(wv[r], cg * rows + r);
+  for (int r = kMergeW; r < rows; ++r) row_step(*reinterpret_cast<const u32x4*>(wbase + (int64_t)r * wrow), cg * rows + r);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) red[(cg * 4 + bb) * a.dv + 8 * jg + e] = acc[bb][e];
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[(cg * 4 + q) * a.dv + 8 * jg + e] = acc[q][e];
   __syncthreads();
-  for (int i = tid; i < 4 * a.dv; i += 256) {
-    const int bb = i / a.dv, j = i % a.dv;
-    if (bb >= nb) continue;
-    float v = 0.0f;
-    for (int g = 0; g < cgs; ++g) v += red[(g * 4 + bb) * a.dv + j];
-    const int64_t oi = (int64_t)(b0 + bb) * a.out_seq_stride + (int64_t)h * a.dv + j;
+  for (int i = tid; i < 4 * a.dv; i += kMergeThreads) {
+    const int q = i / a.dv, j = i % a.dv;
+    if (b0 + q >= a.num_seqs) continue;
+    float o = 0.0f;
+    for (int g = 0; g < cgs; ++g) o += red[(g * 4 + q) * a.dv + j];
+    const int64_t oi = (int64_t)(b0 + q) * a.out_seq_stride + (int64_t)h * a.dv + j;
     if (a.out_f32)
-      static_cast<float*>(a.out)[oi] = v;
+      static_cast<float*>(a.out)[oi] = o;
     else
-      static_cast<uint16_t*>(a.out)[oi] = (uint16_t)f32_to_bf16(v);
+      static_cast<uint16_t*>(a.out)[oi] = (uint16_t)f32_to_bf16(o);
   }
 }
 
@@ -1052,6 +1071,6 @@ extern "C" pa_status pa_mla_decode_attention(void* out, pa_dtype out_dtype, int6
     mla_split_kernel<64><<<(unsigned)grid, 64 * (kWaves + kProducers), 0, st>>>(a);
   else
     mla_split_kernel<0><<<(unsigned)grid, 64 * (kWaves + kProducers), 0, st>>>(a);
-  mla_merge_kernel<<<dim3(kHeads, (unsigned)((num_seqs + 3) / 4)), 256, 0, st>>>(a);
+  mla_merge_kernel<<<dim3(kHeads, (unsigned)((num_seqs + 3) / 4)), kMergeThreads, 0, st>>>(a);
   return after_launch(fn);
 }
