@@ -462,7 +462,10 @@ size_t pa_mla_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t
  *   heads per call), kv_lora_rank 512, rope_dim 0 or 64, qk_nope_dim a
  *   multiple of 8 up to 256, v_dim = 8 * a divisor of 256.
  * Errors: PA_EINVAL, PA_EDTYPE, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_EHIP.
- * num_seqs == 0 is a valid no-op.
+ * num_seqs == 0 is a valid no-op. The attention kernel's waves hand work to
+ * each other through bounded waits; should one ever run past its bound (it
+ * does not when every wave of a workgroup runs), the call ends instead of
+ * hanging and every output of the call is NaN.
  */
 pa_status pa_mla_decode_attention(void* out, pa_dtype out_dtype, int64_t out_seq_stride,
                                   const void* q_nope, int64_t q_nope_seq_stride,

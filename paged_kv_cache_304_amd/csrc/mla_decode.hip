@@ -86,6 +86,7 @@ struct MlaArgs {
   uint16_t* q_hi;   // [B, 16, ROW]
   uint16_t* q_lo;
   int32_t* ts;      // [B + 1] first global tile of each sequence; ts[B] = all tiles
+  int32_t* flag;    // set when a wait of the split ran past its bound (the outputs are then NaN)
   float* ws_m;      // [G + B, 16] per (workgroup, sequence) partial
   float* ws_l;
   float* ws_o;      // [G + B, 16, 512]
@@ -143,7 +144,10 @@ __device__ void plan_tiles(const MlaArgs& a) {
     a.ts[b] = run;
     run += tiles_of(a, b);
   }
-  if (tid == 255) a.ts[B] = part[255];
+  if (tid == 255) {
+    a.ts[B] = part[255];
+    *a.flag = 0;
+  }
 }
 
 // ---------------------------------------------------------------- absorb
@@ -282,14 +286,18 @@ constexpr float kLazyMax = 8.0f;  // log2 headroom of a segment's running max
 //  * ready[p]: items whose share from fetching wave p has landed (raised
 //    after its own vmcnt wait); a computing wave starts item i when both are
 //    past i;
-//  * consumed: +1 per computing wave once it has read item i; a fetching
-//    wave refills item i's buffer (with item i + kRing) only when it reaches
-//    kWaves (i + 1);
-//  * p_ready / p_done: the score waves' P of the k-th tile (bf16 hi and lo,
-//    in one of two LDS buffers) is written (+1 per score wave) and read
-//    (+1 per P.V wave).
-// Every wait polls with a bound: counts that never arrive end the kernel (with
-// wrong results) instead of hanging the device.
+//  * consumed[r]: +1 per computing wave once it has read the item in buffer
+//    r; a fetching wave puts item j there only when it reaches
+//    kWaves (j / kRing), every earlier item of that buffer read by every
+//    computing wave (one count per buffer, not one for the ring: waves of
+//    different roles drift apart, and a sum over the ring would let a fast
+//    wave's reads stand in for a slow wave's);
+//  * p_ready[pb] / p_done[pb]: the score waves' P of the k-th tile (bf16 hi
+//    and lo) goes into LDS buffer pb = k % 2; +1 per score wave once written,
+//    +1 per P.V wave once read, counted per buffer for the same reason.
+// Every wait polls with a bound: counts that never arrive end the kernel
+// instead of hanging the device, and set a flag in the workspace that makes
+// the merge write NaN outputs.
 __device__ __forceinline__ uint32_t lds_load_u32(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
@@ -312,6 +320,11 @@ __device__ __forceinline__ bool wait_at_least(const uint32_t* p, uint32_t target
   return false;
 }
 
+// A wait ran past its bound: the call's outputs become NaN (the merge reads the flag).
+__device__ __forceinline__ void timed_out(const MlaArgs& a) {
+  if ((threadIdx.x & 63) == 0) *a.flag = 1;
+}
+
 template <int DR>
 __global__ __launch_bounds__(64 * (kWaves + kProducers)) void mla_split_kernel(MlaArgs a) {
   using Gm = MlaGeo<DR>;
@@ -329,10 +342,11 @@ __global__ __launch_bounds__(64 * (kWaves + kProducers)) void mla_split_kernel(M
   __shared__ __attribute__((aligned(16))) int32_t tab[kProducers][kTabSlots][64];
   __shared__ int desc[kRing][4];  // item: local tile (-1 q~, -2 none), sequence, last tile of its segment
   __shared__ uint32_t rowmask[kRing][kProducers];
-  __shared__ uint32_t ready[kProducers], consumed, p_ready, p_done;
+  __shared__ uint32_t ready[kProducers], consumed[kRing], p_ready[2], p_done[2];
   if (tid == 0) {
     for (int p2 = 0; p2 < kProducers; ++p2) ready[p2] = 0u;
-    consumed = p_ready = p_done = 0u;
+    for (int r = 0; r < kRing; ++r) consumed[r] = 0u;
+    p_ready[0] = p_ready[1] = p_done[0] = p_done[1] = 0u;
   }
   __syncthreads();  // the counters start at zero (before any load is in flight)
 
@@ -539,8 +553,11 @@ __global__ __launch_bounds__(64 * (kWaves + kProducers)) void mla_split_kernel(M
         compiler_fence();
         if (lane == 0) lds_store_u32(&ready[pw], (uint32_t)(j - kAhead + 1));
       }
-      if (j >= kRing) ok_run = wait_at_least(&consumed, (uint32_t)(kWaves * (j - kRing + 1)));
-      if (!ok_run) break;
+      if (j >= kRing) ok_run = wait_at_least(&consumed[j % kRing], (uint32_t)(kWaves * (j / kRing)));
+      if (!ok_run) {
+        timed_out(a);
+        break;
+      }
       if (dl[0] == -2) {  // item j is past the last one: the end marker in its buffer's slot
         if (pw == 0 && lane == 0) desc[j % kRing][0] = -2;
         break;
@@ -586,7 +603,10 @@ __global__ __launch_bounds__(64 * (kWaves + kProducers)) void mla_split_kernel(M
       bool ok = true;
 #pragma unroll
       for (int p2 = 0; p2 < kProducers; ++p2) ok = ok && wait_at_least(&ready[p2], (uint32_t)(i + 1));
-      if (!ok) break;
+      if (!ok) {
+        timed_out(a);
+        break;
+      }
       const int slot = i % kRing;
       const int lt = uniform(desc[slot][0]);
       if (lt == -2) break;
@@ -600,7 +620,7 @@ __global__ __launch_bounds__(64 * (kWaves + kProducers)) void mla_split_kernel(M
         m_run = -INFINITY;
         l_run = 0.0f;
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // its reads are done: the buffer may be refilled
-        if (lane == 0) lds_add_u32(&consumed, 1u);
+        if (lane == 0) lds_add_u32(&consumed[slot], 1u);
         continue;
       }
       const uint32_t valid = uniform(rowmask[slot][0]) | uniform(rowmask[slot][1]);  // bit r: position r takes part
@@ -614,7 +634,7 @@ __global__ __launch_bounds__(64 * (kWaves + kProducers)) void mla_split_kernel(M
           S[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cop, qb[s], S[rb], 0, 0, 0);
         }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the tile's reads are done
-      if (lane == 0) lds_add_u32(&consumed, 1u);
+      if (lane == 0) lds_add_u32(&consumed[slot], 1u);
       float sc[8];
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
@@ -648,7 +668,10 @@ __global__ __launch_bounds__(64 * (kWaves + kProducers)) void mla_split_kernel(M
       // (li < 8) or its lo part, lo = bf16(p - hi): hi + lo is within 2^-17 of
       // the fp32 p. Lane l writes positions 16 rb + 4 lg .. + 3 (8 bytes each).
       const uint32_t pb = k & 1u;
-      if (k >= 2 && !wait_at_least(&p_done, kPV * (k - 1))) break;  // tile k - 2 has left this buffer
+      if (k >= 2 && !wait_at_least(&p_done[pb], kPV * (k / 2u))) {  // tiles k - 2, k - 4, .. have left this buffer
+        timed_out(a);
+        break;
+      }
       char* prow = pbuf[pb] + qrow * kPRow;
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
@@ -664,7 +687,7 @@ __global__ __launch_bounds__(64 * (kWaves + kProducers)) void mla_split_kernel(M
       if (lane < 8) palpha[pb][8 * sw + lane] = alpha;
       if (lane == 0) praise[pb][sw] = __builtin_amdgcn_ballot_w64(raise) != 0 ? 1 : 0;
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      if (lane == 0) lds_add_u32(&p_ready, 1u);
+      if (lane == 0) lds_add_u32(&p_ready[pb], 1u);
       ++k;
       if (last && lane < 8) {  // the segment's running max and sum of this wave's heads
         const int64_t pslot = (int64_t)w + bb;
@@ -694,7 +717,10 @@ __global__ __launch_bounds__(64 * (kWaves + kProducers)) void mla_split_kernel(M
     bool ok = true;
 #pragma unroll
     for (int p2 = 0; p2 < kProducers; ++p2) ok = ok && wait_at_least(&ready[p2], (uint32_t)(i + 1));
-    if (!ok) break;
+    if (!ok) {
+      timed_out(a);
+      break;
+    }
     const int slot = i % kRing;
     const int lt = uniform(desc[slot][0]);
     if (lt == -2) break;
@@ -703,7 +729,7 @@ __global__ __launch_bounds__(64 * (kWaves + kProducers)) void mla_split_kernel(M
     if (lt == -1) {  // a new segment
 #pragma unroll
       for (int db = 0; db < 4; ++db) acc[db] = f32x16{};
-      if (lane == 0) lds_add_u32(&consumed, 1u);
+      if (lane == 0) lds_add_u32(&consumed[slot], 1u);
       continue;
     }
     const uint32_t valid = uniform(rowmask[slot][0]) | uniform(rowmask[slot][1]);
@@ -724,7 +750,7 @@ __global__ __launch_bounds__(64 * (kWaves + kProducers)) void mla_split_kernel(M
       }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the tile's reads are done: its buffer may be refilled
-    if (lane == 0) lds_add_u32(&consumed, 1u);
+    if (lane == 0) lds_add_u32(&consumed[slot], 1u);
     // C elements of masked positions -> 0 (their slots may hold NaN; their p are 0)
     u32x4 vmask[2];
 #pragma unroll
@@ -735,7 +761,10 @@ __global__ __launch_bounds__(64 * (kWaves + kProducers)) void mla_split_kernel(M
         vmask[ks][q] = (((valid >> p0) & 1u) ? 0xFFFFu : 0u) | (((valid >> (p0 + 1)) & 1u) ? 0xFFFF0000u : 0u);
       }
     const uint32_t pb = k & 1u;
-    if (!wait_at_least(&p_ready, kScore * (k + 1u))) break;
+    if (!wait_at_least(&p_ready[pb], kScore * (k / 2u + 1u))) {  // both score waves' P of tile k
+      timed_out(a);
+      break;
+    }
     // rescale O's rows by their heads' alpha when a score wave raised the max
     if ((uniform(praise[pb][0]) | uniform(praise[pb][1])) != 0) {
       float al[8];  // heads 8 jj + 4 h32 + r: rows 8 j + 4 h32 + r, j = jj, jj + 2
@@ -753,7 +782,7 @@ __global__ __launch_bounds__(64 * (kWaves + kProducers)) void mla_split_kernel(M
     for (int ks = 0; ks < 2; ++ks)
       pa[ks] = *reinterpret_cast<const bf16x8*>(pbuf[pb] + r32 * kPRow + 2 * (16 * ks + 8 * h32));
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if (lane == 0) lds_add_u32(&p_done, 1u);
+    if (lane == 0) lds_add_u32(&p_done[pb], 1u);
     ++k;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
@@ -903,11 +932,13 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(MlaArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) red[(cg * 4 + q) * a.dv + 8 * jg + e] = acc[q][e];
   __syncthreads();
+  const bool failed = uniform(*a.flag) != 0;
   for (int i = tid; i < 4 * a.dv; i += kMergeThreads) {
     const int q = i / a.dv, j = i % a.dv;
     if (b0 + q >= a.num_seqs) continue;
     float o = 0.0f;
     for (int g = 0; g < cgs; ++g) o += red[(g * 4 + q) * a.dv + j];
+    if (failed) o = __builtin_nanf("");
     const int64_t oi = (int64_t)(b0 + q) * a.out_seq_stride + (int64_t)h * a.dv + j;
     if (a.out_f32)
       static_cast<float*>(a.out)[oi] = o;
@@ -918,7 +949,7 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(MlaArgs a) {
 
 struct MlaPlan {
   int row;
-  size_t off_qhi, off_qlo, off_ts, off_m, off_l, off_o, bytes;
+  size_t off_qhi, off_qlo, off_ts, off_flag, off_m, off_l, off_o, bytes;
 };
 
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
@@ -947,6 +978,8 @@ MlaPlan mla_plan(int32_t num_seqs, int32_t rope_dim) {
   off = round256(off + B * kHeads * p.row * 2);
   p.off_ts = off;
   off = round256(off + (B + 1) * 4);
+  p.off_flag = off;
+  off = round256(off + 4);
   p.off_m = off;
   off = round256(off + slots * kHeads * 4);
   p.off_l = off;
@@ -1043,6 +1076,7 @@ extern "C" pa_status pa_mla_decode_attention(void* out, pa_dtype out_dtype, int6
   a.q_hi = reinterpret_cast<uint16_t*>(ws + p.off_qhi);
   a.q_lo = reinterpret_cast<uint16_t*>(ws + p.off_qlo);
   a.ts = reinterpret_cast<int32_t*>(ws + p.off_ts);
+  a.flag = reinterpret_cast<int32_t*>(ws + p.off_flag);
   a.ws_m = reinterpret_cast<float*>(ws + p.off_m);
   a.ws_l = reinterpret_cast<float*>(ws + p.off_l);
   a.ws_o = reinterpret_cast<float*>(ws + p.off_o);
