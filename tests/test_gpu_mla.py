@@ -13,7 +13,8 @@ with and without a RoPE part, block sizes 1, 16, 48, 64, other qk / v widths,
 empty contexts, bad table entries and clamped lengths, NaN in every slot no
 sequence owns, bit-identical output under block relabelling, the full batch-64
 workload on every sequence (one head each), and a decode step whose latent rows
-are first written by concat_and_cache_mla_k."""
+are first written by concat_and_cache_mla_k, and 300 repeated full-size calls
+that must agree bit for bit."""
 import zlib
 
 import numpy as np
@@ -251,3 +252,31 @@ def test_mla_in_a_hip_graph_replays_exactly():
         torch.cuda.synchronize()
         assert torch.equal(out, eager), f"replay {i}"
         del junk
+
+
+def test_repeated_full_size_calls_are_identical_and_finite():
+    """300 calls of the batch-64 workload back to back, ten outputs in flight
+    at a time: the split kernel's waves hand work to each other at their own
+    pace in every call, and the result must not depend on it -- every output
+    bit-identical to the first and finite (a hand-off wait that ran past its
+    bound would make the call's outputs NaN)."""
+    m = pkv()
+    w = workloads.mla_decode_b64()
+    say(f"mla_decode repeated {w['name']}")
+    cache, q_nope, q_rope, w_uk, w_uv = full_size_tensors(w)
+    bt = torch.from_numpy(w["block_tables"]).cuda()
+    ctx = torch.from_numpy(w["context_lens"]).cuda()
+    ws = torch.empty(m.mla_decode_workspace_size(w["num_seqs"], H, w["qk_nope_dim"], w["rope_dim"], DC, w["v_dim"],
+                                                 bt.shape[1], w["block_size"]), dtype=torch.uint8, device="cuda")
+    outs = torch.empty((10, w["num_seqs"], H, w["v_dim"]), dtype=torch.float32, device="cuda")
+    first = None
+    for rnd in range(30):
+        for i in range(10):
+            m.mla_decode_attention(outs[i], q_nope, q_rope, w_uk, w_uv, cache, bt, ctx, w["softmax_scale"],
+                                   workspace=ws)
+        torch.cuda.synchronize()
+        assert bool(torch.isfinite(outs).all()), f"round {rnd}: non-finite output"
+        if first is None:
+            first = outs[0].clone()
+        for i in range(10):
+            assert torch.equal(outs[i], first), f"round {rnd} call {i} differs from the first call"
