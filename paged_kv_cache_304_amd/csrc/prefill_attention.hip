@@ -56,7 +56,6 @@ typedef __bf16 bf16x8 __attribute__((__vector_size__(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // two waves per SIMD (256 registers each)
 #define PA_PREFILL_OCCUPANCY __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -131,23 +130,22 @@ struct PfArgs {
 // base + lane * (bytes per lane) and needs no per-read address arithmetic:
 //  * K: read (kb, s) -- rows 16kb + l%16, dims 32s + 8(l/16) .. +7 -- is the
 //    1 KB at ((kb * KS + s) * 64 + l) * 16.
-//  * V: transposing read (ks, cb, half) of the 32x32x16 P.V -- lane
-//    (m, g) = (l%16, l/16) supplies row 16ks + 8(g/2) + 4half + m/4, dims
-//    32cb + 16(g%2) + 4(m%4) .. +3 -- is the 512 B at
-//    ((ks * CB32 + cb) * 2 + half) * 512 + 8 l; its 16-byte chunk q holds row
-//    16ks + 8(q/16) + 4half + (q%8)/2, dims 32cb + 16((q/8)%2) + 8(q%2) .. +7.
+//  * V: transposing read (st, cb, half) -- lane (m, g) = (l%16, l/16) needs
+//    row 32st + 16half + 4g + m/4, dims 16cb + 4(m%4) .. +3 -- is the 512 B at
+//    ((st * CB + cb) * 2 + half) * 512 + 8 l; its 16-byte chunk q holds row
+//    32st + 16half + 4(q/8) + (q%8)/2, dims 8(2cb + q%2) .. +7.
 template <int D>
 struct Geo {
   static constexpr int RB = D * 2;                 // bytes per cache row of one head
   static constexpr int TB = kKeys * RB;            // bytes per K (or V) tile
   static constexpr int KS = D / 32;                // MFMA steps over the head dim
-  static constexpr int CB32 = D / 32;              // 32-column output blocks of P.V
+  static constexpr int CB = D / 16;                // 16-column output blocks
   static constexpr int TI = TB / 1024;             // 1 KB wave loads per K (or V) tile
   static constexpr int IPW = 2 * TI / kWaves;      // ... per wave and tile, K and V together
   static_assert(TB % 1024 == 0 && (2 * TI) % kWaves == 0, "tile / wave split");
-  static_assert(TI == (kKeys / 16) * KS && TI == (kKeys / 16) * CB32, "reader-ordered layout");
+  static_assert(TI == (kKeys / 16) * KS && TI == (kKeys / 32) * CB, "reader-ordered layout");
   __device__ static int k_off(int kb, int s, int lane) { return ((kb * KS + s) * 64 + lane) * 16; }
-  __device__ static int v_off(int ks, int cb, int half, int lane) { return ((ks * CB32 + cb) * 2 + half) * 512 + 8 * lane; }
+  __device__ static int v_off(int st, int cb, int half, int lane) { return ((st * CB + cb) * 2 + half) * 512 + 8 * lane; }
 };
 
 // Max over the lanes l, l^16, l^32 and l^48 (the four lanes that hold one
@@ -183,7 +181,7 @@ template <int D, int G, bool kFp8>
 __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma_kernel(PfArgs a) {
   using Gm = Geo<D>;
   using G8 = Geo8<D>;
-  constexpr int KS = Gm::KS;
+  constexpr int KS = Gm::KS, CB = Gm::CB;
   constexpr int QT = kRows / G;  // query tokens per workgroup
   const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, lg = lane >> 4;
   const int wave = uniform(tid >> 6);
@@ -439,9 +437,9 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
     } else {            // V regions 2(ii - TI) and 2(ii - TI) + 1
       const int region = 2 * (ii - Gm::TI) + (lane >> 5);
       const int q = lane & 31;
-      const int ks = region / (2 * Gm::CB32), cb = (region >> 1) % Gm::CB32, half = region & 1;
-      row = 16 * ks + 8 * (q >> 4) + 4 * half + ((q & 7) >> 1);
-      el = 32 * cb + 16 * ((q >> 3) & 1) + 8 * (q & 1);
+      const int st = region / (2 * Gm::CB), cb = (region >> 1) % Gm::CB, half = region & 1;
+      row = 32 * st + 16 * half + 4 * (q >> 3) + ((q & 7) >> 1);
+      el = 8 * (2 * cb + (q & 1));
     }
     lane_kb[i] = row >> 4;
     lane_el[i] = (int64_t)(row & 15) * row_el + (int64_t)g * D + el;
@@ -461,8 +459,7 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
   // fp8: this lane's staged chunks of tile t (landed) -> the bf16 operand tiles.
   // K chunk (row r, dims 16c..+15) -> reads (kb, s) = (r/16, c/2), lanes
   // 16 (2(c%2)) + r%16 and 16 (2(c%2) + 1) + r%16; V chunk -> 16-byte slots q0,
-  // q0 + 1 of read (ks, cb, half) = (r/16, c/2, (r%8)/4),
-  // q0 = 16 ((r%16)/8) + 8 (c%2) + 2 (r%4).
+  // q0 + 1 of block (cb, half) = (c, r/16), q0 = 8 ((r%16)/4) + 2 (r%4).
   auto convert = [&](int t) {
     if constexpr (kFp8) {
 #pragma unroll
@@ -488,8 +485,8 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
           *reinterpret_cast<u32x4*>(bt + Gm::k_off(kb, s, l0)) = lo8;
           *reinterpret_cast<u32x4*>(bt + Gm::k_off(kb, s, l0 + 16)) = hi8;
         } else {
-          const int q0 = 16 * ((r & 15) >> 3) + 8 * (c & 1) + 2 * (r & 3);
-          char* blk = bt + (((r >> 4) * Gm::CB32 + (c >> 1)) * 2 + ((r & 7) >> 2)) * 512 + 16 * q0;
+          const int q0 = 8 * ((r & 15) >> 2) + 2 * (r & 3);
+          char* blk = bt + ((0 * CB + c) * 2 + (r >> 4)) * 512 + 16 * q0;
           *reinterpret_cast<u32x4*>(blk) = lo8;
           *reinterpret_cast<u32x4*>(blk + 16) = hi8;
         }
@@ -498,13 +495,11 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
   };
 
   float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.0f, 0.0f};
-  // O of the wave's 32 rows on v_mfma_f32_32x32x16_bf16: lane l holds column
-  // 32cb + l%32 at rows 8(v/4) + 4(l/32) + v%4, v = 0..15
-  constexpr int CB32 = Gm::CB32;
-  const int h32 = lane >> 5;
-  f32x16 acc[CB32];
+  f32x4 acc[2][CB];
 #pragma unroll
-  for (int cb = 0; cb < CB32; ++cb) acc[cb] = f32x16{};
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
   // The tile step in three parts. qk: S^T of a tile (sc[rb][kb] holds keys
   // 16kb + 4lg + r of row (rb, li)). softmax: the online-softmax update of
@@ -604,73 +599,56 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
     }
 #endif
   };
-  // (Row R of the wave -- block R/16, lane row R%16 -- has its alpha in lane R%16.)
   auto rescale = [&](const float (&alpha)[2], const bool (&moved)[2]) {
-    if ((__builtin_amdgcn_ballot_w64(moved[0]) | __builtin_amdgcn_ballot_w64(moved[1])) != 0) {
-      float al[16];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) al[v] = bcast_lane(alpha[v >> 3], 8 * ((v >> 2) & 1) + 4 * h32 + (v & 3));
+    for (int rb = 0; rb < 2; ++rb) {
+      if (__builtin_amdgcn_ballot_w64(moved[rb]) != 0) {
+        float al[4];
 #pragma unroll
-      for (int cb = 0; cb < CB32; ++cb)
+        for (int r = 0; r < 4; ++r) al[r] = bcast_lane(alpha[rb], (lane & 48) + 4 * lg + r);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[cb][v] *= al[v];
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[rb][cb][r] *= al[r];
+      }
     }
   };
-  // O += P V on v_mfma_f32_32x32x16_bf16, two steps of 16 keys. P's A operand
-  // (lane l: row 16(g%2) + li of the wave, g = l/16, keys 16ks + 8(g/2) + e)
-  // comes from the score layout by one cross-row swap: lanes of rows 2j and
-  // 2j + 1 trade the block the other one keeps (v_permlane16_swap), so row
-  // 2j + rb ends up with block rb's keys 16ks + 8j + 0..3 (its own) and
-  // + 4..7 (its partner's). V's operand: two transposing reads per (step,
-  // column block), rows 16ks + 8(l/32) + 0..3 and + 4..7 of column 32cb + l%32.
-  static_assert(kKeys == 32, "P.V steps: two of 16 keys");
+  // O += P V, V's operand by transposing reads (lane m of a 16-lane group
+  // reads row kbase + m/4, columns 16cb + 4(m%4) .. +3, kbase = 32st + 4g,
+  // then + 16); the two reads are the operand's low and high halves.
   auto pv = [&](int kt, int okbits, const bf16x8 (&pop)[2][kSt], const bf16x8 (&plo)[2][kSt],
                 auto mask_tag) {
     constexpr bool kMask = decltype(mask_tag)::value;
     const char* vl = vtile(kt);
     const int key0 = kt * kKeys;
-    const u32x4 h0 = __builtin_bit_cast(u32x4, pop[0][0]), h1 = __builtin_bit_cast(u32x4, pop[1][0]);
-    const u32x4 q0 = __builtin_bit_cast(u32x4, plo[0][0]), q1 = __builtin_bit_cast(u32x4, plo[1][0]);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      uint32_t ah[4], aq[4];
-#pragma unroll
-      for (int d = 0; d < 2; ++d) {
-        const auto sh = __builtin_amdgcn_permlane16_swap(h0[2 * ks + d], h1[2 * ks + d], false, false);
-        const auto sq = __builtin_amdgcn_permlane16_swap(q0[2 * ks + d], q1[2 * ks + d], false, false);
-        ah[d] = sh[0];
-        ah[2 + d] = sh[1];
-        aq[d] = sq[0];
-        aq[2 + d] = sq[1];
-      }
-      const bf16x8 pa = __builtin_bit_cast(bf16x8, u32x4{ah[0], ah[1], ah[2], ah[3]});
-      const bf16x8 pq = __builtin_bit_cast(bf16x8, u32x4{aq[0], aq[1], aq[2], aq[3]});
+    for (int st = 0; st < kSt; ++st) {
       u32x4 vmask = {~0u, ~0u, ~0u, ~0u};  // V elements of masked-out keys -> 0
       if constexpr (kMask) {
         uint32_t m16[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int key = key0 + 16 * ks + 8 * h32 + e;
-          m16[e] = (((okbits >> ks) & 1) && key < L) ? 0xFFFFu : 0u;
+        for (int j = 0; j < 8; ++j) {
+          const int kb = 2 * st + (j >> 2);
+          const int key = key0 + 16 * kb + 4 * lg + (j & 3);
+          m16[j] = (((okbits >> kb) & 1) && key < L) ? 0xFFFFu : 0u;
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) vmask[i] = m16[2 * i] | (m16[2 * i + 1] << 16);
       }
-      bf16x8 vop[CB32];
 #pragma unroll
-      for (int cb = 0; cb < CB32; ++cb) {
+      for (int cb = 0; cb < CB; ++cb) {
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(vl + Gm::v_off(ks, cb, 0, lane)));
+            (__attribute__((address_space(3))) i16x4*)(vl + Gm::v_off(st, cb, 0, lane)));
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(vl + Gm::v_off(ks, cb, 1, lane)));
+            (__attribute__((address_space(3))) i16x4*)(vl + Gm::v_off(st, cb, 1, lane)));
         u32x4 w = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         if constexpr (kMask) w &= vmask;
-        vop[cb] = __builtin_bit_cast(bf16x8, w);
+        const bf16x8 vop = __builtin_bit_cast(bf16x8, w);
+        acc[0][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pop[0][st], vop, acc[0][cb], 0, 0, 0);
+        acc[1][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pop[1][st], vop, acc[1][cb], 0, 0, 0);
+        acc[0][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo[0][st], vop, acc[0][cb], 0, 0, 0);
+        acc[1][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo[1][st], vop, acc[1][cb], 0, 0, 0);
       }
-#pragma unroll
-      for (int cb = 0; cb < CB32; ++cb) acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, vop[cb], acc[cb], 0, 0, 0);
-#pragma unroll
-      for (int cb = 0; cb < CB32; ++cb) acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pq, vop[cb], acc[cb], 0, 0, 0);
     }
   };
 
@@ -786,32 +764,34 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
   }
 
   // ---- finish: sum the row sums over the four lane groups, normalise, store
-  // (the grid is launched with 64 * kWaves threads per workgroup). Row R of
-  // the wave is block R/16's lane row R%16.
-  float lsum[2];
+  // (the grid is launched with 64 * kWaves threads per workgroup)
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
     float l = l_run[rb];
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
-    lsum[rb] = l;
-  }
+    float inv[4];
+    int tok[4], head[4];
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int R = 8 * (v >> 2) + 4 * h32 + (v & 3);
-    const float lr = bcast_lane(lsum[v >> 3], R & 15);
-    const float inv = lr > 0.0f ? vs / lr : 0.0f;
-    const int Rw = wave * kRowsPerWave + R;
-    const int tok = tq0 + Rw / G, head = g * G + Rw % G;
-    if (tok >= tq_end) continue;
-    const int64_t base = (int64_t)(row0 + tok) * a.out_tok_stride + (int64_t)head * D + (lane & 31);
+    for (int r = 0; r < 4; ++r) {
+      const float lr = bcast_lane(l, (lane & 48) + 4 * lg + r);
+      inv[r] = lr > 0.0f ? vs / lr : 0.0f;
+      const int R = wave * kRowsPerWave + 16 * rb + 4 * lg + r;
+      tok[r] = tq0 + R / G;
+      head[r] = g * G + R % G;
+    }
 #pragma unroll
-    for (int cb = 0; cb < CB32; ++cb) {
-      const float o = acc[cb][v] * inv;
-      if (a.out_f32)
-        static_cast<float*>(a.out)[base + 32 * cb] = o;
-      else
-        static_cast<uint16_t*>(a.out)[base + 32 * cb] = (uint16_t)f32_to_bf16(o);
+    for (int r = 0; r < 4; ++r) {
+      if (tok[r] >= tq_end) continue;
+      const int64_t base = (int64_t)(row0 + tok[r]) * a.out_tok_stride + (int64_t)head[r] * D + li;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const float o = acc[rb][cb][r] * inv[r];
+        if (a.out_f32)
+          static_cast<float*>(a.out)[base + 16 * cb] = o;
+        else
+          static_cast<uint16_t*>(a.out)[base + 16 * cb] = (uint16_t)f32_to_bf16(o);
+      }
     }
   }
 }
