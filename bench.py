@@ -11,7 +11,10 @@ attention must read (2 * sum(ctx) * H_KV * d_h * 2 B) divided by the measured
 time per step (write + attention). ``roofline`` is for the dominant kernel
 (decode attention) against MI355X's 8 TB/s; ``cpu_baseline`` is the CPU oracle
 timed on this host on the same step; ``bulk_cache_write`` is the 32,768-token
-bf16 -> fp8 cache write measured in the same run with a cold Infinity Cache.
+bf16 -> fp8 cache write measured in the same run with a cold Infinity Cache;
+``fp8_decode_b256`` and ``mla_k_write`` the other reported configurations, and
+``prefill_chunks`` and ``mla_decode_b64`` the chunked-prefill and MLA latent
+decode workloads, all timed in the same process.
 
 Other workloads (parity-test configurations, for measurement only):
 ``--workload decode_fp8_b256 | decode_b64_tp2 | decode_b64_bs8 | prefill_fp8 | mla_concat_swa | mla_fused |
@@ -338,6 +341,12 @@ def run_decode(args, torch, pkv, workloads, w, metric_name):
         torch.cuda.empty_cache()
         res["mla_k_write"] = measure_mla_k_write(args, torch, pkv, workloads)
         torch.cuda.empty_cache()
+        # the hot path's next rows, timed in the same process: chunked prefill
+        # and MLA latent decode
+        res["prefill_chunks"] = measure_prefill_chunks(args, torch, pkv, workloads)
+        torch.cuda.empty_cache()
+        res["mla_decode_b64"] = measure_mla_decode(args, torch, pkv, workloads)
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         import oracle
         res["cpu_baseline"] = cpu_baseline_decode(torch, t, w, oracle)
@@ -603,7 +612,9 @@ def prefill_flops(w) -> int:
     return total * w["num_q_heads"] * w["head_size"] * 4
 
 
-def run_prefill_chunks(args, torch, pkv, workloads, fp8=False):
+def prefill_setup(torch, pkv, workloads, fp8=False):
+    """Tensors of the chunked-prefill workload (bf16 or the same over an fp8 pool)
+    and one call of it."""
     w = workloads.prefill_chunks()
     B, HQ, HKV, D, BS, NB, T = (w["num_seqs"], w["num_q_heads"], w["num_kv_heads"], w["head_size"],
                                 w["block_size"], w["num_blocks"], w["num_tokens"])
@@ -626,6 +637,36 @@ def run_prefill_chunks(args, torch, pkv, workloads, fp8=False):
     def step():
         pkv.prefill_attention(out, q, cu, kc, vc, bt, cl, w["softmax_scale"], ks, vs)
 
+    return w, step, q, kc, vc
+
+
+def measure_prefill_chunks(args, torch, pkv, workloads):
+    """The bf16 chunked-prefill workload (16 sequences, a 512-token chunk each),
+    K calls back to back on HIP events: rate against the dense bf16 MFMA peak."""
+    w, step, q, kc, vc = prefill_setup(torch, pkv, workloads)
+    stream = torch.cuda.current_stream()
+    for _ in range(max(5, min(args.warmup, 20))):
+        step()
+    tm = Timer(torch, stream)
+    tm.start()
+    for _ in range(args.steps):
+        step()
+    tm.stop()
+    torch.cuda.synchronize()
+    ms = tm.mean_ms() / args.steps
+    flops = prefill_flops(w)
+    tflops = flops / (ms * 1e-3) / 1e12
+    del step, q, kc, vc
+    return {"workload": w["name"], "ms": round(ms, 5), "flops": flops, "TFLOPs": round(tflops, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS, "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "tokens_per_s": round(w["num_tokens"] / (ms * 1e-3), 1),
+            "traffic": traffic_from_profiles("prefill_attention", w["name"])}
+
+
+def run_prefill_chunks(args, torch, pkv, workloads, fp8=False):
+    w, step, q, kc, vc = prefill_setup(torch, pkv, workloads, fp8)
+    B, HQ, HKV, D, BS, T = (w["num_seqs"], w["num_q_heads"], w["num_kv_heads"], w["head_size"],
+                            w["block_size"], w["num_tokens"])
     flops = prefill_flops(w)
     kv_bytes = int(2 * int(w["context_lens"].astype(np.int64).sum()) * HKV * D * (1 if fp8 else 2))
     stream = torch.cuda.current_stream()
@@ -906,10 +947,9 @@ def mla_bytes(w, grid: int = 256) -> dict:
                      + 2 * plan + out)}
 
 
-def run_mla_decode(args, torch, pkv, workloads):
-    """MLA decode step over a latent paged cache (synthetic DeepSeek-V2-Lite shapes):
-    the batch's new latent rows written with concat_and_cache_mla_k (one 'head'),
-    then pa_mla_decode_attention."""
+def mla_setup(torch, pkv, workloads):
+    """Tensors of the batch-64 MLA decode workload, its latent write and its
+    attention call."""
     w = workloads.mla_decode_b64()
     B, H, QK, R, DC, DV = (w["num_seqs"], w["num_heads"], w["qk_nope_dim"], w["rope_dim"],
                            w["kv_lora_rank"], w["v_dim"])
@@ -928,7 +968,6 @@ def run_mla_decode(args, torch, pkv, workloads):
     ws = torch.zeros(pkv.mla_decode_workspace_size(B, H, QK, R, DC, DV, bt.shape[1], BS), dtype=torch.uint8,
                      device="cuda")
     cache4 = cache.view(NB, BS, 1, DC + R)
-    stream = torch.cuda.current_stream()
 
     def write():
         pkv.concat_and_cache_mla_k(new_c, new_r, cache4, slots)
@@ -936,6 +975,49 @@ def run_mla_decode(args, torch, pkv, workloads):
     def attend():
         pkv.mla_decode_attention(out, q_nope, q_rope, w_uk, w_uv, cache, bt, cl, w["softmax_scale"],
                                  workspace=ws)
+
+    return w, write, attend, (cache, q_nope, q_rope, w_uk, w_uv)
+
+
+def measure_mla_decode(args, torch, pkv, workloads):
+    """The batch-64 MLA latent decode: K attention calls back to back on HIP
+    events (absorb + split + merge; the roofline's launches) and K whole steps
+    (latent write + attention)."""
+    w, write, attend, tensors = mla_setup(torch, pkv, workloads)
+    stream = torch.cuda.current_stream()
+    for _ in range(max(5, min(args.warmup, 20))):
+        write()
+        attend()
+    ta, ts = Timer(torch, stream), Timer(torch, stream)
+    ta.start()
+    for _ in range(args.steps):
+        attend()
+    ta.stop()
+    ts.start()
+    for _ in range(args.steps):
+        write()
+        attend()
+    ts.stop()
+    torch.cuda.synchronize()
+    ms, step_ms = ta.mean_ms() / args.steps, ts.mean_ms() / args.steps
+    nb = mla_bytes(w, grid=min(256, torch.cuda.get_device_properties(0).multi_processor_count))
+    gbps = nb["algorithmic"] / (ms * 1e-3) / 1e9
+    del write, attend, tensors
+    return {"workload": w["name"], "ms": round(ms, 5), "bytes": nb["algorithmic"], "GBps": round(gbps, 2),
+            "frac": round(gbps / HBM_PEAK_GBPS, 4), "bytes_with_workspace": nb["call"],
+            "step_ms": round(step_ms, 5), "tokens_per_s": round(w["num_seqs"] / (step_ms * 1e-3), 1),
+            "traffic": traffic_from_profiles("mla_decode", w["name"])}
+
+
+def run_mla_decode(args, torch, pkv, workloads):
+    """MLA decode step over a latent paged cache (synthetic DeepSeek-V2-Lite shapes):
+    the batch's new latent rows written with concat_and_cache_mla_k (one 'head'),
+    then pa_mla_decode_attention."""
+    w, write, attend, (cache, q_nope, q_rope, w_uk, w_uv) = mla_setup(torch, pkv, workloads)
+    B, H, QK, R, DC, DV = (w["num_seqs"], w["num_heads"], w["qk_nope_dim"], w["rope_dim"],
+                           w["kv_lora_rank"], w["v_dim"])
+    BS, NB = w["block_size"], w["num_blocks"]
+    stream = torch.cuda.current_stream()
 
     if args.profile_steps:
         copy_calibration(torch, pkv)
