@@ -806,11 +806,10 @@ __global__ __launch_bounds__(64 * (kWaves + kProducers)) void mla_split_kernel(M
 
 // ---------------------------------------------------------------- merge
 // grid (16 heads, ceil(B / 4)), 8 waves: the partials of each of 4 sequences
-// combined into o~ [512] (normalised), then o = o~ W_UV,h. Once the tile plan
-// is read, every load the workgroup needs goes out in one round: the
-// partials' maxima and sums, their first kMergeBatch outputs, and behind them
-// this thread's first kMergeW rows of W_UV,h (waiting for the partials leaves
-// those in flight). Wave w combines sequence b0 + w % 4 over latent dims
+// combined into o~ [512] (normalised), then o = o~ W_UV,h. This thread's first
+// kMergeW rows of W_UV,h are loaded first; once the tile plan is read (scalar
+// loads), the partials' maxima, sums and first kMergeBatch outputs go out in
+// one round. Wave w combines sequence b0 + w % 4 over latent dims
 // 256 (w / 4) + 4 lane .. + 3; thread (jg, cg) of the product takes 8 output
 // dims 8 jg .. and latent rows cg * rows .., and the row groups meet in LDS.
 constexpr int kMergeThreads = 512;
@@ -830,13 +829,21 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(MlaArgs a) {
   const int h = blockIdx.x, b0 = 4 * blockIdx.y, tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = uniform(tid >> 6);
   __shared__ __attribute__((aligned(16))) float ot[4][kDC];
   __shared__ float red[4 * 8 * kMergeThreads];  // [cg][4][dv]: cgs * dv = 8 * kMergeThreads
   const int jgs = a.dv / 8, cgs = kMergeThreads / jgs, rows = kDC / cgs;
   const int jg = tid % jgs, cg = tid / jgs;
   const int64_t wrow = (int64_t)kHeads * a.dv;
   const uint16_t* wbase = static_cast<const uint16_t*>(a.w_uv) + (int64_t)h * a.dv + 8 * jg + (int64_t)cg * rows * wrow;
+
+  // this thread's first rows of W_UV,h: they need nothing the split wrote, so
+  // they go out first (the plan below comes by scalar loads, which do not wait
+  // behind them)
+  u32x4 wv[kMergeW];
+#pragma unroll
+  for (int r = 0; r < kMergeW; ++r)
+    wv[r] = r < rows ? *reinterpret_cast<const u32x4*>(wbase + (int64_t)r * wrow) : u32x4{0u, 0u, 0u, 0u};
 
   // ---- sequence b0 + bb's partials sit in slots w + b of the workgroups w that served its tiles
   const int bb = wave & 3, hd = wave >> 2;
@@ -866,10 +873,6 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(MlaArgs a) {
   for (int u = 0; u < kMergeBatch; ++u)  // (n is uniform: no load past the count)
     x[u] = u < n ? *reinterpret_cast<const f32x4*>(a.ws_o + (((int64_t)p0 + u) * kHeads + h) * kDC + c4)
                  : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  u32x4 wv[kMergeW];
-#pragma unroll
-  for (int r = 0; r < kMergeW; ++r)
-    wv[r] = r < rows ? *reinterpret_cast<const u32x4*>(wbase + (int64_t)r * wrow) : u32x4{0u, 0u, 0u, 0u};
 
   // ---- weights 2^(m_s - M), the sum L of their l_s, and o~ = sum_s w_s o_s / L
   float M = ms;
