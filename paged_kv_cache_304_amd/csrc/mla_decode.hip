@@ -181,6 +181,19 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(MlaArgs a, int row) {
     wa[s] = *reinterpret_cast<const u32x4*>(wr + jc);
     qb[s] = *reinterpret_cast<const u32x4*>(qr + jc);
   }
+  // the RoPE part (latent block 0 only; 16 * dr <= 1024 values), loaded in the
+  // same round as the operands above, before any store
+  float xr[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  const int drr = a.dr > 0 ? a.dr : 1;
+  if (blockIdx.y == 0) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = tid + 256 * u;
+      const int bb = b0 + i / drr, r = i % drr;
+      if (i < 16 * a.dr && bb < a.num_seqs)
+        xr[u] = load1<Ty::BF16>(a.q_rope, (int64_t)bb * a.qr_seq_stride + (int64_t)h * a.dr + r);
+    }
+  }
 #pragma unroll
   for (int s = 0; s < kMaxSteps; ++s) {
     const bool in = 32 * s + 8 * lg < a.qk;
@@ -197,22 +210,14 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(MlaArgs a, int row) {
     *reinterpret_cast<u32x2*>(a.q_hi + base) = u32x2{hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16)};
     *reinterpret_cast<u32x2*>(a.q_lo + base) = u32x2{lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16)};
   }
-  if (blockIdx.y == 0) {  // the RoPE part: scaled and split as it is (16 * dr <= 1024 values)
-    float x[4];
+  if (blockIdx.y == 0) {  // the RoPE part: scaled and split as it is
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int i = tid + 256 * u;
-      const int bb = b0 + i / (a.dr > 0 ? a.dr : 1), r = i % (a.dr > 0 ? a.dr : 1);
-      const bool ok = i < 16 * a.dr && bb < a.num_seqs;
-      x[u] = ok ? load1<Ty::BF16>(a.q_rope, (int64_t)bb * a.qr_seq_stride + (int64_t)h * a.dr + r) : 0.0f;
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = tid + 256 * u;
-      const int bb = b0 + i / (a.dr > 0 ? a.dr : 1), r = i % (a.dr > 0 ? a.dr : 1);
+      const int bb = b0 + i / drr, r = i % drr;
       if (!(i < 16 * a.dr && bb < a.num_seqs)) continue;
       uint16_t hi, lo;
-      split_hi_lo(x[u] * a.scale_log2, hi, lo);
+      split_hi_lo(xr[u] * a.scale_log2, hi, lo);
       const int64_t base = ((int64_t)bb * kHeads + h) * row + kDC;
       a.q_hi[base + r] = hi;
       a.q_lo[base + r] = lo;

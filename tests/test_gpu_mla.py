@@ -99,6 +99,11 @@ CASES = [
     # narrow values: each merge thread's slice of W_UV is 2 (v8) or 4 (v16) latent rows
     ("qk16 v8", [70, 3, 300], 64, 16, 8, 16),
     ("qk24 v16", [129, 1], 0, 24, 16, 16),
+    # more than 64 sequences: the split's segment set-up searches the tile plan
+    ("B65 one past a single round of set-up loads", [(37 * i) % 200 + 1 for i in range(65)], 64, 128, 128, 16),
+    # on 256 compute units the first workgroup's two tiles are sequence 0's and
+    # sequence 71's, 71 entries apart: its list of segments is refilled
+    ("B73 a refilled segment list", [1] + [0] * 70 + [1, 9600], 64, 128, 128, 16),
 ]
 
 
