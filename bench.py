@@ -14,7 +14,8 @@ timed on this host on the same step; ``bulk_cache_write`` is the 32,768-token
 bf16 -> fp8 cache write measured in the same run with a cold Infinity Cache;
 ``fp8_decode_b256`` and ``mla_k_write`` the other reported configurations, and
 ``prefill_chunks`` and ``mla_decode_b64`` the chunked-prefill and MLA latent
-decode workloads, all timed in the same process.
+decode workloads, all timed in the same process, each after at least 100 ms of its
+own untimed calls.
 
 Other workloads (parity-test configurations, for measurement only):
 ``--workload decode_fp8_b256 | decode_b64_tp2 | decode_b64_bs8 | prefill_fp8 | mla_concat_swa | mla_fused |
@@ -93,6 +94,25 @@ def gpu_spin_up(torch, pkv, min_ms: float = 200.0):
             pkv.hbm_read(buf, sink)
         torch.cuda.synchronize()
     del buf, sink
+
+
+SETTLE_MS = 100.0
+
+
+def settle(torch, call, min_calls: int, min_ms: float = SETTLE_MS) -> int:
+    """Untimed calls call(i) of one workload, at least min_calls and at least min_ms
+    of wall time, before its timed calls: the clocks ramp over the first ~30 ms of a
+    new kind of work (chunked-prefill calls measured 352 -> 237 us over their first
+    120 calls, and the same again after 2 s idle), so a short warm-up would time
+    the ramp, not the kernel. Returns the number of calls made."""
+    n, t0 = 0, time.perf_counter()
+    while True:
+        for _ in range(8):
+            call(n)
+            n += 1
+        torch.cuda.synchronize()
+        if n >= min_calls and (time.perf_counter() - t0) * 1e3 >= min_ms:
+            return n
 
 
 def cpu_model() -> str:
@@ -360,8 +380,7 @@ def measure_fp8_decode(args, torch, pkv, workloads):
     w = workloads.mixed_decode_fp8()
     t = setup_decode(torch, pkv, workloads, w)
     stream = torch.cuda.current_stream()
-    for _ in range(max(8, args.warmup)):
-        decode_attn(pkv, t, w)
+    settle(torch, lambda i: decode_attn(pkv, t, w), max(8, args.warmup))
     ta, ts = Timer(torch, stream), Timer(torch, stream)
     ta.start()
     for _ in range(args.steps):
@@ -392,8 +411,7 @@ def measure_mla_k_write(args, torch, pkv, workloads):
     out = {}
     for label, builder in (("unfused", mla_unfused_step), ("fused", mla_fused_step)):
         step, nbytes, kernel, name, T = builder(torch, pkv, workloads)
-        for _ in range(max(3, min(args.warmup, 10))):
-            step()
+        settle(torch, lambda i: step(), max(3, min(args.warmup, 10)))
         tm = Timer(torch, stream)
         tm.start()
         for _ in range(args.steps):
@@ -516,8 +534,7 @@ def measure_bulk_write(args, torch, pkv, workloads):
     back to back rotating over the four sets (cold Infinity Cache)."""
     call, nbytes, T = bulk_write_setup(torch, pkv, workloads)
     stream = torch.cuda.current_stream()
-    for i in range(max(8, args.warmup)):
-        call(i)
+    settle(torch, call, max(8, args.warmup))
     tm = Timer(torch, stream)
     tm.start()
     for i in range(args.steps):
@@ -645,8 +662,7 @@ def measure_prefill_chunks(args, torch, pkv, workloads):
     K calls back to back on HIP events: rate against the dense bf16 MFMA peak."""
     w, step, q, kc, vc = prefill_setup(torch, pkv, workloads)
     stream = torch.cuda.current_stream()
-    for _ in range(max(5, min(args.warmup, 20))):
-        step()
+    settle(torch, lambda i: step(), max(5, min(args.warmup, 20)))
     tm = Timer(torch, stream)
     tm.start()
     for _ in range(args.steps):
@@ -985,9 +1001,10 @@ def measure_mla_decode(args, torch, pkv, workloads):
     (latent write + attention)."""
     w, write, attend, tensors = mla_setup(torch, pkv, workloads)
     stream = torch.cuda.current_stream()
-    for _ in range(max(5, min(args.warmup, 20))):
+    def both(i):
         write()
         attend()
+    settle(torch, both, max(5, min(args.warmup, 20)))
     ta, ts = Timer(torch, stream), Timer(torch, stream)
     ta.start()
     for _ in range(args.steps):
