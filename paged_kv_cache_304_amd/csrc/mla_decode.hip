@@ -123,29 +123,37 @@ __device__ __forceinline__ int tile_owner(int t, int T, int G) {
 }
 __device__ __forceinline__ int tiles_of(const MlaArgs& a, int b) { return (clamp_ctx(a, b) + kTile - 1) / kTile; }
 
-// ts[b] = tiles of sequences 0 .. b - 1 (ts[B] = T), by one workgroup of 256.
+// ts[b] = tiles of sequences 0 .. b - 1 (ts[B] = T), by one workgroup of 256:
+// each thread sums a run of sequences, a lane scan per wave and the four wave
+// totals give each run's first tile (one workgroup barrier).
 __device__ void plan_tiles(const MlaArgs& a) {
-  __shared__ int part[256];
-  const int tid = threadIdx.x, B = a.num_seqs;
+  __shared__ int wsum[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, B = a.num_seqs;
   const int per = (B + 255) / 256;
   const int lo = min(B, tid * per), hi = min(B, lo + per);
   int mine = 0;
   for (int b = lo; b < hi; ++b) mine += tiles_of(a, b);
-  part[tid] = mine;
+  int incl = mine;  // inclusive prefix over this wave's lanes
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, (unsigned)o, 64);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) wsum[wave] = incl;
   __syncthreads();
-  for (int o = 1; o < 256; o <<= 1) {  // inclusive prefix over the threads
-    const int v = tid >= o ? part[tid - o] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
+  int run = incl - mine;
+  for (int w = 0; w < wave; ++w) run += wsum[w];
+  if (per == 1) {  // (B <= 256: the run is one sequence, its count already summed)
+    if (lo < hi) a.ts[lo] = run;
+    run += mine;
+  } else {
+    for (int b = lo; b < hi; ++b) {
+      a.ts[b] = run;
+      run += tiles_of(a, b);
+    }
   }
-  int run = part[tid] - mine;
-  for (int b = lo; b < hi; ++b) {
-    a.ts[b] = run;
-    run += tiles_of(a, b);
-  }
-  if (tid == 255) {
-    a.ts[B] = part[255];
+  if (tid == 255) {  // the last run ends at T
+    a.ts[B] = run;
     *a.flag = 0;
   }
 }

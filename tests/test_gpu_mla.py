@@ -104,6 +104,8 @@ CASES = [
     # on 256 compute units the first workgroup's two tiles are sequence 0's and
     # sequence 71's, 71 entries apart: its list of segments is refilled
     ("B73 a refilled segment list", [1] + [0] * 70 + [1, 9600], 64, 128, 128, 16),
+    # more than 256 sequences: each thread of the tile plan sums a run of two
+    ("B300 two sequences per plan thread", [(17 * i) % 90 + (i % 7 != 3) for i in range(300)], 64, 128, 128, 16),
 ]
 
 
