@@ -38,6 +38,16 @@
  *     validated; device-resident metadata (slots, tables, lengths) cannot be
  *     checked on the host, so the kernels treat out-of-range values as
  *     documented below instead of faulting.
+ *   - PA_CHECK=1 in the environment (read at every call; a test and
+ *     debugging aid, not for graph capture or timing): the calls that take
+ *     device-resident metadata first synchronise `stream`, copy that metadata
+ *     to the host and validate it, and refuse with PA_EINVAL (nothing
+ *     enqueued, pa_last_error() naming the first violation) what the kernels
+ *     would otherwise skip or cannot handle: a kept token's slot outside the
+ *     SWA table or the pool, two kept tokens resolving to one final slot (the
+ *     writes would race), a context length outside [0, W * block_size], a
+ *     used table entry outside [0, num_blocks), packed query offsets that go
+ *     backwards or past the packed tokens, a chunk longer than its context.
  *   - Calls that write overlapping memory from different streams race; calls
  *     on one stream are ordered.
  */

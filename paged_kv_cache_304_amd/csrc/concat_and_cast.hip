@@ -341,6 +341,11 @@ extern "C" pa_status pa_concat_and_cache_mla_k(const void* k_nope, pa_dtype src_
       (nope_stride0 * sb) % 16 != 0 || (nope_stride1 * sb) % 16 != 0 ||
       (rope_dim > 0 && (!aligned(k_rope, 16) || (rope_stride0 * sb) % 16 != 0)))
     return fail(PA_EINVAL, "%s: sources must be 16-byte aligned per row, the cache %d-byte aligned per block", fn, c_align);
+  if (checks_on()) {
+    const pa_status c = check_slots(fn, reinterpret_cast<hipStream_t>(stream), slot_mapping, num_tokens,
+                                    swa_slot_mapping, swa_len, num_blocks, block_size);
+    if (c != PA_OK) return c;
+  }
 
   CacheCatArgs a;
   a.k_nope = k_nope;

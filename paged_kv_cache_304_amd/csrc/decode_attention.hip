@@ -1294,6 +1294,12 @@ pa_status decode_common(const char* fn, void* out, pa_dtype out_dtype, int64_t o
   const Plan p = make_plan(num_seqs, num_q_heads, num_kv_heads, head_size, max_blocks_per_seq, block_size);
   if (!workspace || workspace_bytes < p.bytes || !aligned(workspace, 256))
     return fail(PA_EWORKSPACE, "%s: workspace needs %zu bytes, 256-byte aligned (got %zu)", fn, p.bytes, workspace_bytes);
+  if (checks_on()) {
+    const hipStream_t cs = reinterpret_cast<hipStream_t>(stream);
+    s = check_tables(fn, cs, block_tables, num_seqs, max_blocks_per_seq, context_lens, num_blocks, block_size);
+    if (s == PA_OK && nt) s = check_slots(fn, cs, nt->slots, num_seqs, nullptr, 0, num_blocks, block_size);
+    if (s != PA_OK) return s;
+  }
 
   DecArgs a;
   a.out = out;

@@ -1078,6 +1078,11 @@ extern "C" pa_status pa_mla_decode_attention(void* out, pa_dtype out_dtype, int6
   const MlaPlan p = mla_plan(num_seqs, rope_dim);
   if (!workspace || workspace_bytes < p.bytes || !aligned(workspace, 256))
     return fail(PA_EWORKSPACE, "%s: workspace needs %zu bytes, 256-byte aligned (got %zu)", fn, p.bytes, workspace_bytes);
+  if (checks_on()) {
+    const pa_status c = check_tables(fn, reinterpret_cast<hipStream_t>(stream), block_tables, num_seqs,
+                                     max_blocks_per_seq, context_lens, num_blocks, block_size);
+    if (c != PA_OK) return c;
+  }
 
   MlaArgs a;
   a.out = out;

@@ -857,6 +857,12 @@ extern "C" pa_status pa_prefill_attention(void* out, pa_dtype out_dtype, int64_t
     return fail(PA_EINVAL, "%s: caches must be 16-byte aligned per block", fn);
   if (((int64_t)num_kv_heads * head_size * cbytes) % 16 != 0)
     return fail(PA_EINVAL, "%s: cache rows must be a multiple of 16 bytes", fn);
+  if (checks_on()) {
+    const hipStream_t cs = reinterpret_cast<hipStream_t>(stream);
+    pa_status c = check_tables(fn, cs, block_tables, num_seqs, max_blocks_per_seq, context_lens, num_blocks, block_size);
+    if (c == PA_OK) c = check_chunks(fn, cs, cu_seqlens_q, num_seqs, num_tokens, context_lens);
+    if (c != PA_OK) return c;
+  }
 
   PfArgs a;
   a.out = out;

@@ -252,6 +252,11 @@ extern "C" pa_status pa_reshape_and_cache(const void* key, const void* value, pa
   if (key_token_stride < row || (value && value_token_stride < row))
     return fail(PA_EINVAL, "%s: token stride smaller than num_heads*head_size", fn);
   if (num_tokens > (int64_t)INT32_MAX * 4) return fail(PA_EINVAL, "%s: num_tokens too large", fn);
+  if (checks_on()) {
+    const pa_status c = check_slots(fn, reinterpret_cast<hipStream_t>(stream), slot_mapping, num_tokens,
+                                    swa_slot_mapping, swa_len, num_blocks, block_size);
+    if (c != PA_OK) return c;
+  }
   if (num_blocks == 0) return PA_OK;  // every slot lies outside an empty pool
 
   RacArgs a;
