@@ -383,7 +383,7 @@ pa_status pa_decode_step(const void* new_k, const void* new_v, pa_dtype new_dtyp
  *            for pa_decode_attention; cache_dtype PA_BF16 or PA_FP8_E4M3FN
  *            (fp8 values are dequantised by multiplying with the scales).
  * No workspace: each query row's softmax is completed inside one workgroup.
- * Supported: head_size in {64, 128}; num_q_heads / num_kv_heads in
+ * Supported: head_size in {64, 128, 256}; num_q_heads / num_kv_heads in
  *   {1, 2, 4, 8}; block_size a multiple of 16.
  * Errors: PA_EINVAL, PA_EDTYPE, PA_EUNSUPPORTED, PA_EHIP. num_seqs == 0 or
  * num_tokens == 0 is a valid no-op.

@@ -60,13 +60,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // two waves per SIMD (256 registers each)
 #define PA_PREFILL_OCCUPANCY __attribute__((amdgpu_waves_per_eu(2, 2)))
 
-#ifndef PA_PREFILL_WAVES
-#define PA_PREFILL_WAVES 4
-#endif
 #ifndef PA_PREFILL_KEYS
 #define PA_PREFILL_KEYS 32
 #endif
-constexpr int kWaves = PA_PREFILL_WAVES;
 #ifndef PA_PREFILL_PRIO_SM
 #define PA_PREFILL_PRIO_SM 1
 #endif
@@ -79,8 +75,16 @@ template <int P> __device__ __forceinline__ void set_prio() {
   static_assert(P >= 0 && P <= 3, "priority 0..3");
   __builtin_amdgcn_s_setprio(P);
 }
-constexpr int kRowsPerWave = 32;              // two 16-row MFMA blocks
-constexpr int kRows = kWaves * kRowsPerWave;  // (token, head) rows per workgroup
+// A workgroup holds kRows (token, head) rows: four waves of two 16-row MFMA
+// blocks for D = 64 and 128; for D = 256, whose accumulators and q operands are
+// twice as wide, eight waves of one block (one workgroup per compute unit: its
+// K/V ring is 128 KB).
+constexpr int kRows = 128;
+template <int D>
+struct Shape {
+  static constexpr int RB = D == 256 ? 1 : 2;       // 16-row MFMA blocks per wave
+  static constexpr int WAVES = kRows / (16 * RB);   // waves per workgroup
+};
 constexpr int kKeys = PA_PREFILL_KEYS;        // positions per key tile
 constexpr int kKB = kKeys / 16;               // 16-key blocks per tile
 constexpr int kBufs = 4;                      // LDS ring: tiles in P.V, in S, and two in flight
@@ -141,8 +145,8 @@ struct Geo {
   static constexpr int KS = D / 32;                // MFMA steps over the head dim
   static constexpr int CB = D / 16;                // 16-column output blocks
   static constexpr int TI = TB / 1024;             // 1 KB wave loads per K (or V) tile
-  static constexpr int IPW = 2 * TI / kWaves;      // ... per wave and tile, K and V together
-  static_assert(TB % 1024 == 0 && (2 * TI) % kWaves == 0, "tile / wave split");
+  static constexpr int IPW = 2 * TI / Shape<D>::WAVES;  // ... per wave and tile, K and V together
+  static_assert(TB % 1024 == 0 && (2 * TI) % Shape<D>::WAVES == 0, "tile / wave split");
   static_assert(TI == (kKeys / 16) * KS && TI == (kKeys / 32) * CB, "reader-ordered layout");
   __device__ static int k_off(int kb, int s, int lane) { return ((kb * KS + s) * 64 + lane) * 16; }
   __device__ static int v_off(int st, int cb, int half, int lane) { return ((st * CB + cb) * 2 + half) * 512 + 8 * lane; }
@@ -173,14 +177,15 @@ template <int D>
 struct Geo8 {
   static constexpr int TB = kKeys * D;         // bytes per fp8 K (or V) tile
   static constexpr int TI = TB / 1024;         // 1 KB wave loads per K (or V) tile
-  static constexpr int IPW = 2 * TI / kWaves;  // ... per wave and tile, K and V together
-  static_assert(TB % 1024 == 0 && (2 * TI) % kWaves == 0 && IPW >= 1, "fp8 tile / wave split");
+  static constexpr int IPW = 2 * TI / Shape<D>::WAVES;  // ... per wave and tile, K and V together
+  static_assert(TB % 1024 == 0 && (2 * TI) % Shape<D>::WAVES == 0 && IPW >= 1, "fp8 tile / wave split");
 };
 
 template <int D, int G, bool kFp8>
-__global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma_kernel(PfArgs a) {
+__global__ __launch_bounds__(64 * Shape<D>::WAVES) PA_PREFILL_OCCUPANCY void prefill_mfma_kernel(PfArgs a) {
   using Gm = Geo<D>;
   using G8 = Geo8<D>;
+  constexpr int kRB = Shape<D>::RB, kWaves = Shape<D>::WAVES, kRowsPerWave = 16 * kRB;
   constexpr int KS = Gm::KS, CB = Gm::CB;
   constexpr int QT = kRows / G;  // query tokens per workgroup
   const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, lg = lane >> 4;
@@ -196,12 +201,9 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
   const int64_t t = item % a.tiles_ub;     // query tile among this head's
   if (g >= a.HKV) return;  // uniform
 
-  // One shared object with the K/V ring first, so that every LDS-DMA
-  // destination lies in the first 64 KB of LDS (the range the DMA path is used
-  // in throughout this library).
+  // One shared object with the K/V ring first (the LDS-DMA destinations).
   // bf16 caches: a kBufs-slot ring of bf16 tiles filled by the DMA. fp8
-  // caches: a kBufs-slot ring of fp8 tiles filled by the DMA (first, below
-  // 64 KB) and two bf16 tiles (the tile in P.V and the tile in S).
+  // caches: a kBufs-slot ring of fp8 tiles filled by the DMA (first) and two bf16 tiles (the tile in P.V and the tile in S).
   constexpr int kDmaBufs = kBufs, kBfBufs = kFp8 ? 2 : kBufs;
   constexpr int kDmaTile = kFp8 ? G8::TB : Gm::TB;
   struct Smem {
@@ -213,7 +215,7 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
     int bins[kBins];            // query tiles per length class
     int64_t pick[2];            // the class holding this workgroup's tile, its rank inside
   };
-  static_assert(sizeof(Smem::dma) <= 65536, "LDS-DMA targets stay below 64 KB");
+  static_assert(sizeof(Smem) <= 160 * 1024, "one compute unit's LDS");
   __shared__ __attribute__((aligned(16))) Smem sm;
   // operand tiles (bf16, reader-ordered) of key tile t
   auto ktile = [&](int t) -> const char* { return kFp8 ? sm.bf[t % kBfBufs][0] : sm.dma[t % kBufs][0]; };
@@ -326,10 +328,10 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
   const float sl2 = flip_q ? -sl2_signed : sl2_signed;
 
   // ---- this wave's rows: block rb, lane row li -> token / head
-  int pos_row[2];  // query position of the lane's row in each block (-1: no key / no query)
-  bf16x8 qop[2][KS];
+  int pos_row[kRB];  // query position of the lane's row in each block (-1: no key / no query)
+  bf16x8 qop[kRB][KS];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < kRB; ++rb) {
     const int R = wave * kRowsPerWave + 16 * rb + li;
     const int tq = tq0 + R / G, hh = g * G + R % G;
     const bool live = tq < tq_end;
@@ -494,12 +496,15 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
     }
   };
 
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.0f, 0.0f};
-  f32x4 acc[2][CB];
+  float m_run[kRB], l_run[kRB];
+  f32x4 acc[kRB][CB];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+  for (int rb = 0; rb < kRB; ++rb) {
+    m_run[rb] = -INFINITY;
+    l_run[rb] = 0.0f;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
 
   // The tile step in three parts. qk: S^T of a tile (sc[rb][kb] holds keys
   // 16kb + 4lg + r of row (rb, li)). softmax: the online-softmax update of
@@ -509,29 +514,30 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
   // kMask: some score of the tile is causal-masked, past the context end, or
   // in a block outside the pool.
   constexpr int kSt = kKeys / 32;  // 32-key steps of P.V
-  auto qk = [&](int t, f32x4 (&sc)[2][kKB]) {
+  auto qk = [&](int t, f32x4 (&sc)[kRB][kKB]) {
     const char* kl = ktile(t);
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb) {
-      sc[0][kb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      sc[1][kb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) sc[rb][kb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         const bf16x8 kop = *reinterpret_cast<const bf16x8*>(kl + Gm::k_off(kb, s, lane));
-        sc[0][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[0][s], sc[0][kb], 0, 0, 0);
-        sc[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[1][s], sc[1][kb], 0, 0, 0);
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb)
+          sc[rb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[rb][s], sc[rb][kb], 0, 0, 0);
       }
     }
   };
-  auto softmax = [&](int kt, int okbits, const f32x4 (&sc)[2][kKB], bf16x8 (&pop)[2][kSt],
-                     bf16x8 (&plo)[2][kSt], float (&alpha)[2], bool (&moved)[2], auto mask_tag) {
+  auto softmax = [&](int kt, int okbits, const f32x4 (&sc)[kRB][kKB], bf16x8 (&pop)[kRB][kSt],
+                     bf16x8 (&plo)[kRB][kSt], float (&alpha)[kRB], bool (&moved)[kRB], auto mask_tag) {
     constexpr bool kMask = decltype(mask_tag)::value;
     const int key0 = kt * kKeys;
     bool kb_ok[kKB];
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb) kb_ok[kb] = kMask ? ((okbits >> kb) & 1) != 0 : true;
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < kRB; ++rb) {
       bool ok[kKB][4];
       float mx = -INFINITY;
 #pragma unroll
@@ -593,15 +599,15 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
 #if PA_PREFILL_SCHED
     __builtin_amdgcn_sched_group_barrier(0x100, 2 * KS, 0);  // DS reads: K operands
 #pragma unroll
-    for (int i = 0; i < 4 * KS; ++i) {
+    for (int i = 0; i < kRB * kKB * KS; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                // one MFMA
       __builtin_amdgcn_sched_group_barrier(0x002, PA_PREFILL_SCHED, 0);  // vector ALU
     }
 #endif
   };
-  auto rescale = [&](const float (&alpha)[2], const bool (&moved)[2]) {
+  auto rescale = [&](const float (&alpha)[kRB], const bool (&moved)[kRB]) {
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < kRB; ++rb) {
       if (__builtin_amdgcn_ballot_w64(moved[rb]) != 0) {
         float al[4];
 #pragma unroll
@@ -616,7 +622,7 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
   // O += P V, V's operand by transposing reads (lane m of a 16-lane group
   // reads row kbase + m/4, columns 16cb + 4(m%4) .. +3, kbase = 32st + 4g,
   // then + 16); the two reads are the operand's low and high halves.
-  auto pv = [&](int kt, int okbits, const bf16x8 (&pop)[2][kSt], const bf16x8 (&plo)[2][kSt],
+  auto pv = [&](int kt, int okbits, const bf16x8 (&pop)[kRB][kSt], const bf16x8 (&plo)[kRB][kSt],
                 auto mask_tag) {
     constexpr bool kMask = decltype(mask_tag)::value;
     const char* vl = vtile(kt);
@@ -644,10 +650,12 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
         u32x4 w = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         if constexpr (kMask) w &= vmask;
         const bf16x8 vop = __builtin_bit_cast(bf16x8, w);
-        acc[0][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pop[0][st], vop, acc[0][cb], 0, 0, 0);
-        acc[1][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pop[1][st], vop, acc[1][cb], 0, 0, 0);
-        acc[0][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo[0][st], vop, acc[0][cb], 0, 0, 0);
-        acc[1][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo[1][st], vop, acc[1][cb], 0, 0, 0);
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb)
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pop[rb][st], vop, acc[rb][cb], 0, 0, 0);
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb)
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo[rb][st], vop, acc[rb][cb], 0, 0, 0);
       }
     }
   };
@@ -703,10 +711,10 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
       barrier_no_vmem_wait();
     }
   };
-  f32x4 sc_cur[2][kKB], sc_nxt[2][kKB];
-  bf16x8 pop[2][kSt], plo[2][kSt];
-  float alpha[2];
-  bool moved[2];
+  f32x4 sc_cur[kRB][kKB], sc_nxt[kRB][kKB];
+  bf16x8 pop[kRB][kSt], plo[kRB][kSt];
+  float alpha[kRB];
+  bool moved[kRB];
   if (n_kt > 0) {  // tile 0 in, with tiles 1 and 2 (if any) still in flight
     if (n_kt > 2)
       wait_vmem<2 * kLoadsPerTile>();
@@ -741,7 +749,7 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
     if (kPrioSM) set_prio<0>();
     pv(kt, okb, pop, plo, std::false_type{});
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
       for (int kb = 0; kb < kKB; ++kb) sc_cur[rb][kb] = sc_nxt[rb][kb];
   }
@@ -758,7 +766,7 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
     if (kPrioSM) set_prio<0>();
     pv(kt, okb, pop, plo, std::true_type{});
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
       for (int kb = 0; kb < kKB; ++kb) sc_cur[rb][kb] = sc_nxt[rb][kb];
   }
@@ -766,7 +774,7 @@ __global__ __launch_bounds__(64 * kWaves) PA_PREFILL_OCCUPANCY void prefill_mfma
   // ---- finish: sum the row sums over the four lane groups, normalise, store
   // (the grid is launched with 64 * kWaves threads per workgroup)
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < kRB; ++rb) {
     float l = l_run[rb];
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
@@ -800,10 +808,10 @@ template <int D, bool kFp8>
 bool launch_g(int G, const PfArgs& a, hipStream_t st) {
   const unsigned grid = (unsigned)((a.tiles_ub * a.HKV + 7) / 8 * 8);
   switch (G) {
-    case 1: prefill_mfma_kernel<D, 1, kFp8><<<grid, 64 * kWaves, 0, st>>>(a); return true;
-    case 2: prefill_mfma_kernel<D, 2, kFp8><<<grid, 64 * kWaves, 0, st>>>(a); return true;
-    case 4: prefill_mfma_kernel<D, 4, kFp8><<<grid, 64 * kWaves, 0, st>>>(a); return true;
-    case 8: prefill_mfma_kernel<D, 8, kFp8><<<grid, 64 * kWaves, 0, st>>>(a); return true;
+    case 1: prefill_mfma_kernel<D, 1, kFp8><<<grid, 64 * Shape<D>::WAVES, 0, st>>>(a); return true;
+    case 2: prefill_mfma_kernel<D, 2, kFp8><<<grid, 64 * Shape<D>::WAVES, 0, st>>>(a); return true;
+    case 4: prefill_mfma_kernel<D, 4, kFp8><<<grid, 64 * Shape<D>::WAVES, 0, st>>>(a); return true;
+    case 8: prefill_mfma_kernel<D, 8, kFp8><<<grid, 64 * Shape<D>::WAVES, 0, st>>>(a); return true;
     default: return false;
   }
 }
@@ -833,8 +841,8 @@ extern "C" pa_status pa_prefill_attention(void* out, pa_dtype out_dtype, int64_t
   const int G = num_q_heads / num_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8)
     return fail(PA_EUNSUPPORTED, "%s: group size H_Q/H_KV = %d not supported (1, 2, 4, 8)", fn, G);
-  if (head_size != 64 && head_size != 128)
-    return fail(PA_EUNSUPPORTED, "%s: head_size %d not supported (64, 128)", fn, head_size);
+  if (head_size != 64 && head_size != 128 && head_size != 256)
+    return fail(PA_EUNSUPPORTED, "%s: head_size %d not supported (64, 128, 256)", fn, head_size);
   if (block_size % 16 != 0) return fail(PA_EUNSUPPORTED, "%s: block_size %d must be a multiple of 16", fn, block_size);
   if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX) return fail(PA_EINVAL, "%s: max_blocks_per_seq*block_size too large", fn);
   if (out_dtype != PA_BF16 && out_dtype != PA_F32) return fail(PA_EDTYPE, "%s: out dtype %s not supported", fn, dtype_name(out_dtype));
@@ -897,8 +905,9 @@ extern "C" pa_status pa_prefill_attention(void* out, pa_dtype out_dtype, int64_t
   if (a.tiles_ub * num_kv_heads + 7 > 0x7FFFFFFF) return fail(PA_EINVAL, "%s: too many query tiles", fn);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const bool fp8 = cache_dtype == PA_FP8_E4M3FN;
-  const bool ok = head_size == 64 ? (fp8 ? launch_g<64, true>(G, a, st) : launch_g<64, false>(G, a, st))
-                                  : (fp8 ? launch_g<128, true>(G, a, st) : launch_g<128, false>(G, a, st));
+  const bool ok = head_size == 64    ? (fp8 ? launch_g<64, true>(G, a, st) : launch_g<64, false>(G, a, st))
+                  : head_size == 128 ? (fp8 ? launch_g<128, true>(G, a, st) : launch_g<128, false>(G, a, st))
+                                     : (fp8 ? launch_g<256, true>(G, a, st) : launch_g<256, false>(G, a, st));
   if (!ok) return fail(PA_EUNSUPPORTED, "%s: no kernel for this shape", fn);
   return after_launch(fn);
 }

@@ -4,7 +4,7 @@ bf16 outputs are one more rounding, allowed half a bf16 ulp only where
 |oracle| >= 2, as for decode).
 
 Cases: ragged chunks on cached prefixes and whole prompts over every group
-size, both head sizes and block sizes 16..64 (48 included), many sequences
+size, head sizes 64, 128 and 256 and block sizes 16..64 (48 included), many sequences
 with empties, chunks longer than their context, bad table entries and
 NaN-filled unwritten slots, bit-identical output under block relabelling, the
 full-size prefill batch (every row and head), and the same kinds of cases over
@@ -103,6 +103,10 @@ CASES = [
     ("G4 D64 bs64", [700, 65], [300, 65], 8, 2, 64, 64, None),
     ("G2 D128 chunk longer than context, empty sequences",
      [5, 0, 40, 0, 3], [20, 0, 40, 3, 1], 16, 8, 128, 16, 4),
+    ("G2 D256 chunks on prefixes", [100, 700, 64, 129], [37, 128, 64, 129], 16, 8, 256, 16, None),
+    ("G1 D256 whole prompts", [1, 17, 65, 200], [1, 17, 65, 200], 8, 8, 256, 16, None),
+    ("G8 D256 bs32", [260, 7], [70, 7], 16, 2, 256, 32, None),
+    ("G4 D256 chunk longer than context, empty sequences", [5, 0, 40, 0, 3], [20, 0, 40, 3, 1], 16, 4, 256, 16, 4),
     ("G2 D128 300 sequences",
      [1 + (i * 53) % 300 for i in range(300)], [(0 if i % 7 == 0 else 1 + (i * 13) % 40) for i in range(300)],
      16, 8, 128, 16, None),
@@ -127,6 +131,8 @@ FP8_CASES = [
     ("fp8 G8 D64", [333, 20], [40, 20], 8, 1, 64, 16, None),
     ("fp8 G2 D128 chunk longer than context, empty sequences",
      [5, 0, 40, 0, 3], [20, 0, 40, 3, 1], 16, 8, 128, 16, 4),
+    ("fp8 G2 D256 chunks on prefixes", [100, 700, 64, 129], [37, 128, 64, 129], 16, 8, 256, 16, None),
+    ("fp8 G4 D256 bs32", [513, 33], [200, 33], 16, 4, 256, 32, None),
     ("fp8 G2 D128 70 sequences",
      [1 + (i * 97) % 900 for i in range(70)], [(0 if i % 9 == 0 else 1 + (i * 13) % 70) for i in range(70)],
      16, 8, 128, 16, None),
