@@ -12,18 +12,19 @@
 // head h / G. A query with p < 0 gives zeros.
 //
 // gfx950 design (matrix cores for both products):
-//  * Workgroup = 4 waves = 128 (token, head) rows of one KV head: 128/G
-//    consecutive query tokens of one sequence times the G query heads of the
-//    group (row R -> token R / G, head R % G), two workgroups per compute unit
-//    (256 registers per lane each). Each wave owns 32 rows as two 16-row MFMA
-//    blocks that share every K/V operand read. Workgroups are ordered so that
-//    each XCD runs the query tiles of the same (KV head, sequence) together and
-//    its L2 serves their K/V.
+//  * Workgroup = 128 (token, head) rows of one KV head: 128/G consecutive
+//    query tokens of one sequence times the G query heads of the group (row R
+//    -> token R / G, head R % G), two waves per SIMD (256 registers per lane
+//    each). For D = 64 and 128, 4 waves own 32 rows each as two 16-row MFMA
+//    blocks that share every K/V operand read (two workgroups per compute
+//    unit); for D = 256, 8 waves own one 16-row block each (one workgroup per
+//    compute unit). Workgroups are ordered so that each XCD runs the query
+//    tiles of the same (KV head, sequence) together and its L2 serves their K/V.
 //  * Key tiles of 32 positions: the tile's K and V arrive as 1 KB
 //    global_load_lds_dwordx4 wave loads dealt over the waves, straight into an
 //    LDS ring in the order the operand reads consume them (every read is one
-//    contiguous, conflict-free block), tiles ahead of the compute. The ring is
-//    at most 64 KB at the start of LDS.
+//    contiguous, conflict-free block), tiles ahead of the compute. The ring
+//    comes first in LDS (64 KB for D = 128, 128 KB for D = 256).
 //  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (K rows from LDS as A, the
 //    wave's q rows from registers as B): lane l gets the scores of keys
 //    16*kb + 4*(l/16) + r for query row l%16, so each lane keeps one row's
