@@ -919,20 +919,22 @@ def cpu_baseline_engine(torch, w, W, oracle, kc, vc, q, nk, nv, lens):
 
 
 def mla_segments(ctx: np.ndarray, grid: int, tile: int = 32) -> int:
-    """(workgroup, sequence) segments of the persistent MLA split: the tiles of
-    32 positions of all sequences, in sequence order, cut into ``grid`` even
-    ranges (the first T % grid ranges one tile longer); a segment is a
-    sequence's tiles within one range."""
+    """(workgroup, sequence) segments of the persistent MLA split: the work of
+    all sequences in sequence order forms one list of units (a sequence with
+    tiles of 32 positions contributes one unit for its absorbed query, then one
+    per tile), cut into ``grid`` even ranges (the first T % grid ranges one unit
+    longer); a segment is a sequence's tiles within one range."""
     tiles = -(-ctx.astype(np.int64) // tile)
-    ts = np.concatenate([[0], np.cumsum(tiles)])
+    units = np.where(tiles > 0, tiles + 1, 0)
+    ts = np.concatenate([[0], np.cumsum(units)])
     T = int(ts[-1])
     q, r = divmod(T, grid)
     starts = np.array([w * q + min(w, r) for w in range(grid + 1)], dtype=np.int64)
     n = 0
     for w in range(grid):
         t0, t1 = starts[w], starts[w + 1]
-        if t1 > t0:
-            n += int(np.sum((np.minimum(t1, ts[1:]) > np.maximum(t0, ts[:-1]))))
+        if t1 > t0:  # a sequence's tiles are units ts[b] + 1 .. ts[b + 1] - 1
+            n += int(np.sum((np.minimum(t1, ts[1:]) > np.maximum(t0, ts[:-1] + 1))))
     return n
 
 

@@ -20,8 +20,8 @@
 //    hi + lo (x - hi rounded again), so that the products below keep ~16 more
 //    bits than a bf16 q~ would.
 //  * split: persistent, one workgroup per compute unit over an even share of
-//    the 32-position tiles of all sequences; 2 fetching waves move each item
-//    -- a segment's q~, then its latent tiles -- by LDS-DMA into a 4-deep LDS
+//    the items of all sequences (each sequence's q~, then its 32-position
+//    tiles); 2 fetching waves move each item by LDS-DMA into a 4-deep LDS
 //    ring, and the computing waves meet them and each other through LDS
 //    counters (no workgroup barrier per tile). Two score waves (8 heads each)
 //    form S^T = C [q~hi | q~lo] on v_mfma_f32_16x16x32_bf16 with q~ held in
@@ -85,7 +85,7 @@ struct MlaArgs {
   const int32_t* ctx_lens;
   uint16_t* q_hi;   // [B, 16, ROW]
   uint16_t* q_lo;
-  int32_t* ts;      // [B + 1] first global tile of each sequence; ts[B] = all tiles
+  int32_t* ts;      // [B + 1] first work unit of each sequence; ts[B] = all units (q~ items and tiles)
   int32_t* flag;    // set when a wait of the split ran past its bound (the outputs are then NaN)
   float* ws_m;      // [G + B, 16] per (workgroup, sequence) partial
   float* ws_l;
@@ -110,9 +110,13 @@ __device__ __forceinline__ void split_hi_lo(float x, uint16_t& hi, uint16_t& lo)
   lo = (uint16_t)f32_to_bf16(x - __uint_as_float((uint32_t)hi << 16));
 }
 
-// The tiles of all sequences in sequence order form one list of T tiles;
-// workgroup w of G serves tiles range_start(w) .. range_start(w + 1) - 1 (an
-// even split), tile t belongs to workgroup tile_owner(t).
+// The work of all sequences in sequence order forms one list of T units: a
+// sequence with tiles contributes one unit for its q~ item followed by one per
+// tile (an empty sequence none), so that the q~ items a workgroup fetches are
+// part of its even share. Workgroup w of G serves units range_start(w) ..
+// range_start(w + 1) - 1; unit u belongs to workgroup tile_owner(u). A
+// workgroup whose share holds some of a sequence's tiles fetches that
+// sequence's q~ item even when the q~ unit itself lies in the previous share.
 __device__ __forceinline__ int range_start(int w, int T, int G) {
   const int q = T / G, r = T % G;
   return w * q + min(w, r);
@@ -122,8 +126,12 @@ __device__ __forceinline__ int tile_owner(int t, int T, int G) {
   return t < big ? t / (q + 1) : r + (t - big) / q;
 }
 __device__ __forceinline__ int tiles_of(const MlaArgs& a, int b) { return (clamp_ctx(a, b) + kTile - 1) / kTile; }
+__device__ __forceinline__ int units_of(const MlaArgs& a, int b) {
+  const int t = tiles_of(a, b);
+  return t > 0 ? t + 1 : 0;
+}
 
-// ts[b] = tiles of sequences 0 .. b - 1 (ts[B] = T), by one workgroup of 256:
+// ts[b] = units of sequences 0 .. b - 1 (ts[B] = T), by one workgroup of 256:
 // each thread sums a run of sequences, a lane scan per wave and the four wave
 // totals give each run's first tile (one workgroup barrier).
 __device__ void plan_tiles(const MlaArgs& a) {
@@ -132,7 +140,7 @@ __device__ void plan_tiles(const MlaArgs& a) {
   const int per = (B + 255) / 256;
   const int lo = min(B, tid * per), hi = min(B, lo + per);
   int mine = 0;
-  for (int b = lo; b < hi; ++b) mine += tiles_of(a, b);
+  for (int b = lo; b < hi; ++b) mine += units_of(a, b);
   int incl = mine;  // inclusive prefix over this wave's lanes
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -149,7 +157,7 @@ __device__ void plan_tiles(const MlaArgs& a) {
   } else {
     for (int b = lo; b < hi; ++b) {
       a.ts[b] = run;
-      run += tiles_of(a, b);
+      run += units_of(a, b);
     }
   }
   if (tid == 255) {  // the last run ends at T
@@ -278,7 +286,7 @@ __device__ __forceinline__ void block_of(const MlaArgs& a, int pos, int& blk, in
 constexpr float kLazyMax = 8.0f;  // log2 headroom of a segment's running max
 
 // Persistent: one workgroup per compute unit, each over an even share of the
-// T tiles of all sequences (sequence order). Its share falls into segments,
+// T units of all sequences (sequence order). Its share falls into segments,
 // one per sequence it touches; a segment is processed as an item stream --
 // the sequence's q~ (hi and lo, 32 rows of the row length: exactly one tile's
 // bytes), then its tiles -- and ends with a partial (running max, sum and
@@ -392,11 +400,11 @@ __global__ __launch_bounds__(64 * (kWaves + kProducers)) void mla_split_kernel(M
       const int b = b_next + lane;
       bool live = false;
       int lt0 = 0, nt = 0, cx = 0;
-      if (b < B) {
+      if (b < B) {  // its tiles are units tsb + 1 .. tse - 1
         const int tsb = a.ts[b], tse = a.ts[b + 1];
-        const int lo_t = max(t0, tsb), hi_t = min(t1, tse);
+        const int lo_t = max(t0, tsb + 1), hi_t = min(t1, tse);
         live = hi_t > lo_t;
-        lt0 = lo_t - tsb;
+        lt0 = lo_t - tsb - 1;
         nt = hi_t - lo_t;
         cx = clamp_ctx(a, b);
       }
@@ -410,7 +418,7 @@ __global__ __launch_bounds__(64 * (kWaves + kProducers)) void mla_split_kernel(M
       sg_ctx = __builtin_amdgcn_ds_permute(dst, cx);
       nseg = cnt;
       const int nb = b_next + 64;
-      more = nb < B && uniform(a.ts[nb < B ? nb : B]) < t1;  // tiles of later sequences remain
+      more = nb < B && uniform(a.ts[nb < B ? nb : B]) + 1 < t1;  // tiles of later sequences remain
       b_next = nb;
     };
     int cur_k = 0, cur_idx = 0;  // item cursor: segment, item within it (0: q~)
@@ -864,8 +872,8 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(MlaArgs a) {
   int n = 0, p0 = 0;
   if (b < a.num_seqs) {
     const int T = a.ts[a.num_seqs], tsb = a.ts[b], tse = a.ts[b + 1];
-    if (tse > tsb) {
-      const int wf = tile_owner(tsb, T, a.grid), wl = tile_owner(tse - 1, T, a.grid);
+    if (tse > tsb) {  // its tiles are units tsb + 1 .. tse - 1
+      const int wf = tile_owner(tsb + 1, T, a.grid), wl = tile_owner(tse - 1, T, a.grid);
       n = wl - wf + 1;
       p0 = wf + b;
     }

@@ -198,7 +198,7 @@ def prefill(L, **over):
 @pytest.mark.parametrize("over,code", [
     (dict(HQ=12), "PA_EINVAL"),              # 12 % 8
     (dict(HQ=24, HKV=8), "PA_EUNSUPPORTED"),  # G = 3
-    (dict(D=256), "PA_EUNSUPPORTED"),
+    (dict(D=96), "PA_EUNSUPPORTED"),          # head sizes 64, 128, 256 only
     (dict(BS=8), "PA_EUNSUPPORTED"),          # not a multiple of 16
     (dict(T=-1), "PA_EINVAL"),
     (dict(B=-1), "PA_EINVAL"),

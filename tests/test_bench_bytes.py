@@ -94,20 +94,24 @@ def test_mla_algorithmic_bytes_match_a_walk_of_the_workload():
     assert bench.mla_bytes(w)["algorithmic"] == nbytes
 
 
-def test_mla_segments_match_a_walk_of_the_tile_ranges():
+def test_mla_segments_match_a_walk_of_the_unit_ranges():
     """Each workgroup of the persistent split owns a contiguous run of the
-    32-position tiles of all sequences (sequence order, the first T % G runs one
-    tile longer); a segment is one sequence seen by one workgroup."""
+    units of all sequences (sequence order: a sequence with tiles of 32
+    positions gives one unit for its absorbed query, then one per tile; the
+    first T % G runs one unit longer); a segment is one sequence whose tiles a
+    workgroup sees (a run holding only a query unit makes none)."""
     rng = np.random.default_rng(5)
     for grid in (1, 3, 7, 256):
         ctx = rng.integers(0, 300, size=int(rng.integers(1, 40)))
-        owner_of_tile = []
+        units = []  # (sequence, is a tile)
         for b, c in enumerate(ctx):
-            owner_of_tile += [b] * int(-(-int(c) // 32))
-        T = len(owner_of_tile)
+            n = int(-(-int(c) // 32))
+            if n:
+                units += [(b, False)] + [(b, True)] * n
+        T = len(units)
         segs = 0
         for w in range(grid):
             lo = w * (T // grid) + min(w, T % grid)
             hi = (w + 1) * (T // grid) + min(w + 1, T % grid)
-            segs += len(set(owner_of_tile[lo:hi]))
+            segs += len({b for b, tile in units[lo:hi] if tile})
         assert bench.mla_segments(ctx, grid) == segs

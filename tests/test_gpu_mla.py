@@ -101,9 +101,10 @@ CASES = [
     ("qk24 v16", [129, 1], 0, 24, 16, 16),
     # more than 64 sequences: the split's segment set-up searches the tile plan
     ("B65 one past a single round of set-up loads", [(37 * i) % 200 + 1 for i in range(65)], 64, 128, 128, 16),
-    # on 256 compute units the first workgroup's two tiles are sequence 0's and
-    # sequence 71's, 71 entries apart: its list of segments is refilled
-    ("B73 a refilled segment list", [1] + [0] * 70 + [1, 9600], 64, 128, 128, 16),
+    # on 256 compute units the first workgroup's five units are sequence 0's
+    # query and tile, sequence 71's query and tile and sequence 72's query:
+    # its tiles lie 71 entries apart and its list of segments is refilled
+    ("B73 a refilled segment list", [1] + [0] * 70 + [1, 40000], 64, 128, 128, 16),
     # more than 256 sequences: each thread of the tile plan sums a run of two
     ("B300 two sequences per plan thread", [(17 * i) % 90 + (i % 7 != 3) for i in range(300)], 64, 128, 128, 16),
 ]
