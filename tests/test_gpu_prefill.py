@@ -5,7 +5,7 @@ bf16 outputs are one more rounding, allowed half a bf16 ulp only where
 
 Cases: ragged chunks on cached prefixes and whole prompts over every group
 size, head sizes 64, 128 and 256 and block sizes 16..64 (48 included), many sequences
-with empties, chunks longer than their context, bad table entries and
+with empties, contexts past the kernel's 2,048-entry window of the block table, chunks longer than their context, bad table entries and
 NaN-filled unwritten slots, bit-identical output under block relabelling, the
 full-size prefill batch (every row and head), and the same kinds of cases over
 fp8 e4m3fn caches with k/v scales."""
@@ -110,6 +110,10 @@ CASES = [
     ("G2 D128 300 sequences",
      [1 + (i * 53) % 300 for i in range(300)], [(0 if i % 7 == 0 else 1 + (i * 13) % 40) for i in range(300)],
      16, 8, 128, 16, None),
+    # the kernel holds 2,048 table entries in LDS at a time and restages the
+    # window when a sequence's keys run past it
+    ("G2 D64 a context across three table windows", [2 * 2048 * 16 + 700, 90], [96, 90], 4, 2, 64, 16, None),
+    ("G2 D256 bs32 a context past one table window", [2048 * 32 + 300], [40], 4, 2, 256, 32, None),
 ]
 
 
@@ -136,6 +140,7 @@ FP8_CASES = [
     ("fp8 G2 D128 70 sequences",
      [1 + (i * 97) % 900 for i in range(70)], [(0 if i % 9 == 0 else 1 + (i * 13) % 70) for i in range(70)],
      16, 8, 128, 16, None),
+    ("fp8 G4 D128 a context past one table window", [2048 * 16 + 5000, 30], [70, 30], 8, 2, 128, 16, None),
 ]
 
 
