@@ -1080,7 +1080,8 @@ extern "C" pa_status pa_mla_decode_attention(void* out, pa_dtype out_dtype, int6
   if (!aligned(w_uk, 16) || !aligned(w_uv, 16)) return fail(PA_EINVAL, "%s: weights must be 16-byte aligned", fn);
   if (!aligned(q_nope, 16) || (q_nope_seq_stride * 2) % 16 != 0)
     return fail(PA_EINVAL, "%s: q_nope must be 16-byte aligned per sequence", fn);
-  // tiles of 32 positions over all sequences must count in 32 bits
+  // the split's units (tiles of 32 positions over all sequences, plus one
+  // query item per sequence: at most 2^20 more) must count in 32 bits
   if ((int64_t)num_seqs * (((int64_t)max_blocks_per_seq * block_size + kTile - 1) / kTile) > INT32_MAX / 2)
     return fail(PA_EINVAL, "%s: too many (sequence, tile) items", fn);
   const MlaPlan p = mla_plan(num_seqs, rope_dim);
