@@ -1208,8 +1208,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the paged "
-              "KV cache kernels shard by sequence or KV head with no exchange; see the design "
-              "notes)", file=sys.stderr)
+              "KV cache kernels shard by sequence or KV head with no exchange between GPUs, so "
+              "one GPU's share at its real shape is the measured unit)", file=sys.stderr)
         sys.exit(2)
     import torch
 
