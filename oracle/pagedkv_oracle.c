@@ -34,8 +34,7 @@
  *    token strides, optional second-stage SWA slot remap, optional division by
  *    a per-tensor k/v scale before the store, block stride of the cache).
  *
- * Readings taken where the pages leave a step open (each is listed in the
- * design notes as well):
+ * Readings taken where the pages leave a step open:
  *  R1  Any negative slot skips the token; a negative first-stage slot skips it
  *      before the SWA table is consulted (the SGLang kernel would index the
  *      table with -1).
