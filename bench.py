@@ -966,8 +966,9 @@ def mla_bytes(w, grid: int = 256) -> dict:
 
 
 def mla_setup(torch, pkv, workloads):
-    """Tensors of the batch-64 MLA decode workload, its latent write and its
-    attention call."""
+    """Tensors of the batch-64 MLA decode workload, its decode step (the new
+    latent rows written, then the attention: one pa_mla_decode_step call) and
+    its attention call alone."""
     w = workloads.mla_decode_b64()
     B, H, QK, R, DC, DV = (w["num_seqs"], w["num_heads"], w["qk_nope_dim"], w["rope_dim"],
                            w["kv_lora_rank"], w["v_dim"])
@@ -985,28 +986,25 @@ def mla_setup(torch, pkv, workloads):
     out = torch.empty((B, H, DV), dtype=torch.bfloat16, device="cuda")
     ws = torch.zeros(pkv.mla_decode_workspace_size(B, H, QK, R, DC, DV, bt.shape[1], BS), dtype=torch.uint8,
                      device="cuda")
-    cache4 = cache.view(NB, BS, 1, DC + R)
 
-    def write():
-        pkv.concat_and_cache_mla_k(new_c, new_r, cache4, slots)
+    def step():
+        pkv.mla_decode_step(new_c, new_r, slots, out, q_nope, q_rope, w_uk, w_uv, cache, bt, cl,
+                            w["softmax_scale"], workspace=ws)
 
     def attend():
         pkv.mla_decode_attention(out, q_nope, q_rope, w_uk, w_uv, cache, bt, cl, w["softmax_scale"],
                                  workspace=ws)
 
-    return w, write, attend, (cache, q_nope, q_rope, w_uk, w_uv)
+    return w, step, attend, (cache, q_nope, q_rope, w_uk, w_uv)
 
 
 def measure_mla_decode(args, torch, pkv, workloads):
     """The batch-64 MLA latent decode: K attention calls back to back on HIP
     events (absorb + split + merge; the roofline's launches) and K whole steps
-    (latent write + attention)."""
-    w, write, attend, tensors = mla_setup(torch, pkv, workloads)
+    (latent write + attention in one pa_mla_decode_step call)."""
+    w, step, attend, tensors = mla_setup(torch, pkv, workloads)
     stream = torch.cuda.current_stream()
-    def both(i):
-        write()
-        attend()
-    settle(torch, both, max(5, min(args.warmup, 20)))
+    settle(torch, lambda i: step(), max(5, min(args.warmup, 20)))
     ta, ts = Timer(torch, stream), Timer(torch, stream)
     ta.start()
     for _ in range(args.steps):
@@ -1014,14 +1012,13 @@ def measure_mla_decode(args, torch, pkv, workloads):
     ta.stop()
     ts.start()
     for _ in range(args.steps):
-        write()
-        attend()
+        step()
     ts.stop()
     torch.cuda.synchronize()
     ms, step_ms = ta.mean_ms() / args.steps, ts.mean_ms() / args.steps
     nb = mla_bytes(w, grid=min(256, torch.cuda.get_device_properties(0).multi_processor_count))
     gbps = nb["algorithmic"] / (ms * 1e-3) / 1e9
-    del write, attend, tensors
+    del step, attend, tensors
     return {"workload": w["name"], "ms": round(ms, 5), "bytes": nb["algorithmic"], "GBps": round(gbps, 2),
             "frac": round(gbps / HBM_PEAK_GBPS, 4), "bytes_with_workspace": nb["call"],
             "step_ms": round(step_ms, 5), "tokens_per_s": round(w["num_seqs"] / (step_ms * 1e-3), 1),
@@ -1030,9 +1027,9 @@ def measure_mla_decode(args, torch, pkv, workloads):
 
 def run_mla_decode(args, torch, pkv, workloads):
     """MLA decode step over a latent paged cache (synthetic DeepSeek-V2-Lite shapes):
-    the batch's new latent rows written with concat_and_cache_mla_k (one 'head'),
-    then pa_mla_decode_attention."""
-    w, write, attend, (cache, q_nope, q_rope, w_uk, w_uv) = mla_setup(torch, pkv, workloads)
+    the batch's new latent rows written, then the attention, in one
+    pa_mla_decode_step call."""
+    w, step, attend, (cache, q_nope, q_rope, w_uk, w_uv) = mla_setup(torch, pkv, workloads)
     B, H, QK, R, DC, DV = (w["num_seqs"], w["num_heads"], w["qk_nope_dim"], w["rope_dim"],
                            w["kv_lora_rank"], w["v_dim"])
     BS, NB = w["block_size"], w["num_blocks"]
@@ -1041,21 +1038,21 @@ def run_mla_decode(args, torch, pkv, workloads):
     if args.profile_steps:
         copy_calibration(torch, pkv)
         for _ in range(args.warmup + args.profile_steps):
-            write()
+            step()
+        # the launches roofline.achieved times: attention calls back to back
+        for _ in range(args.profile_steps):
             attend()
         torch.cuda.synchronize()
         print(json.dumps({"profile_steps": args.profile_steps, "workload": w["name"]}))
         return
     for _ in range(args.warmup):
-        write()
-        attend()
+        step()
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record(stream)
     for _ in range(args.steps):
-        write()
-        attend()
+        step()
     t1.record(stream)
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps

@@ -18,6 +18,7 @@
  *   pa_mla_decode_attention   decode over a paged cache of latent rows, with
  *                             W_UK absorbed into the query and W_UV applied
  *                             after the softmax
+ *   pa_mla_decode_step        the new latent rows written, then that decode
  * and, on the host, the bookkeeping that feeds them:
  *   pa_bm_*                   block manager: allocation in block_size units,
  *                             per-step slot_mapping / block_tables /
@@ -488,6 +489,48 @@ pa_status pa_mla_decode_attention(void* out, pa_dtype out_dtype, int64_t out_seq
                                   int32_t num_heads, int32_t qk_nope_dim, int32_t rope_dim,
                                   int32_t kv_lora_rank, int32_t v_dim, float softmax_scale,
                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_mla_decode_step -- one decode step over the latent cache: the batch's new
+ * latent rows written, then pa_mla_decode_attention over the cache that holds
+ * them.
+ *
+ * Defined by: "PagedAttention principle" page, the decode dataflow section (each
+ * step stores the new token's cache entry through its slot, then attends over
+ * the sequence's blocks) with the MLA paragraphs of the GQA/MLA shapes section
+ * (what is stored per token is the latent c and the shared RoPE key). Sequence
+ * b's row c = new_c[b] (kv_lora_rank values) followed by new_rope[b] (rope_dim
+ * values) goes to slot new_slots[b] of latent_cache (block slot / block_size,
+ * offset slot % block_size), exactly as pa_concat_and_cache_mla_k with
+ * num_heads = 1 writes it; a negative slot, or one past num_blocks *
+ * block_size, writes nothing. The attention then reads the cache with the
+ * rows in place (a new position is normally the last, context_lens[b] - 1).
+ * The rows are written by the launch that also absorbs the query, so the step
+ * takes three kernels, as the attention alone.
+ *
+ * Arguments
+ *   new_c    [num_seqs, kv_lora_rank], row stride new_c_stride (elements),
+ *            16-byte aligned per row; new_rope [num_seqs, rope_dim], row
+ *            stride new_rope_stride, 16-byte aligned per row (unused when
+ *            rope_dim = 0); new_dtype PA_BF16 (the cache's type: a copy).
+ *   new_slots [num_seqs] int64, device; two kept rows must not share a slot.
+ *   the rest: as pa_mla_decode_attention, with latent_cache writable.
+ * Errors: as pa_mla_decode_attention; nothing is written or launched when a
+ * call returns an error.
+ */
+pa_status pa_mla_decode_step(const void* new_c, int64_t new_c_stride, const void* new_rope,
+                             int64_t new_rope_stride, pa_dtype new_dtype, const int64_t* new_slots,
+                             void* out, pa_dtype out_dtype, int64_t out_seq_stride,
+                             const void* q_nope, int64_t q_nope_seq_stride,
+                             const void* q_rope, int64_t q_rope_seq_stride, pa_dtype q_dtype,
+                             const void* w_uk, const void* w_uv, pa_dtype w_dtype,
+                             void* latent_cache, pa_dtype cache_dtype, int64_t num_blocks,
+                             int32_t block_size, int64_t block_stride, const int32_t* block_tables,
+                             int32_t max_blocks_per_seq, const int32_t* context_lens,
+                             int32_t num_seqs, int32_t num_heads, int32_t qk_nope_dim,
+                             int32_t rope_dim, int32_t kv_lora_rank, int32_t v_dim,
+                             float softmax_scale, void* workspace, size_t workspace_bytes,
+                             void* stream);
 
 /* ------------------------------------------------------------------------
  * Block manager (host side).

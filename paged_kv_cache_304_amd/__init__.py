@@ -19,6 +19,7 @@ from .ops import (  # noqa: F401
     hbm_copy,
     hbm_read,
     mla_decode_attention,
+    mla_decode_step,
     mla_decode_workspace_size,
     prefill_attention,
     reshape_and_cache,

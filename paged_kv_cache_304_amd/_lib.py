@@ -27,7 +27,7 @@ EXPORTS = ("pa_last_error", "pa_abi_version", "pa_reshape_and_cache", "pa_concat
            "pa_hbm_copy", "pa_hbm_read",
            "pa_bm_create", "pa_bm_destroy", "pa_bm_layout_of", "pa_bm_free_blocks", "pa_bm_seq_len",
            "pa_bm_seq_table", "pa_bm_release", "pa_bm_plan_step", "pa_bm_upload",
-           "pa_mla_decode_workspace_size", "pa_mla_decode_attention")
+           "pa_mla_decode_workspace_size", "pa_mla_decode_attention", "pa_mla_decode_step")
 
 
 class BmLayout(ctypes.Structure):
@@ -89,6 +89,8 @@ def _load() -> ctypes.CDLL:
     L.pa_mla_decode_attention.argtypes = [P, I32, I64, P, I64, P, I64, I32, P, P, I32, P, I32, I64, I32,
                                           I64, P, I32, P, I32, I32, I32, I32, I32, I32, F, P, SZ, P]
     L.pa_mla_decode_attention.restype = I32
+    L.pa_mla_decode_step.argtypes = [P, I64, P, I64, I32, P] + L.pa_mla_decode_attention.argtypes
+    L.pa_mla_decode_step.restype = I32
     L.pa_bm_create.argtypes = [I64, I32, I32, I32, I32, I64, ctypes.POINTER(P)]
     L.pa_bm_create.restype = I32
     L.pa_bm_destroy.argtypes = [P]

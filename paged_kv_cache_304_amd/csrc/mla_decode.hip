@@ -96,6 +96,13 @@ struct MlaArgs {
   int32_t bs_log2;  // log2(block_size) when a power of two, else -1
   int32_t out_f32;
   float scale_log2;
+  // decode step only (new_slots null otherwise): the batch's new latent rows,
+  // written by the absorb launch before the split reads the cache
+  uint16_t* wcache;            // the latent cache, writable
+  const uint16_t* new_c;       // [B, 512], row stride new_c_stride
+  const uint16_t* new_r;       // [B, rope_dim], row stride new_r_stride
+  const int64_t* new_slots;    // [B]; negative or outside the pool: no write
+  int64_t new_c_stride, new_r_stride;
 };
 
 __device__ __forceinline__ int clamp_ctx(const MlaArgs& a, int b) {
@@ -166,16 +173,39 @@ __device__ void plan_tiles(const MlaArgs& a) {
   }
 }
 
+// Decode step: sequence r's new latent row (c ++ RoPE key) into cache slot
+// new_slots[r], one wave a row (a lane moves 16 bytes of c, lanes < dr / 8 16
+// bytes of the RoPE key); workgroup wg of nwg takes rows 4 wg + wave, + 4 nwg, ...
+__device__ void write_new_rows(const MlaArgs& a, int row, int wg, int nwg) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t pool = a.num_blocks * (int64_t)a.block_size;
+  for (int r = 4 * wg + wave; r < a.num_seqs; r += 4 * nwg) {
+    const int64_t slot = a.new_slots[r];
+    if (slot < 0 || slot >= pool) continue;  // (uniform across the wave)
+    const int64_t blk = slot / a.block_size, off = slot - blk * a.block_size;
+    uint16_t* dst = a.wcache + blk * a.block_stride + off * row;
+    *reinterpret_cast<u32x4*>(dst + 8 * lane) = *reinterpret_cast<const u32x4*>(a.new_c + (int64_t)r * a.new_c_stride + 8 * lane);
+    if (lane < a.dr / 8)
+      *reinterpret_cast<u32x4*>(dst + kDC + 8 * lane) =
+          *reinterpret_cast<const u32x4*>(a.new_r + (int64_t)r * a.new_r_stride + 8 * lane);
+  }
+}
+
 // ---------------------------------------------------------------- absorb
 // q~^T [512 c x B] = W_UK,h [512 x qk] q_h^T [qk x B] per head on the matrix
 // cores (bf16 x bf16 products are exact in fp32, sums in fp32). grid (16
 // heads, 8 blocks of 64 latent dims, ceil(B / 16) + 1: the last layer writes the
-// tile plan of the split and nothing else); wave w computes latent
+// tile plan of the split and, in a decode step, the new latent rows); wave w computes latent
 // dims 64 cb + 16 w .. +15 for 16 sequences. The A operand is 16 bytes of a
 // W_UK row (dims 8 (l/16) .. of row l%16), the B operand 16 bytes of a q row.
 __global__ __launch_bounds__(256) void mla_absorb_kernel(MlaArgs a, int row) {
-  if (blockIdx.z == gridDim.z - 1) {  // the extra layer: its first workgroup writes the tile plan
-    if (blockIdx.x == 0 && blockIdx.y == 0) plan_tiles(a);
+  if (blockIdx.z == gridDim.z - 1) {  // the extra layer: its first workgroup writes the tile plan,
+    // and in a decode step the others write the new latent rows
+    const int lid = (int)(blockIdx.y * gridDim.x + blockIdx.x);
+    if (lid == 0)
+      plan_tiles(a);
+    else if (a.new_slots)
+      write_new_rows(a, row, lid - 1, (int)(gridDim.x * gridDim.y) - 1);
     return;
   }
   const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1042,19 +1072,26 @@ extern "C" size_t pa_mla_decode_workspace_size(int32_t num_seqs, int32_t num_hea
   return mla_plan(num_seqs, rope_dim).bytes;
 }
 
-extern "C" pa_status pa_mla_decode_attention(void* out, pa_dtype out_dtype, int64_t out_seq_stride, const void* q_nope,
-                                             int64_t q_nope_seq_stride, const void* q_rope, int64_t q_rope_seq_stride,
-                                             pa_dtype q_dtype, const void* w_uk, const void* w_uv, pa_dtype w_dtype,
-                                             const void* latent_cache, pa_dtype cache_dtype, int64_t num_blocks,
-                                             int32_t block_size, int64_t block_stride, const int32_t* block_tables,
-                                             int32_t max_blocks_per_seq, const int32_t* context_lens,
-                                             int32_t num_seqs, int32_t num_heads, int32_t qk_nope_dim,
-                                             int32_t rope_dim, int32_t kv_lora_rank, int32_t v_dim,
-                                             float softmax_scale, void* workspace, size_t workspace_bytes,
-                                             void* stream) {
-  using namespace pa;
-  clear_error();
-  const char* fn = "pa_mla_decode_attention";
+namespace pa {
+namespace {
+
+// The new latent rows of a decode step (null for plain attention).
+struct MlaNewRows {
+  const void* c;
+  int64_t c_stride;
+  const void* r;
+  int64_t r_stride;
+  pa_dtype dtype;
+  const int64_t* slots;
+};
+
+pa_status mla_launch(const char* fn, const MlaNewRows* nr, void* out, pa_dtype out_dtype, int64_t out_seq_stride,
+                     const void* q_nope, int64_t q_nope_seq_stride, const void* q_rope, int64_t q_rope_seq_stride,
+                     pa_dtype q_dtype, const void* w_uk, const void* w_uv, pa_dtype w_dtype, const void* latent_cache,
+                     pa_dtype cache_dtype, int64_t num_blocks, int32_t block_size, int64_t block_stride,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                     int32_t num_seqs, int32_t num_heads, int32_t qk_nope_dim, int32_t rope_dim, int32_t kv_lora_rank,
+                     int32_t v_dim, float softmax_scale, void* workspace, size_t workspace_bytes, void* stream) {
   pa_status s = check_mla_shape(fn, num_seqs, num_heads, qk_nope_dim, rope_dim, kv_lora_rank, v_dim,
                                 max_blocks_per_seq, block_size);
   if (s != PA_OK) return s;
@@ -1080,6 +1117,15 @@ extern "C" pa_status pa_mla_decode_attention(void* out, pa_dtype out_dtype, int6
   if (!aligned(w_uk, 16) || !aligned(w_uv, 16)) return fail(PA_EINVAL, "%s: weights must be 16-byte aligned", fn);
   if (!aligned(q_nope, 16) || (q_nope_seq_stride * 2) % 16 != 0)
     return fail(PA_EINVAL, "%s: q_nope must be 16-byte aligned per sequence", fn);
+  if (nr) {
+    if (nr->dtype != PA_BF16) return fail(PA_EDTYPE, "%s: new latent rows must be bf16", fn);
+    if (!nr->c || !nr->slots || (rope_dim > 0 && !nr->r)) return fail(PA_EINVAL, "%s: null new-row argument", fn);
+    if (nr->c_stride < kDC || (rope_dim > 0 && nr->r_stride < rope_dim))
+      return fail(PA_EINVAL, "%s: new-row strides below the row widths", fn);
+    if (!aligned(nr->c, 16) || (nr->c_stride * 2) % 16 != 0 ||
+        (rope_dim > 0 && (!aligned(nr->r, 16) || (nr->r_stride * 2) % 16 != 0)))
+      return fail(PA_EINVAL, "%s: new latent rows must be 16-byte aligned per row", fn);
+  }
   // the split's units (tiles of 32 positions over all sequences, plus one
   // query item per sequence: at most 2^20 more) must count in 32 bits
   if ((int64_t)num_seqs * (((int64_t)max_blocks_per_seq * block_size + kTile - 1) / kTile) > INT32_MAX / 2)
@@ -1088,8 +1134,11 @@ extern "C" pa_status pa_mla_decode_attention(void* out, pa_dtype out_dtype, int6
   if (!workspace || workspace_bytes < p.bytes || !aligned(workspace, 256))
     return fail(PA_EWORKSPACE, "%s: workspace needs %zu bytes, 256-byte aligned (got %zu)", fn, p.bytes, workspace_bytes);
   if (checks_on()) {
-    const pa_status c = check_tables(fn, reinterpret_cast<hipStream_t>(stream), block_tables, num_seqs,
-                                     max_blocks_per_seq, context_lens, num_blocks, block_size);
+    pa_status c = check_tables(fn, reinterpret_cast<hipStream_t>(stream), block_tables, num_seqs,
+                               max_blocks_per_seq, context_lens, num_blocks, block_size);
+    if (c == PA_OK && nr)
+      c = check_slots(fn, reinterpret_cast<hipStream_t>(stream), nr->slots, num_seqs, nullptr, 0, num_blocks,
+                      block_size);
     if (c != PA_OK) return c;
   }
 
@@ -1124,6 +1173,12 @@ extern "C" pa_status pa_mla_decode_attention(void* out, pa_dtype out_dtype, int6
   a.dv = v_dim;
   a.out_f32 = out_dtype == PA_F32;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.wcache = nr ? const_cast<uint16_t*>(static_cast<const uint16_t*>(latent_cache)) : nullptr;
+  a.new_c = nr ? static_cast<const uint16_t*>(nr->c) : nullptr;
+  a.new_r = nr ? static_cast<const uint16_t*>(nr->r) : nullptr;
+  a.new_slots = nr ? nr->slots : nullptr;
+  a.new_c_stride = nr ? nr->c_stride : 0;
+  a.new_r_stride = nr ? nr->r_stride : 0;
 
   int grid = 0;
   s = split_grid(fn, &grid);
@@ -1137,4 +1192,43 @@ extern "C" pa_status pa_mla_decode_attention(void* out, pa_dtype out_dtype, int6
     mla_split_kernel<0><<<(unsigned)grid, 64 * (kWaves + kProducers), 0, st>>>(a);
   mla_merge_kernel<<<dim3(kHeads, (unsigned)((num_seqs + 3) / 4)), kMergeThreads, 0, st>>>(a);
   return after_launch(fn);
+}
+
+}  // namespace
+}  // namespace pa
+
+extern "C" pa_status pa_mla_decode_attention(void* out, pa_dtype out_dtype, int64_t out_seq_stride, const void* q_nope,
+                                             int64_t q_nope_seq_stride, const void* q_rope, int64_t q_rope_seq_stride,
+                                             pa_dtype q_dtype, const void* w_uk, const void* w_uv, pa_dtype w_dtype,
+                                             const void* latent_cache, pa_dtype cache_dtype, int64_t num_blocks,
+                                             int32_t block_size, int64_t block_stride, const int32_t* block_tables,
+                                             int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                             int32_t num_seqs, int32_t num_heads, int32_t qk_nope_dim,
+                                             int32_t rope_dim, int32_t kv_lora_rank, int32_t v_dim,
+                                             float softmax_scale, void* workspace, size_t workspace_bytes,
+                                             void* stream) {
+  pa::clear_error();
+  return pa::mla_launch("pa_mla_decode_attention", nullptr, out, out_dtype, out_seq_stride, q_nope, q_nope_seq_stride,
+                        q_rope, q_rope_seq_stride, q_dtype, w_uk, w_uv, w_dtype, latent_cache, cache_dtype, num_blocks,
+                        block_size, block_stride, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads,
+                        qk_nope_dim, rope_dim, kv_lora_rank, v_dim, softmax_scale, workspace, workspace_bytes, stream);
+}
+
+extern "C" pa_status pa_mla_decode_step(const void* new_c, int64_t new_c_stride, const void* new_rope,
+                                        int64_t new_rope_stride, pa_dtype new_dtype, const int64_t* new_slots,
+                                        void* out, pa_dtype out_dtype, int64_t out_seq_stride, const void* q_nope,
+                                        int64_t q_nope_seq_stride, const void* q_rope, int64_t q_rope_seq_stride,
+                                        pa_dtype q_dtype, const void* w_uk, const void* w_uv, pa_dtype w_dtype,
+                                        void* latent_cache, pa_dtype cache_dtype, int64_t num_blocks,
+                                        int32_t block_size, int64_t block_stride, const int32_t* block_tables,
+                                        int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                                        int32_t num_heads, int32_t qk_nope_dim, int32_t rope_dim,
+                                        int32_t kv_lora_rank, int32_t v_dim, float softmax_scale, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  pa::clear_error();
+  const pa::MlaNewRows nr = {new_c, new_c_stride, new_rope, new_rope_stride, new_dtype, new_slots};
+  return pa::mla_launch("pa_mla_decode_step", &nr, out, out_dtype, out_seq_stride, q_nope, q_nope_seq_stride, q_rope,
+                        q_rope_seq_stride, q_dtype, w_uk, w_uv, w_dtype, latent_cache, cache_dtype, num_blocks,
+                        block_size, block_stride, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads,
+                        qk_nope_dim, rope_dim, kv_lora_rank, v_dim, softmax_scale, workspace, workspace_bytes, stream);
 }

@@ -351,13 +351,9 @@ def mla_decode_workspace_size(num_seqs: int, num_heads: int, qk_nope_dim: int, r
     return n
 
 
-def mla_decode_attention(out: torch.Tensor, q_nope: torch.Tensor, q_rope: Optional[torch.Tensor],
-                         w_uk: torch.Tensor, w_uv: torch.Tensor, latent_cache: torch.Tensor,
-                         block_tables: torch.Tensor, context_lens: torch.Tensor, softmax_scale: float,
-                         workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """MLA decode over a paged latent cache [NB, BS, kv_lora_rank + rope_dim]:
-    q_nope [B, H, qk], q_rope [B, H, r] (or None), w_uk [kv_lora_rank, H*qk],
-    w_uv [kv_lora_rank, H*dv]; writes and returns out [B, H, dv]."""
+def _mla_args(out, q_nope, q_rope, w_uk, w_uv, latent_cache, block_tables, context_lens, softmax_scale,
+              workspace, stream):
+    """Checked argument list of pa_mla_decode_attention (shared by the step)."""
     _on_gpu(out, q_nope, q_rope, w_uk, w_uv, latent_cache, block_tables, context_lens, workspace)
     B, H, QK = q_nope.shape
     NB, BS, ROW = latent_cache.shape
@@ -385,11 +381,56 @@ def mla_decode_attention(out: torch.Tensor, q_nope: torch.Tensor, q_rope: Option
     if workspace is None:
         workspace = _scratch(mla_decode_workspace_size(max(B, 1), H, QK, R, DC, DV, W, BS),
                              q_nope.device, stream)
-    check(lib.pa_mla_decode_attention(
-        out.data_ptr(), _code(out, "out"), out.stride(0), q_nope.data_ptr(), q_nope.stride(0),
-        _ptr(q_rope), q_rope.stride(0) if q_rope is not None else 0, _code(q_nope, "q_nope"),
-        w_uk.data_ptr(), w_uv.data_ptr(), _code(w_uk, "w_uk"), latent_cache.data_ptr(),
-        _code(latent_cache, "latent_cache"), NB, BS, latent_cache.stride(0), block_tables.data_ptr(), W,
-        context_lens.data_ptr(), B, H, QK, R, DC, DV, float(softmax_scale), workspace.data_ptr(),
-        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return (out.data_ptr(), _code(out, "out"), out.stride(0), q_nope.data_ptr(), q_nope.stride(0),
+            _ptr(q_rope), q_rope.stride(0) if q_rope is not None else 0, _code(q_nope, "q_nope"),
+            w_uk.data_ptr(), w_uv.data_ptr(), _code(w_uk, "w_uk"), latent_cache.data_ptr(),
+            _code(latent_cache, "latent_cache"), NB, BS, latent_cache.stride(0), block_tables.data_ptr(), W,
+            context_lens.data_ptr(), B, H, QK, R, DC, DV, float(softmax_scale), workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(), _stream(stream))
+
+
+def mla_decode_attention(out: torch.Tensor, q_nope: torch.Tensor, q_rope: Optional[torch.Tensor],
+                         w_uk: torch.Tensor, w_uv: torch.Tensor, latent_cache: torch.Tensor,
+                         block_tables: torch.Tensor, context_lens: torch.Tensor, softmax_scale: float,
+                         workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """MLA decode over a paged latent cache [NB, BS, kv_lora_rank + rope_dim]:
+    q_nope [B, H, qk], q_rope [B, H, r] (or None), w_uk [kv_lora_rank, H*qk],
+    w_uv [kv_lora_rank, H*dv]; writes and returns out [B, H, dv]."""
+    check(lib.pa_mla_decode_attention(*_mla_args(out, q_nope, q_rope, w_uk, w_uv, latent_cache, block_tables,
+                                                 context_lens, softmax_scale, workspace, stream)))
+    return out
+
+
+def mla_decode_step(new_c: torch.Tensor, new_rope: Optional[torch.Tensor], new_slots: torch.Tensor,
+                    out: torch.Tensor, q_nope: torch.Tensor, q_rope: Optional[torch.Tensor],
+                    w_uk: torch.Tensor, w_uv: torch.Tensor, latent_cache: torch.Tensor,
+                    block_tables: torch.Tensor, context_lens: torch.Tensor, softmax_scale: float,
+                    workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One MLA decode step: sequence b's new latent row new_c[b] [kv_lora_rank]
+    ++ new_rope[b] [rope_dim] (bf16, rows of the trailing dims may be [B, 1, n])
+    into latent_cache slot new_slots[b] (int64; negative skips), then
+    mla_decode_attention over the cache; returns out."""
+    _on_gpu(new_c, new_rope, new_slots)
+    B = q_nope.shape[0]
+    R = 0 if q_rope is None else q_rope.shape[2]
+    DC = latent_cache.shape[2] - R
+    def rows(t):  # [B, 1, n] -> the [B, n] view (never a copy: the pointer goes to the launch)
+        if t is None or t.dim() != 3:
+            return t
+        if t.shape[1] != 1:
+            raise ValueError("new rows must be [B, n] or [B, 1, n]")
+        return t[:, 0, :]
+    c2, r2 = rows(new_c), rows(new_rope)
+    if c2.dim() != 2 or c2.shape != (B, DC) or c2.stride(1) != 1:
+        raise ValueError("new_c must be [B, kv_lora_rank] with contiguous rows")
+    if (R > 0) != (r2 is not None) or (r2 is not None and (r2.shape != (B, R) or r2.stride(1) != 1)):
+        raise ValueError("new_rope must be [B, rope_dim] with contiguous rows (None when rope_dim is 0)")
+    if r2 is not None and r2.dtype != c2.dtype:
+        raise ValueError("new_c and new_rope must share a dtype")
+    if new_slots.dtype != torch.int64 or new_slots.numel() != B or not new_slots.is_contiguous():
+        raise ValueError("new_slots must be contiguous int64 [B]")
+    args = _mla_args(out, q_nope, q_rope, w_uk, w_uv, latent_cache, block_tables, context_lens, softmax_scale,
+                     workspace, stream)
+    check(lib.pa_mla_decode_step(c2.data_ptr(), c2.stride(0), _ptr(r2), r2.stride(0) if r2 is not None else 0,
+                                 _code(c2, "new_c"), new_slots.data_ptr(), *args))
     return out

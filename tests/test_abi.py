@@ -274,6 +274,43 @@ def test_mla_decode_empty_and_workspace_size(L):
     assert f(64, 8, 128, 64, 512, 128, 256, 16) == 0 and L.last_error()
 
 
+def mla_step(L, **over):
+    a = dict(nc=1 << 29, ncs=512, nr=(1 << 29) + (1 << 20), nrs=64, ndt=L.PA_BF16, ns=(1 << 29) + (1 << 21),
+             out=1 << 20, odt=L.PA_BF16, os=16 * 128, qn=1 << 21, qns=16 * 128, qr=1 << 22, qrs=16 * 64,
+             qdt=L.PA_BF16, wuk=1 << 23, wuv=1 << 24, wdt=L.PA_BF16, cache=1 << 25, cdt=L.PA_BF16, NB=16,
+             BS=16, bstride=16 * 576, bt=1 << 26, W=4, cl=1 << 27, B=2, H=16, QK=128, R=64, DC=512, DV=128,
+             scale=0.07, ws=1 << 28, wsb=16)
+    a.update(over)
+    return L.lib.pa_mla_decode_step(a["nc"], a["ncs"], a["nr"], a["nrs"], a["ndt"], a["ns"],
+                                    a["out"], a["odt"], a["os"], a["qn"], a["qns"], a["qr"], a["qrs"],
+                                    a["qdt"], a["wuk"], a["wuv"], a["wdt"], a["cache"], a["cdt"], a["NB"],
+                                    a["BS"], a["bstride"], a["bt"], a["W"], a["cl"], a["B"], a["H"],
+                                    a["QK"], a["R"], a["DC"], a["DV"], a["scale"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(), "PA_EWORKSPACE"),                 # valid new rows: the call reaches the workspace check
+    (dict(ndt=2), "PA_EDTYPE"),                # f32 rows into a bf16 cache
+    (dict(ns=None), "PA_EINVAL"),
+    (dict(nc=None), "PA_EINVAL"),
+    (dict(nr=None), "PA_EINVAL"),              # RoPE part expected (rope_dim 64)
+    (dict(ncs=500), "PA_EINVAL"),              # row stride below 512
+    (dict(nrs=32), "PA_EINVAL"),
+    (dict(nc=(1 << 29) + 8), "PA_EINVAL"),     # rows not 16-byte aligned
+    (dict(ncs=516), "PA_EINVAL"),
+    (dict(H=8), "PA_EUNSUPPORTED"),            # the attention's own checks come first
+])
+def test_mla_decode_step_rejects_before_enqueueing(L, over, code):
+    assert mla_step(L, **over) == getattr(L, code)
+    assert L.last_error()
+
+
+def test_mla_decode_step_empty_and_without_rope(L):
+    assert mla_step(L, B=0, nc=None, ns=None, qn=None, out=None) == L.PA_OK
+    # no RoPE part: new_rope may be NULL (the call then stops at the too-small workspace)
+    assert mla_step(L, R=0, qr=None, nr=None, bstride=16 * 512) == L.PA_EWORKSPACE
+
+
 def test_hbm_read_rejects(L):
     assert L.lib.pa_hbm_read(None, 64, 1 << 20, None) == L.PA_EINVAL
     assert L.lib.pa_hbm_read(1 << 20, 64, None, None) == L.PA_EINVAL

@@ -192,3 +192,25 @@ def test_mla_decode_checks_its_tables(m, checked):
     m.mla_decode_attention(out, qn, qr, wuk, wuv, cache, bt, cl, 0.1)
     bt[1, 1] = -5
     refused(m, lambda: m.mla_decode_attention(out, qn, qr, wuk, wuv, cache, bt, cl, 0.1), "outside the pool")
+
+
+def test_mla_decode_step_checks_the_new_slots(m, checked):
+    say("PA_CHECK mla_decode_step")
+    B, H, QK, R, DC, DV, W = 2, 16, 64, 64, 512, 64, 4
+    ctx = (20, 33)
+    _, _, _, bt, cl = decode_case(ctx=ctx, W=W)
+    cache = randn(NB, BS, DC + R, seed=17)
+    qn, qr = randn(B, H, QK, seed=18), randn(B, H, R, seed=19)
+    wuk, wuv = randn(DC, H * QK, seed=20) * 0.05, randn(DC, H * DV, seed=21) * 0.05
+    nc, nr = randn(B, DC, seed=22), randn(B, R, seed=23)
+    out = torch.empty((B, H, DV), dtype=torch.bfloat16, device="cuda")
+    pos = cl.long() - 1
+    slots = bt.long().gather(1, (pos // BS)[:, None])[:, 0] * BS + pos % BS
+    m.mla_decode_step(nc, nr, slots, out, qn, qr, wuk, wuv, cache, bt, cl, 0.1)
+    before = cache.clone()
+    slots[1] = slots[0]
+    refused(m, lambda: m.mla_decode_step(nc, nr, slots, out, qn, qr, wuk, wuv, cache, bt, cl, 0.1),
+            "both write slot")
+    torch.cuda.synchronize()
+    assert torch.equal(cache, before)
+

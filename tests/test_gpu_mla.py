@@ -223,6 +223,61 @@ def test_mla_decode_step_writes_latent_rows_then_attends():
     assert_attention_close(got, ref, "mla step", out_bf16=False)
 
 
+@pytest.mark.parametrize("R", [64, 0])
+def test_mla_decode_step_entry_writes_then_attends_in_one_call(R):
+    """pa_mla_decode_step: the cache bit-exact against the oracle's concat + write
+    (a negative slot and one past the pool write nothing), the output against
+    the oracle's MLA decode on that cache, and bit-identical to the two calls it
+    replaces (concat_and_cache_mla_k, then mla_decode_attention). 520 sequences:
+    more rows than the absorb launch's writing waves (508)."""
+    m = pkv()
+    ctx = [40, 1, 300, 17, 64] + [1 + (i * 7) % 12 for i in range(515)]
+    say(f"mla decode step entry R={R} B={len(ctx)}")
+    c = make_case(4243 + R, ctx, R=R)
+    rng = np.random.default_rng(8 + R)
+    B = len(c["ctx"])
+    bs = c["cache"].shape[1]
+    nb = c["cache"].shape[0]
+    new_c = workloads.normal_bf16_bits(rng, (B, DC))
+    new_r = workloads.normal_bf16_bits(rng, (B, R)) if R else None
+    pos = c["ctx"].astype(np.int64) - 1
+    slots = workloads.slots_for_positions(c["bt"], np.arange(B), pos, bs)
+    cache = c["cache"].copy()
+    for b in range(B):
+        if b not in (2, 3):                  # the new positions hold NaN until written
+            cache[slots[b] // bs, slots[b] % bs] = NAN_BF16
+    slots[2] = -1                            # skipped: its last position keeps its row
+    slots[3] = nb * bs                       # past the pool: skipped too
+    ocache = cache.copy()
+    k = np.zeros((B, 1, DC + R), dtype=np.float32)
+    oracle.concat_and_cast(k, oracle.F32, new_c[:, None, :], BF16,
+                           new_r[:, None, :] if R else np.zeros((B, 1, 0), dtype=np.uint16), BF16)
+    oracle.reshape_and_cache(k, None, oracle.F32, ocache.reshape(-1, bs, 1, DC + R), None, BF16, slots)
+    ref = oracle_mla(c, cache=ocache)
+
+    dslots = torch.from_numpy(slots).cuda()
+    args = lambda dc, out: (out, to_dev(c["q_nope"], BF16), None if R == 0 else to_dev(c["q_rope"], BF16),
+                            to_dev(c["w_uk"], BF16), to_dev(c["w_uv"], BF16), dc,
+                            torch.from_numpy(c["bt"]).cuda(), torch.from_numpy(c["ctx"]).cuda(), c["scale"])
+    dcache = to_dev(cache, BF16)
+    out = torch.full((B, H, c["DV"]), float("nan"), device="cuda")
+    m.mla_decode_step(to_dev(new_c, BF16), None if R == 0 else to_dev(new_r, BF16), dslots, *args(dcache, out))
+    # the two calls it replaces
+    dcache2 = to_dev(cache, BF16)
+    out2 = torch.full_like(out, float("nan"))
+    if R:
+        m.concat_and_cache_mla_k(to_dev(new_c, BF16)[:, None, :], to_dev(new_r, BF16)[:, None, :],
+                                 dcache2.view(-1, bs, 1, DC + R), dslots)
+    m.mla_decode_attention(*args(dcache2, out2))
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(dcache, BF16), ocache), "latent cache"
+    assert_attention_close(widen_out(out), ref, "mla step entry", out_bf16=False)
+    if R:
+        # (bit patterns: slots no sequence owns hold NaN)
+        assert torch.equal(dcache.view(torch.int16), dcache2.view(torch.int16)), "fused step's cache differs"
+        assert torch.equal(out.view(torch.int32), out2.view(torch.int32)), "fused step's output differs"
+
+
 def test_mla_in_a_hip_graph_replays_exactly():
     """Captured once (workspace supplied), replayed four times with new queries
     and eager work in between; every replay equals an eager call."""
