@@ -317,6 +317,55 @@ def test_mla_in_a_hip_graph_replays_exactly():
         del junk
 
 
+def test_mla_decode_step_in_a_hip_graph_replays_exactly():
+    """The one-call step captured once, replayed four times with new latent rows
+    and queries and eager work in between: every replay leaves the new rows in
+    their slots and equals an eager step."""
+    m = pkv()
+    say("mla_decode_step graph capture")
+    c = make_case(516, [300, 1, 700, 64])
+    B, R, bs = len(c["ctx"]), c["R"], c["cache"].shape[1]
+    qn, qr = to_dev(c["q_nope"], BF16), to_dev(c["q_rope"], BF16)
+    wk, wv, cache = to_dev(c["w_uk"], BF16), to_dev(c["w_uv"], BF16), to_dev(c["cache"], BF16)
+    bt, cl = torch.from_numpy(c["bt"]).cuda(), torch.from_numpy(c["ctx"]).cuda()
+    slots = workloads.slots_for_positions(c["bt"], np.arange(B), c["ctx"].astype(np.int64) - 1, bs)
+    dslots = torch.from_numpy(slots).cuda()
+    rng = np.random.default_rng(3)
+    nc = to_dev(workloads.normal_bf16_bits(rng, (B, DC)), BF16)
+    nr = to_dev(workloads.normal_bf16_bits(rng, (B, R)), BF16)
+    ws = torch.empty(m.mla_decode_workspace_size(B, H, c["QK"], R, DC, c["DV"], c["bt"].shape[1], bs),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.zeros((B, H, c["DV"]), dtype=torch.float32, device="cuda")
+    eager = torch.zeros_like(out)
+    step = lambda o: m.mla_decode_step(nc, nr, dslots, o, qn, qr, wk, wv, cache, bt, cl, c["scale"],  # noqa: E731
+                                       workspace=ws)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(out)
+    flat = cache.view(-1, DC + R)
+    for i in range(4):
+        nc.copy_(to_dev(workloads.normal_bf16_bits(rng, (B, DC)), BF16))
+        nr.copy_(to_dev(workloads.normal_bf16_bits(rng, (B, R)), BF16))
+        qn.copy_(to_dev(workloads.normal_bf16_bits(rng, c["q_nope"].shape), BF16))
+        out.zero_()
+        junk = torch.randn(1 << 18, device="cuda").sum()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        rows = flat[dslots]
+        assert torch.equal(rows.view(torch.int16), torch.cat([nc, nr], dim=1).view(torch.int16)), f"rows {i}"
+        step(eager)
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i}"
+        del junk
+
+
 def test_repeated_full_size_calls_are_identical_and_finite():
     """300 calls of the batch-64 workload back to back, ten outputs in flight
     at a time: the split kernel's waves hand work to each other at their own
